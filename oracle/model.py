@@ -1,0 +1,181 @@
+"""Target decoder, draft module (PDM) and multi-depth features (test infrastructure only)."""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from .layers import F32, apply_rope, attention, bf16_round, rmsnorm, rope_cos_sin, silu
+from .schedule import pattern, stage_layers
+
+
+class KVCache:
+    """Per-layer key/value store with a length word.
+
+    Entries are kept in the model's storage precision (bf16-rounded for bf16
+    models).  `length` is the number of valid positions; truncation is a
+    write of the length alone, as in the rollback of [RB] method step 5.
+    """
+
+    def __init__(self, max_ctx: int, Hkv: int, hd: int, bf16: bool):
+        self.K = np.zeros((max_ctx, Hkv, hd), dtype=F32)
+        self.V = np.zeros((max_ctx, Hkv, hd), dtype=F32)
+        self.length = 0
+        self.bf16 = bf16
+
+    def write(self, pos: int, k: np.ndarray, v: np.ndarray) -> None:
+        if self.bf16:
+            k, v = bf16_round(k), bf16_round(v)
+        self.K[pos] = k
+        self.V[pos] = v
+
+
+def _qkv(lw, u, Hq, Hkv, hd):
+    qkv = lw["w_qkv"] @ u
+    q = qkv[: Hq * hd].reshape(Hq, hd)
+    k = qkv[Hq * hd: (Hq + Hkv) * hd].reshape(Hkv, hd)
+    v = qkv[(Hq + Hkv) * hd:].reshape(Hkv, hd)
+    return q, k, v
+
+
+def _ffn(lw, h, F, eps):
+    u2 = rmsnorm(h, lw["ffn_norm"], eps)
+    gu = lw["w_gu"] @ u2
+    return h + lw["w_down"] @ (silu(gu[:F]) * gu[F:])
+
+
+class _Shape:
+    def __init__(self, w):
+        self.L, self.d, self.Hq, self.Hkv, self.hd = w.L, w.d, w.Hq, w.Hkv, w.hd
+        self.F, self.V, self.n, self.Ls = w.F, w.V, w.n, w.Ls
+        self.anchors = list(w.anchors)
+        self.eps, self.base = w.eps, w.rope_base
+        self.bf16 = w.dtype == "bf16"
+        self.max_ctx = w.max_ctx
+
+
+def layer_step(s: _Shape, lw, h: np.ndarray, pos: int, kv: KVCache, check_len: bool = True):
+    """One decoder layer for one token at position `pos` (pre-norm, GQA, SwiGLU).
+
+    Appends the token's k, v at index pos (asserting the cache holds exactly
+    positions 0..pos-1 when `check_len`) and attends over 0..pos.
+    """
+    u = rmsnorm(h, lw["attn_norm"], s.eps)
+    q, k, v = _qkv(lw, u, s.Hq, s.Hkv, s.hd)
+    c, sn = rope_cos_sin(pos, s.hd, s.base)
+    q, k = apply_rope(q, c, sn), apply_rope(k, c, sn)
+    if check_len:
+        assert kv.length == pos, f"KV length {kv.length} != position {pos}"
+    kv.write(pos, k, v)
+    kv.length = pos + 1
+    o = attention(q, kv.K[: pos + 1], kv.V[: pos + 1])
+    h = h + lw["w_o"] @ o.reshape(-1)
+    return _ffn(lw, h, s.F, s.eps)
+
+
+def layer_rows(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache) -> np.ndarray:
+    """One decoder layer over M consecutive positions pos0..pos0+M-1 (causal).
+
+    Row i attends to cached positions 0..pos0-1 and to rows 0..i.  The rows'
+    k, v are written at positions pos0.. of `kv`; whether they stay valid is
+    the caller's decision (the length word is not touched).
+    """
+    M = X.shape[0]
+    Q = []
+    for i in range(M):
+        u = rmsnorm(X[i], lw["attn_norm"], s.eps)
+        q, k, v = _qkv(lw, u, s.Hq, s.Hkv, s.hd)
+        c, sn = rope_cos_sin(pos0 + i, s.hd, s.base)
+        Q.append(apply_rope(q, c, sn))
+        kv.write(pos0 + i, apply_rope(k, c, sn), v)
+    out = np.empty_like(X)
+    for i in range(M):
+        p = pos0 + i
+        o = attention(Q[i], kv.K[: p + 1], kv.V[: p + 1])
+        h = X[i] + lw["w_o"] @ o.reshape(-1)
+        out[i] = _ffn(lw, h, s.F, s.eps)
+    return out
+
+
+class Target:
+    """The L-layer target decoder with per-layer KV caches and anchor taps."""
+
+    def __init__(self, w, W):
+        self.s = _Shape(w)
+        self.W = W
+        self.kv = [KVCache(self.s.max_ctx, self.s.Hkv, self.s.hd, self.s.bf16)
+                   for _ in range(self.s.L)]
+        # anchor index of each layer boundary b (residual after b layers)
+        self.anchor_at = {b: i for i, b in enumerate(self.s.anchors)}
+
+    def embed(self, tok: int) -> np.ndarray:
+        return self.W["embed"][tok].astype(F32).copy()
+
+    def run_layers(self, h: np.ndarray, pos: int, layers: Sequence[int],
+                   taps: Optional[List] = None) -> np.ndarray:
+        """Run `layers` for one token; record anchors h^(b) into `taps`."""
+        for l in layers:
+            h = layer_step(self.s, self.W["layers"][l], h, pos, self.kv[l])
+            if taps is not None and (l + 1) in self.anchor_at:
+                taps[self.anchor_at[l + 1]] = h.copy()
+        return h
+
+    def run_stage(self, h, pos, k, taps=None):
+        return self.run_layers(h, pos, stage_layers(k, self.s.L, self.s.n), taps)
+
+    def logits(self, h: np.ndarray) -> np.ndarray:
+        """Full-depth logits W_lm * rmsnorm(h^(L)) (float32)."""
+        return self.W["lm_head"] @ rmsnorm(h, self.W["final_norm"], self.s.eps)
+
+    def forward_token(self, tok: int, pos: int):
+        """Whole-model pass for one token: (final hidden, anchors)."""
+        taps = [None] * len(self.s.anchors)
+        h = self.embed(tok)
+        taps[0] = h.copy()
+        h = self.run_layers(h, pos, range(self.s.L), taps)
+        return h, taps
+
+    def truncate(self, length: int) -> None:
+        for kv in self.kv:
+            kv.length = length
+
+
+class PDM:
+    """Pipeline draft module: FC fusion of anchors, Ls causal decoder layers, own head.
+
+    [PL] §3.1: an Ls-layer Transformer decoder with an independent LM head that
+    predicts one token; [RB] method steps 3-4: features of each position are
+    the concatenated reachable anchors projected by the FC of its pattern.
+    Reading taken: the layers have the target's layer shape with their own
+    weights, positions are the true sequence positions, and a final RMSNorm
+    precedes the head.
+    """
+
+    def __init__(self, w, W):
+        self.s = _Shape(w)
+        self.W = W
+        self.kv = [KVCache(self.s.max_ctx, self.s.Hkv, self.s.hd, self.s.bf16)
+                   for _ in range(self.s.Ls)]
+        self.C = 0  # committed positions 0..C-1 (features at full depth n)
+
+    def feature(self, taps: Sequence[np.ndarray], k: int) -> np.ndarray:
+        """g(p, k) = W_fc[f(k)] * concat(A[p][0..f(k)]) ([RB] core method)."""
+        f = pattern(k, self.s.anchors, self.s.L, self.s.n)
+        x = np.concatenate([taps[i] for i in range(f + 1)]).astype(F32)
+        return self.W["fc"][f] @ x
+
+    def run_rows(self, G: np.ndarray, pos0: int) -> np.ndarray:
+        """All Ls layers over feature rows at positions pos0.. (pos0 == C)."""
+        assert pos0 == self.C, "trailing rows must start at the committed length"
+        X = G.astype(F32)
+        for l in range(self.s.Ls):
+            X = layer_rows(self.s, self.W["pdm_layers"][l], X, pos0, self.kv[l])
+        return X
+
+    def logits(self, x: np.ndarray) -> np.ndarray:
+        return self.W["pdm_lm_head"] @ rmsnorm(x, self.W["pdm_final_norm"], self.s.eps)
+
+    def commit(self, count: int) -> None:
+        self.C += count
+        for kv in self.kv:
+            kv.length = self.C

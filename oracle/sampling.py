@@ -1,0 +1,76 @@
+"""Temperature sampling and rejection-sampling verification (test infrastructure only).
+
+[YB] §2.1: a draft x drawn from Q is accepted with probability
+min(1, P(x)/Q(x)); otherwise the token is redrawn from the adjusted
+distribution normalize(max(0, P - Q)).  [YB] §2.2: the emitted token is then
+distributed exactly as P.  [TW] §6 / [PL] §3.4: SPD applies this rule at the
+streaming verification of each position.
+
+Precision (the decisions are taken the same way on both sides): weights
+w_v = exp(l_v/T - max) in float32; normalisers, CDFs and the acceptance
+comparison in float64; inverse CDF = smallest id i whose ascending-id
+cumulative weight exceeds u * (total weight).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def softmax_weights(logits: np.ndarray, temperature: float = 1.0):
+    """(w float32, Z float64): unnormalised softmax weights and their sum."""
+    l = logits.astype(np.float32)
+    if temperature != 1.0:
+        l = l / np.float32(temperature)
+    w = np.exp(l - l.max()).astype(np.float32)
+    return w, float(np.sum(w.astype(np.float64)))
+
+
+def inverse_cdf(weights: np.ndarray, u: float):
+    """Smallest i with cumsum(weights)[i] > u * sum(weights) (float64 cumsum).
+
+    Returns (index, gap) where gap is the distance of the threshold from the
+    nearest boundary of the chosen interval, relative to the total (used to
+    judge whether another implementation may legitimately differ).
+    """
+    c = np.cumsum(weights.astype(np.float64))
+    total = c[-1]
+    thr = np.float64(u) * total
+    i = int(np.searchsorted(c, thr, side="right"))
+    if i >= len(c):
+        i = int(np.flatnonzero(weights > 0)[-1])
+    lo = c[i - 1] if i > 0 else 0.0
+    gap = min(thr - lo, c[i] - thr) / total if total > 0 else 0.0
+    return i, float(gap)
+
+
+def accept_test(p_w, p_Z, q_w, q_Z, x: int, u: float):
+    """Accept draft x iff u * Q(x) < P(x)  (i.e. u < min(1, P/Q)).
+
+    Returns (accepted, gap): gap = |u*Q(x) - P(x)| / Q(x).
+    """
+    Px = np.float64(p_w[x]) / p_Z
+    Qx = np.float64(q_w[x]) / q_Z
+    lhs = np.float64(u) * Qx
+    return bool(lhs < Px), float(abs(lhs - Px) / Qx) if Qx > 0 else float("inf")
+
+
+def residual(p_w, p_Z, q_w, q_Z) -> np.ndarray:
+    """max(0, P - Q) (float64, unnormalised: inverse_cdf normalises)."""
+    P = p_w.astype(np.float64) / p_Z
+    Q = q_w.astype(np.float64) / q_Z
+    return np.maximum(0.0, P - Q)
+
+
+def emit_distribution(P: np.ndarray, Q: np.ndarray) -> np.ndarray:
+    """Exact law of the token the rule emits when x ~ Q (for enumeration pins).
+
+    Pr[emit v] = Q(v) min(1, P(v)/Q(v)) + (1 - sum_x min(P(x), Q(x))) r(v),
+    with r = normalize(max(0, P - Q)).  [YB] §2.2 states that this equals P.
+    """
+    P = P.astype(np.float64)
+    Q = Q.astype(np.float64)
+    acc = np.where(Q > 0, Q * np.minimum(1.0, np.divide(P, Q, out=np.zeros_like(P), where=Q > 0)), 0.0)
+    rej_mass = 1.0 - np.minimum(P, Q).sum()
+    r = np.maximum(0.0, P - Q)
+    r = r / r.sum() if r.sum() > 0 else np.zeros_like(P)
+    return acc + rej_mass * r

@@ -1,0 +1,97 @@
+"""Closed forms of the SPD schedule (test infrastructure only).
+
+Conventions: positions and layers are 0-indexed; stage k (0..n-1) holds
+layers k*L/n .. (k+1)*L/n - 1; the depth of a token is the number of stages
+it has completed (0..n); anchor b means the residual stream after b layers
+(b = 0 is the token embedding).
+"""
+from __future__ import annotations
+
+from typing import List, Sequence
+
+
+def lmax(k: int, L: int, n: int) -> int:
+    """Deepest layer index a token at depth k has reached: min(L, k*L/n).
+
+    [RB] core method (bounded incompleteness); [PL] §3.2.
+    """
+    return min(L, k * (L // n))
+
+
+def pattern(k: int, anchors: Sequence[int], L: int, n: int) -> int:
+    """f(k) = max{i : b_i <= lmax(k)}: the last anchor reachable at depth k.
+
+    The feature of a depth-k token concatenates anchors 0..f(k).  [RB] core
+    method; [PL] §3.2 (k = 0 reduces to the embedding alone).
+    """
+    lm = lmax(k, L, n)
+    return max(i for i, b in enumerate(anchors) if b <= lm)
+
+
+def pattern_table(anchors: Sequence[int], L: int, n: int) -> List[int]:
+    return [pattern(k, anchors, L, n) for k in range(n + 1)]
+
+
+def n_patterns(anchors: Sequence[int], L: int, n: int) -> int:
+    """Number of distinct fusion projections the depths 0..n use.
+
+    [RB] method step 3: several depths share one fusion pattern when m < n+1;
+    [RB] technical novelty: the L=32, n=8 example needs m = 5 projections.
+    """
+    return len(set(pattern_table(anchors, L, n)))
+
+
+def stage_layers(k: int, L: int, n: int) -> range:
+    """Layers of stage k under the uniform split ([RB] core method: L/n each)."""
+    per = L // n
+    return range(k * per, (k + 1) * per)
+
+
+def depth_layout(a: int, pending: bool, n: int) -> List[int]:
+    """Depths of the trailing feature rows the draft module sees pre-step.
+
+    Rows are ordered by position.  The just-verified position (if its
+    full-depth feature is not cached yet) is at depth n; the a in-flight
+    tokens are at depths a-1 .. 0, the newest contributing the embedding
+    only.  Steady state (a = n) is the staircase g_n, g_{n-1}, ..., g_0 of
+    [RB] method step 2 / [PL] appendix A intro; warm-up (a < n) is the
+    shortened staircase of [PL] §A.2 with the prefix at depth n.
+    """
+    return ([n] if pending else []) + list(range(a - 1, -1, -1))
+
+
+def key_depth(t: int, T: int, fill: int, n: int) -> int:
+    """Depth at which position T appears in the feature sequence of step t.
+
+    [PL] §A.3: a query at step t and depth d sees key T at depth
+    min(n, d + t - T); keys further back than the fill level are redirected to
+    the deepest block.  For the newest query (d = 0) with `fill` tokens in
+    flight this is t - T when t - T < fill, else n.  Used as an independent
+    formulation that pins `depth_layout` and the state machine's depths.
+    """
+    assert T <= t
+    dist = t - T
+    return dist if dist < fill else n
+
+
+def cycle_count(n: int, G: int, rejects: int) -> int:
+    """Cycles needed to emit G tokens (the first from prefill) with R rejects.
+
+    Derived here from the schedule, not printed on the pages: the first exit
+    happens at cycle n; every later verification needs one more cycle, and a
+    rejection among the first G-2 verifications costs n-1 refill cycles.
+    [TW] §8 defines alpha = N/K and the SPD speedup alpha*n from this count.
+    """
+    return n + (G - 2) + (n - 1) * rejects
+
+
+def validate_shape(L: int, n: int, Ls: int, anchors: Sequence[int]) -> None:
+    """Constraints the pages fix: n | L ([RB] core method), Ls <= L/n
+    ([RB] core method / technical novelty: S = S0 iff Ls <= L/n), anchors
+    strictly increasing from 0 and within L ([RB] core method)."""
+    if L % n:
+        raise ValueError("n must divide L")
+    if Ls > L // n:
+        raise ValueError("draft module deeper than one stage")
+    if anchors[0] != 0 or any(b >= c for b, c in zip(anchors, anchors[1:])) or anchors[-1] > L:
+        raise ValueError("anchors must increase strictly from 0 and stay <= L")

@@ -1,0 +1,14 @@
+"""Shared pytest configuration: markers are declared in pytest.ini.
+
+GPU tests are marked `gpu`; everything else runs on the CPU.
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
