@@ -1,0 +1,204 @@
+// Internal declarations shared by the libspd HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spd.h"
+
+namespace spd {
+
+constexpr int kWG = 256;          // threads per workgroup for the streaming kernels
+constexpr int kWave = 64;         // CDNA wavefront
+constexpr int kSplit = 256;       // attention positions per split (one per thread)
+constexpr int kMaxQ = 16;         // query vectors per attention workgroup
+constexpr int kRowsMR = 16;       // activation rows per pass of the row-batched GEMV
+constexpr int kGemvRowsPerWave = 4;
+constexpr int kGemvRowsPerWG = kGemvRowsPerWave * (kWG / kWave);  // 16
+
+// Device control block.  Written by the entry kernel (cycle state), the
+// verification kernel (r_*, reseed, seed_*, pend_next, emitted, done) and the
+// draft finalisation kernel (r_draft, r_raw, C); every field has one writer
+// per cycle, and each cycle's readers run after that writer.
+struct Ctrl {
+  int32_t t;          // newest in-flight position (this cycle's seed)
+  int32_t a;          // occupancy after entry
+  int32_t pending;    // this cycle commits the full-depth row at position C
+  int32_t C;          // PDM committed length
+  int32_t emitted;    // tokens emitted (incl. the prefill token)
+  int32_t done;       // emitted == max_new
+  int32_t active;     // this cycle does work
+  int32_t cycle;      // cycles executed
+  int32_t reseed;     // next entry starts an empty pipeline at (seed_tok, seed_pos)
+  int32_t seed_tok;
+  int32_t seed_pos;
+  int32_t pend_next;  // the next cycle has a row to commit
+  int32_t r_exit;     // last cycle: exit position or -1
+  int32_t r_accept;
+  int32_t r_y;
+  int32_t r_draft;    // last cycle: draft for t+1
+  int32_t r_raw;      // last cycle: PDM argmax / draw
+  uint32_t flags;     // accumulated SPD_FLAG_*
+  int32_t ar_pos;     // position of the token the AR decoder processes next
+  int32_t pad[13];
+};
+
+struct ArgPair {
+  float v;
+  int32_t i;
+};
+
+// A token id from an argmax/draw, forced into [0, V); flags non-finite input.
+__device__ __forceinline__ int valid_token(int y, int V, uint32_t* flags) {
+  if (y < 0 || y >= V) {
+    atomicOr(flags, SPD_FLAG_BADTOKEN);
+    return 0;
+  }
+  return y;
+}
+
+__device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// 16 bytes of weights as floats: 8 bf16 or 4 fp32 elements.
+template <typename WT>
+struct WVec;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <>
+struct WVec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const uint16_t* p, float* out) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    out[0] = __uint_as_float(v.x << 16);
+    out[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    out[2] = __uint_as_float(v.y << 16);
+    out[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    out[4] = __uint_as_float(v.z << 16);
+    out[5] = __uint_as_float(v.z & 0xFFFF0000u);
+    out[6] = __uint_as_float(v.w << 16);
+    out[7] = __uint_as_float(v.w & 0xFFFF0000u);
+  }
+};
+template <>
+struct WVec<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float* out) {
+    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    out[0] = v.x;
+    out[1] = v.y;
+    out[2] = v.z;
+    out[3] = v.w;
+  }
+};
+
+// Storage of KV-cache elements.
+template <typename KT>
+__device__ __forceinline__ KT to_store(float v);
+template <>
+__device__ __forceinline__ float to_store<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t to_store<uint16_t>(float v) { return f32_to_bf16_rne(v); }
+__device__ __forceinline__ float from_store(float v) { return v; }
+__device__ __forceinline__ float from_store(uint16_t v) { return bf16_bits_to_f32(v); }
+
+// Butterfly sum over the 64 lanes; every lane ends with the identical value.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v2 = __shfl_xor(v, o, 64);
+    int i2 = __shfl_xor(i, o, 64);
+    if (better(v2, i2, v, i)) {
+      v = v2;
+      i = i2;
+    }
+  }
+}
+
+// Block sum over kWG threads in a fixed order (waves 0,1,2,3); all threads
+// get the same value.  `red` is kWG/kWave floats of shared memory.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x % kWave) == 0) red[w] = v;
+  __syncthreads();
+  float s = red[0];
+#pragma unroll
+  for (int i = 1; i < kWG / kWave; ++i) s += red[i];
+  return s;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x % kWave) == 0) red[w] = v;
+  __syncthreads();
+  float s = red[0];
+#pragma unroll
+  for (int i = 1; i < kWG / kWave; ++i) s = fmaxf(s, red[i]);
+  return s;
+}
+
+// Sum of squares of x[0..K) by kWG threads, fixed order; returns
+// 1/sqrt(mean + eps).  Every kernel that normalises a row uses this, so the
+// same row gets the same scale everywhere.
+__device__ __forceinline__ float row_rstd(const float* __restrict__ x, int K, float eps, float* red) {
+  float s = 0.f;
+  for (int i = threadIdx.x; i < K; i += kWG) s = fmaf(x[i], x[i], s);
+  s = block_sum(s, red);
+  return 1.0f / sqrtf(s / (float)K + eps);
+}
+
+// Geometry of the engine, passed by value to kernels.
+struct Geo {
+  int L, d, Hq, Hkv, hd, F, V, n, Ls, m;
+  int per;       // layers per stage
+  int nslots;    // n + 1: position-indexed ring of in-flight slots
+  int ctx_cap;   // KV capacity (positions), multiple of kSplit
+  int nsplit;    // ctx_cap / kSplit
+  int qkv_rows;  // (Hq + 2 Hkv) hd
+  int max_new;
+  int max_ctx;   // positions must stay below this (uniform-table rows, KV capacity)
+  float eps;
+  int anchor_of_layer[SPD_MAX_LAYERS + 1];  // anchor index of boundary b, or -1
+  int fpat[SPD_MAX_STAGES + 1];             // f(k) for k = 0..n
+};
+
+// KV-cache addressing.  K is stored [layer][kvh][hd/8][ctx][8] so that
+// consecutive positions are consecutive 16-byte chunks (one position per
+// lane in the score loop); V is [layer][kvh][ctx][hd].
+__device__ __forceinline__ size_t k_index(const Geo& g, int layer, int kvh, int pos, int dim) {
+  return ((((size_t)layer * g.Hkv + kvh) * (g.hd / 8) + (dim >> 3)) * g.ctx_cap + pos) * 8 + (dim & 7);
+}
+__device__ __forceinline__ size_t v_index(const Geo& g, int layer, int kvh, int pos, int dim) {
+  return (((size_t)layer * g.Hkv + kvh) * g.ctx_cap + pos) * g.hd + dim;
+}
+
+}  // namespace spd

@@ -1,0 +1,1062 @@
+// libspd: host orchestration and the C ABI declared in spd.h.
+//
+// Per cycle the host enqueues, without waiting:
+//   stage stream:  wait(previous draft done) -> entry -> record(E_entry)
+//                  -> L/n x [qkv+RoPE+KV append, split-KV attention, combine,
+//                            o-proj + residual, norm + gate/up + SwiGLU,
+//                            down + residual + anchor taps]
+//                  -> verification head -> verify / rollback
+//   draft stream:  wait(E_entry) -> anchor gather + FC -> Ls x [the same layer
+//                  over the trailing rows] -> draft head -> finalise -> record(E_pdm)
+// The draft module reads only pre-step state, so the two streams overlap; the
+// next cycle's entry joins them.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "attention.h"
+#include "common.h"
+#include "control.h"
+#include "gemv.h"
+
+using namespace spd;
+
+namespace {
+
+constexpr int kPersistPerCU = 4;
+constexpr int kCUs = 256;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+  size_t ctrl, kv_len, tokens, dring, qring, qz, kc, vc, pkc, pvc, rcos, rsin, hslots, anchors;
+  size_t s_q, s_pacc, s_pml, s_o, s_act;
+  size_t Xt, Xp, r_q, r_pacc, r_pml, r_o, r_act, taps;
+  size_t logits, plogits, pw, parts, pparts, ring;
+  size_t total;
+  int ctx_cap, nsplit, mr, log_cap, nparts_max;
+};
+
+bool valid_config(const spd_config* c) {
+  if (!c) return false;
+  if (c->n_layers < 1 || c->n_layers > SPD_MAX_LAYERS) return false;
+  if (c->n_stages < 1 || c->n_stages > SPD_MAX_STAGES || c->n_layers % c->n_stages) return false;
+  if (c->pdm_layers < 1 || c->pdm_layers > SPD_MAX_PDM_LAYERS || c->pdm_layers > c->n_layers / c->n_stages)
+    return false;
+  if (c->n_anchors < 1 || c->n_anchors > SPD_MAX_ANCHORS || c->anchors[0] != 0) return false;
+  for (int i = 1; i < c->n_anchors; ++i)
+    if (c->anchors[i] <= c->anchors[i - 1]) return false;
+  if (c->anchors[c->n_anchors - 1] > c->n_layers) return false;
+  if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return false;
+  if (c->head_dim != 64 && c->head_dim != 128) return false;
+  const int G = c->n_heads / c->n_kv_heads;
+  if (G > kMaxQ) return false;
+  if (c->d_model % 256 || c->d_ffn % 256 || (c->n_heads * c->head_dim) % 256) return false;
+  if (c->d_model * c->n_anchors > 64 * 1024) return false;
+  if (c->d_ffn > 12288 || c->d_model > 12288 || c->n_heads * c->head_dim > 12288) return false;
+  if (c->vocab < 2) return false;
+  if (c->dtype != SPD_DTYPE_F32 && c->dtype != SPD_DTYPE_BF16) return false;
+  if (c->mode != SPD_MODE_GREEDY && c->mode != SPD_MODE_SAMPLE) return false;
+  if (c->mode == SPD_MODE_SAMPLE && !(c->temperature > 0.f)) return false;
+  if (c->max_new < 1 || c->max_ctx < c->n_stages + 2) return false;
+  if (!(c->rms_eps >= 0.f) || !(c->rope_base > 1.f)) return false;
+  return true;
+}
+
+Layout make_layout(const spd_config* c) {
+  Layout L{};
+  const size_t es = c->dtype == SPD_DTYPE_BF16 ? 2 : 4;
+  const int n = c->n_stages, d = c->d_model, Hq = c->n_heads, Hkv = c->n_kv_heads, hd = c->head_dim;
+  const int F = c->d_ffn, V = c->vocab, m = c->n_anchors;
+  L.ctx_cap = (int)align_up((size_t)c->max_ctx, kSplit);
+  L.nsplit = L.ctx_cap / kSplit;
+  L.mr = std::max(kRowsMR, (int)align_up((size_t)(n + 1), kRowsMR));
+  L.log_cap = std::max(4096, n * c->max_new + 64);
+  L.nparts_max = kCUs * kPersistPerCU;
+  const int nslots = n + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  L.ctrl = take(sizeof(Ctrl));
+  L.kv_len = take(sizeof(int32_t) * SPD_MAX_LAYERS);
+  L.tokens = take(sizeof(int32_t) * L.ctx_cap);
+  L.dring = take(sizeof(int32_t) * nslots);
+  const bool smp = c->mode == SPD_MODE_SAMPLE;
+  L.qring = take(smp ? sizeof(float) * nslots * (size_t)V : 0);
+  L.qz = take(sizeof(double) * nslots);
+  const size_t kvl = (size_t)Hkv * hd * L.ctx_cap * es;
+  L.kc = take(kvl * c->n_layers);
+  L.vc = take(kvl * c->n_layers);
+  L.pkc = take(kvl * c->pdm_layers);
+  L.pvc = take(kvl * c->pdm_layers);
+  L.rcos = take(sizeof(float) * (size_t)L.ctx_cap * (hd / 2));
+  L.rsin = take(sizeof(float) * (size_t)L.ctx_cap * (hd / 2));
+  L.hslots = take(sizeof(float) * (size_t)nslots * d);
+  L.anchors = take(sizeof(float) * (size_t)nslots * m * d);
+  const size_t qd = (size_t)Hq * hd;
+  L.s_q = take(sizeof(float) * n * qd);
+  L.s_pacc = take(sizeof(float) * n * (size_t)Hq * L.nsplit * hd);
+  L.s_pml = take(sizeof(float) * n * (size_t)Hq * L.nsplit * 2);
+  L.s_o = take(sizeof(float) * n * qd);
+  L.s_act = take(sizeof(float) * n * (size_t)F);
+  L.Xt = take(sizeof(float) * L.mr * (size_t)d);
+  L.Xp = take(sizeof(float) * L.mr * (size_t)d);
+  L.r_q = take(sizeof(float) * L.mr * qd);
+  L.r_pacc = take(sizeof(float) * L.mr * (size_t)Hq * L.nsplit * hd);
+  L.r_pml = take(sizeof(float) * L.mr * (size_t)Hq * L.nsplit * 2);
+  L.r_o = take(sizeof(float) * L.mr * qd);
+  L.r_act = take(sizeof(float) * L.mr * (size_t)F);
+  L.taps = take(sizeof(float) * kRowsMR * (size_t)m * d);
+  L.logits = take(sizeof(float) * (size_t)V);
+  L.plogits = take(sizeof(float) * (size_t)V);
+  L.pw = take(sizeof(float) * (size_t)V);
+  L.parts = take(sizeof(ArgPair) * L.nparts_max);
+  L.pparts = take(sizeof(ArgPair) * L.nparts_max);
+  L.ring = take(sizeof(spd_cycle_rec) * (size_t)L.log_cap);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct spd_handle {
+  spd_config cfg;
+  spd_weights w;
+  Geo g;
+  Layout lay;
+  hipStream_t ss, ps;
+  hipEvent_t ev_entry, ev_pdm;
+  char* ws;
+  Ctrl* ctrl;
+  int32_t *kv_len, *tokens, *dring;
+  float* qring;
+  double* qz;
+  void *kc, *vc, *pkc, *pvc;
+  float *rcos, *rsin, *hslots, *anchors;
+  float *s_q, *s_pacc, *s_pml, *s_o, *s_act;
+  float *Xt, *Xp, *r_q, *r_pacc, *r_pml, *r_o, *r_act, *taps;
+  float *logits, *plogits, *pw;
+  ArgPair *parts, *pparts;
+  spd_cycle_rec* ring;
+  int policy = SPD_DRAFT_NATURAL;
+  float p_accept = 0.f;
+  const int32_t* ref = nullptr;
+  int ref_len = 0;
+  const float* uni = nullptr;
+  int uni_len = 0;
+  int prefilled = 0, P = 0, needs_rollback = 0, ar_complete = 0;
+  long long cyc = 0;
+  int hip_err = 0;
+  // timing
+  int timing = 0;
+  std::vector<hipEvent_t> pool;
+  size_t pool_next = 0;
+  std::vector<hipEvent_t> cyc_ev;   // 3 per timed cycle: start, stage end, pdm end
+  std::vector<hipEvent_t> gu_ev;    // 2 per timed gate/up launch
+};
+
+#define HIPCHK(h, x)                          \
+  do {                                        \
+    hipError_t _e = (x);                      \
+    if (_e != hipSuccess) {                   \
+      (h)->hip_err = (int)_e;                 \
+      return SPD_EHIP;                        \
+    }                                         \
+  } while (0)
+
+namespace {
+
+hipEvent_t pool_event(spd_t* h) {
+  if (h->pool_next == h->pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    h->pool.push_back(e);
+  }
+  return h->pool[h->pool_next++];
+}
+
+int stage_grid(int units, int upt, int n_groups, int K) {
+  const int tiles = n_groups * ((units + upt - 1) / upt);
+  const int lds = K * (int)sizeof(float) + 512;
+  const int occ = std::max(1, std::min(kPersistPerCU, 160 * 1024 / lds));
+  return std::max(1, std::min(tiles, kCUs * occ));
+}
+
+template <typename WT, int EPI>
+void launch_stage(spd_t* h, const StageGemv& a, int n_groups_max, hipStream_t s, int* grid_out = nullptr) {
+  constexpr int upt = (epi_pairs(EPI) ? 2 : 4) * (kWG / kWave);
+  const int grid = stage_grid(a.units, upt, n_groups_max, a.K);
+  if (grid_out) *grid_out = grid;
+  hipLaunchKernelGGL((k_gemv_stage<WT, EPI>), dim3(grid), dim3(kWG), a.K * sizeof(float), s, a);
+}
+
+template <typename WT, int EPI>
+void launch_rows(spd_t* h, RowsGemv a, int max_rows, hipStream_t s) {
+  constexpr int upt = (epi_pairs(EPI) ? 2 : 4) * (kWG / kWave);
+  const int tiles = (a.units + upt - 1) / upt;
+  for (int rb = 0; rb < max_rows; rb += kRowsMR) {
+    a.row_base = rb;
+    hipLaunchKernelGGL((k_gemv_rows<WT, EPI>), dim3(tiles, a.n_groups), dim3(kWG), 0, s, a);
+    if (a.rmode == RM_FC) break;
+  }
+}
+
+StageGemv stage_base(spd_t* h) {
+  StageGemv a;
+  memset(&a, 0, sizeof(a));
+  for (int i = 0; i < SPD_MAX_STAGES; ++i) a.anchor_idx[i] = -1;
+  a.ctrl = h->ctrl;
+  a.g = h->g;
+  a.rcos = h->rcos;
+  a.rsin = h->rsin;
+  return a;
+}
+
+RowsGemv rows_base(spd_t* h) {
+  RowsGemv a;
+  memset(&a, 0, sizeof(a));
+  a.anchor_idx = -1;
+  a.ctrl = h->ctrl;
+  a.g = h->g;
+  a.rcos = h->rcos;
+  a.rsin = h->rsin;
+  a.n_groups = 1;
+  return a;
+}
+
+// One decoder layer over row-batched activations X (target prefill chunk,
+// autoregressive token, or the draft module's trailing rows).
+template <typename WT>
+void rows_layer(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int layer, float* X, int M,
+                int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s) {
+  const Geo& g = h->g;
+  const int max_rows = from_ctrl ? g.n + 1 : M;
+  const int qd = g.Hq * g.hd;
+  RowsGemv a = rows_base(h);
+  a.from_ctrl = from_ctrl;
+  a.M_arg = M;
+  a.pos0_arg = pos0;
+  // q/k/v + RoPE + cache append
+  a.W[0] = lw.w_qkv;
+  a.Kg[0] = g.d;
+  a.gamma = (const float*)lw.attn_norm;
+  a.N = g.qkv_rows;
+  a.units = g.qkv_rows / 2;
+  a.x = X;
+  a.ldx = g.d;
+  a.out = h->r_q;
+  a.ldo = qd;
+  a.layer = layer;
+  a.kc = kc;
+  a.vc = vc;
+  a.kv_len = kv_len;
+  launch_rows<WT, EPI_QKV>(h, a, max_rows, s);
+  // attention
+  Attn t;
+  memset(&t, 0, sizeof(t));
+  t.pmode = PM_ROWS;
+  t.layer[0] = layer;
+  t.kc = kc;
+  t.vc = vc;
+  t.q = h->r_q;
+  t.pacc = h->r_pacc;
+  t.pml = h->r_pml;
+  t.o = h->r_o;
+  t.from_ctrl = from_ctrl;
+  t.pos0_arg = pos0;
+  t.nrows_arg = M;
+  t.QB = std::max(1, kMaxQ / (g.Hq / g.Hkv));
+  t.ctrl = h->ctrl;
+  t.g = g;
+  const int qblocks = (max_rows + t.QB - 1) / t.QB;
+  hipLaunchKernelGGL((k_attn<WT>), dim3(g.nsplit, g.Hkv * qblocks, 1), dim3(kWG), 0, s, t);
+  hipLaunchKernelGGL(k_attn_combine, dim3(g.Hq, max_rows), dim3(128), 0, s, t);
+  // output projection + residual
+  a = rows_base(h);
+  a.from_ctrl = from_ctrl;
+  a.M_arg = M;
+  a.pos0_arg = pos0;
+  a.W[0] = lw.w_o;
+  a.Kg[0] = qd;
+  a.N = g.d;
+  a.units = g.d;
+  a.x = h->r_o;
+  a.ldx = qd;
+  a.out = X;
+  a.ldo = g.d;
+  launch_rows<WT, EPI_RESID>(h, a, max_rows, s);
+  // norm + gate/up + SwiGLU
+  a.W[0] = lw.w_gu;
+  a.Kg[0] = g.d;
+  a.gamma = (const float*)lw.ffn_norm;
+  a.N = 2 * g.F;
+  a.units = g.F;
+  a.x = X;
+  a.ldx = g.d;
+  a.out = h->r_act;
+  a.ldo = g.F;
+  launch_rows<WT, EPI_SWIGLU>(h, a, max_rows, s);
+  // down + residual (+ anchor taps)
+  a.W[0] = lw.w_down;
+  a.Kg[0] = g.F;
+  a.gamma = nullptr;
+  a.N = g.d;
+  a.units = g.d;
+  a.x = h->r_act;
+  a.ldx = g.F;
+  a.out = X;
+  a.ldo = g.d;
+  a.anchors = taps;
+  a.anchor_idx = anchor_idx;
+  launch_rows<WT, EPI_RESID>(h, a, max_rows, s);
+}
+
+// Head GEMV (final norm + LM head + per-workgroup argmax) on a fixed input row.
+template <typename WT>
+int head_fixed(spd_t* h, const float* x, const void* W, const void* gamma, float* logits, ArgPair* parts,
+               hipStream_t s) {
+  StageGemv a = stage_base(h);
+  a.W[0] = W;
+  a.gamma[0] = (const float*)gamma;
+  a.N = h->g.V;
+  a.K = h->g.d;
+  a.units = h->g.V;
+  a.n_groups = 1;
+  a.gmode = GM_FIXED;
+  a.x = x;
+  a.out = logits;
+  a.parts = parts;
+  int grid = 0;
+  launch_stage<WT, EPI_ARGMAX>(h, a, 1, s, &grid);
+  return grid;
+}
+
+template <typename WT>
+int enqueue_cycle(spd_t* h) {
+  const Geo& g = h->g;
+  const spd_weights& w = h->w;
+  hipStream_t ss = h->ss, ps = h->ps;
+  const int c = (int)(h->cyc % 0x7FFFFFFF);
+  hipEvent_t e_start = nullptr, e_stage = nullptr, e_pdm_t = nullptr;
+  if (h->timing) {
+    e_start = pool_event(h);
+    e_stage = pool_event(h);
+    e_pdm_t = pool_event(h);
+  }
+  HIPCHK(h, hipStreamWaitEvent(ss, h->ev_pdm, 0));
+  if (e_start) HIPCHK(h, hipEventRecord(e_start, ss));
+  hipLaunchKernelGGL((k_entry<WT>), dim3(1), dim3(kWG), 0, ss, h->ctrl, g, h->tokens, (const WT*)w.embed,
+                     h->hslots, h->anchors, h->ring, h->lay.log_cap, c);
+  HIPCHK(h, hipEventRecord(h->ev_entry, ss));
+  HIPCHK(h, hipStreamWaitEvent(ps, h->ev_entry, 0));
+
+  // ---------------- draft module (pre-step) on the draft stream ----------------
+  {
+    RowsGemv a = rows_base(h);
+    a.rmode = RM_FC;
+    a.from_ctrl = 1;
+    a.n_groups = g.m;
+    for (int f = 0; f < g.m; ++f) {
+      a.W[f] = w.fc[f];
+      a.Kg[f] = (f + 1) * g.d;
+    }
+    a.N = g.d;
+    a.units = g.d;
+    a.out = h->Xp;
+    a.ldo = g.d;
+    a.slot_anchors = h->anchors;
+    launch_rows<WT, EPI_STORE>(h, a, g.n + 1, ps);
+    for (int l = 0; l < g.Ls; ++l)
+      rows_layer<WT>(h, w.pdm[l], h->pkc, h->pvc, l, h->Xp, 0, 0, 1, nullptr, nullptr, -1, ps);
+    StageGemv hd = stage_base(h);
+    hd.W[0] = w.pdm_lm_head;
+    hd.gamma[0] = (const float*)w.pdm_final_norm;
+    hd.N = g.V;
+    hd.K = g.d;
+    hd.units = g.V;
+    hd.n_groups = 1;
+    hd.gmode = GM_PDMLAST;
+    hd.x = h->Xp;
+    hd.x_stride = g.d;
+    hd.out = h->plogits;
+    hd.parts = h->pparts;
+    int grid = 0;
+    launch_stage<WT, EPI_ARGMAX>(h, hd, 1, ps, &grid);
+    FinalizeArgs f;
+    memset(&f, 0, sizeof(f));
+    f.parts = h->pparts;
+    f.nparts = grid;
+    f.logits = h->plogits;
+    f.dring = h->dring;
+    f.qring = h->qring;
+    f.qz = h->qz;
+    f.uni = h->uni;
+    f.mode = h->cfg.mode;
+    f.temp = h->cfg.temperature;
+    f.policy = h->policy;
+    f.p_accept = h->p_accept;
+    f.ref = h->ref;
+    f.ref_len = h->ref_len;
+    f.ring = h->ring;
+    f.log_cap = h->lay.log_cap;
+    f.cyc = c;
+    f.ctrl = h->ctrl;
+    f.g = g;
+    hipLaunchKernelGGL(k_pdm_finalize, dim3(1), dim3(kCtlThreads), 0, ps, f);
+    if (e_pdm_t) HIPCHK(h, hipEventRecord(e_pdm_t, ps));
+    HIPCHK(h, hipEventRecord(h->ev_pdm, ps));
+  }
+
+  // ---------------- stage step on the stage stream ----------------
+  const int qd = g.Hq * g.hd;
+  for (int j = 0; j < g.per; ++j) {
+    StageGemv a = stage_base(h);
+    a.n_groups = g.n;
+    a.gmode = GM_STAGE;
+    for (int k = 0; k < g.n; ++k) a.layer[k] = k * g.per + j;
+    // q/k/v + RoPE + KV append
+    for (int k = 0; k < g.n; ++k) {
+      a.W[k] = w.layers[a.layer[k]].w_qkv;
+      a.gamma[k] = (const float*)w.layers[a.layer[k]].attn_norm;
+    }
+    a.N = g.qkv_rows;
+    a.K = g.d;
+    a.units = g.qkv_rows / 2;
+    a.x = h->hslots;
+    a.x_stride = g.d;
+    a.x_by_slot = 1;
+    a.out = h->s_q;
+    a.out_stride = qd;
+    a.kc = h->kc;
+    a.vc = h->vc;
+    a.kv_len = h->kv_len;
+    launch_stage<WT, EPI_QKV>(h, a, g.n, ss);
+    // attention over each group's own layer cache
+    Attn t;
+    memset(&t, 0, sizeof(t));
+    t.pmode = PM_STAGE;
+    for (int k = 0; k < g.n; ++k) t.layer[k] = a.layer[k];
+    t.kc = h->kc;
+    t.vc = h->vc;
+    t.q = h->s_q;
+    t.pacc = h->s_pacc;
+    t.pml = h->s_pml;
+    t.o = h->s_o;
+    t.ctrl = h->ctrl;
+    t.g = g;
+    hipLaunchKernelGGL((k_attn<WT>), dim3(g.nsplit, g.Hkv, g.n), dim3(kWG), 0, ss, t);
+    hipLaunchKernelGGL(k_attn_combine, dim3(g.Hq, g.n), dim3(128), 0, ss, t);
+    // output projection + residual
+    StageGemv o = stage_base(h);
+    o.n_groups = g.n;
+    o.gmode = GM_STAGE;
+    for (int k = 0; k < g.n; ++k) {
+      o.layer[k] = a.layer[k];
+      o.W[k] = w.layers[a.layer[k]].w_o;
+    }
+    o.N = g.d;
+    o.K = qd;
+    o.units = g.d;
+    o.x = h->s_o;
+    o.x_stride = qd;
+    o.out = h->hslots;
+    o.out_stride = g.d;
+    o.out_by_slot = 1;
+    launch_stage<WT, EPI_RESID>(h, o, g.n, ss);
+    // norm + gate/up + SwiGLU
+    StageGemv u = stage_base(h);
+    u.n_groups = g.n;
+    u.gmode = GM_STAGE;
+    for (int k = 0; k < g.n; ++k) {
+      u.layer[k] = a.layer[k];
+      u.W[k] = w.layers[a.layer[k]].w_gu;
+      u.gamma[k] = (const float*)w.layers[a.layer[k]].ffn_norm;
+    }
+    u.N = 2 * g.F;
+    u.K = g.d;
+    u.units = g.F;
+    u.x = h->hslots;
+    u.x_stride = g.d;
+    u.x_by_slot = 1;
+    u.out = h->s_act;
+    u.out_stride = g.F;
+    hipEvent_t g0 = nullptr, g1 = nullptr;
+    if (h->timing) {
+      g0 = pool_event(h);
+      g1 = pool_event(h);
+      HIPCHK(h, hipEventRecord(g0, ss));
+    }
+    launch_stage<WT, EPI_SWIGLU>(h, u, g.n, ss);
+    if (g1) {
+      HIPCHK(h, hipEventRecord(g1, ss));
+      h->gu_ev.push_back(g0);
+      h->gu_ev.push_back(g1);
+    }
+    // down + residual + anchor taps
+    StageGemv dn = stage_base(h);
+    dn.n_groups = g.n;
+    dn.gmode = GM_STAGE;
+    for (int k = 0; k < g.n; ++k) {
+      dn.layer[k] = a.layer[k];
+      dn.W[k] = w.layers[a.layer[k]].w_down;
+      dn.anchor_idx[k] = g.anchor_of_layer[a.layer[k] + 1];
+    }
+    dn.N = g.d;
+    dn.K = g.F;
+    dn.units = g.d;
+    dn.x = h->s_act;
+    dn.x_stride = g.F;
+    dn.out = h->hslots;
+    dn.out_stride = g.d;
+    dn.out_by_slot = 1;
+    dn.anchors = h->anchors;
+    launch_stage<WT, EPI_RESID>(h, dn, g.n, ss);
+  }
+  // verification head on the exiting token, then verify / rollback
+  StageGemv hd = stage_base(h);
+  hd.W[0] = w.lm_head;
+  hd.gamma[0] = (const float*)w.final_norm;
+  hd.N = g.V;
+  hd.K = g.d;
+  hd.units = g.V;
+  hd.n_groups = 1;
+  hd.gmode = GM_EXIT;
+  hd.x = h->hslots;
+  hd.x_stride = g.d;
+  hd.x_by_slot = 1;
+  hd.out = h->logits;
+  hd.parts = h->parts;
+  int grid = 0;
+  launch_stage<WT, EPI_ARGMAX>(h, hd, 1, ss, &grid);
+  VerifyArgs v;
+  memset(&v, 0, sizeof(v));
+  v.parts = h->parts;
+  v.nparts = grid;
+  v.logits = h->logits;
+  v.pw = h->pw;
+  v.dring = h->dring;
+  v.qring = h->qring;
+  v.qz = h->qz;
+  v.uni = h->uni;
+  v.mode = h->cfg.mode;
+  v.temp = h->cfg.temperature;
+  v.tokens = h->tokens;
+  v.kv_len = h->kv_len;
+  v.ring = h->ring;
+  v.log_cap = h->lay.log_cap;
+  v.cyc = c;
+  v.ctrl = h->ctrl;
+  v.g = g;
+  hipLaunchKernelGGL(k_verify, dim3(1), dim3(kCtlThreads), 0, ss, v);
+  if (e_stage) {
+    HIPCHK(h, hipEventRecord(e_stage, ss));
+    h->cyc_ev.push_back(e_start);
+    h->cyc_ev.push_back(e_stage);
+    h->cyc_ev.push_back(e_pdm_t);
+  }
+  HIPCHK(h, hipGetLastError());
+  h->cyc += 1;
+  return SPD_OK;
+}
+
+template <typename WT>
+int do_prefill(spd_t* h, int P) {
+  const Geo& g = h->g;
+  const spd_weights& w = h->w;
+  hipStream_t s = h->ss;
+  for (int s0 = 0; s0 < P; s0 += kRowsMR) {
+    const int M = std::min(kRowsMR, P - s0);
+    hipLaunchKernelGGL((k_embed_rows<WT>), dim3(M), dim3(kWG), 0, s, h->tokens, s0, (const WT*)w.embed, g.d, h->Xt,
+                       h->taps, g.m);
+    for (int l = 0; l < g.L; ++l)
+      rows_layer<WT>(h, w.layers[l], h->kc, h->vc, l, h->Xt, M, s0, 0, h->kv_len, h->taps,
+                     g.anchor_of_layer[l + 1], s);
+    // draft module prefill on the full-depth features of the chunk
+    RowsGemv a = rows_base(h);
+    a.M_arg = M;
+    a.pos0_arg = s0;
+    a.W[0] = w.fc[g.m - 1];
+    a.Kg[0] = g.m * g.d;
+    a.N = g.d;
+    a.units = g.d;
+    a.x = h->taps;
+    a.ldx = g.m * g.d;
+    a.out = h->Xp;
+    a.ldo = g.d;
+    launch_rows<WT, EPI_STORE>(h, a, M, s);
+    for (int l = 0; l < g.Ls; ++l)
+      rows_layer<WT>(h, w.pdm[l], h->pkc, h->pvc, l, h->Xp, M, s0, 0, nullptr, nullptr, -1, s);
+    if (s0 + M == P) {
+      const int grid = head_fixed<WT>(h, h->Xt + (size_t)(M - 1) * g.d, w.lm_head, w.final_norm, h->logits,
+                                      h->parts, s);
+      hipLaunchKernelGGL(k_pick_token, dim3(1), dim3(kCtlThreads), 0, s, h->parts, grid, h->logits, h->pw, g.V,
+                         h->cfg.mode, h->cfg.temperature, h->uni, h->tokens, P, h->ctrl, &h->ctrl->flags);
+    }
+  }
+  HIPCHK(h, hipGetLastError());
+  return SPD_OK;
+}
+
+template <typename WT>
+int do_ar(spd_t* h, int s0, int n) {
+  const Geo& g = h->g;
+  const spd_weights& w = h->w;
+  hipStream_t s = h->ss;
+  for (int i = 0; i < n; ++i) {
+    const int pos = s0 + i;
+    hipLaunchKernelGGL((k_embed_rows<WT>), dim3(1), dim3(kWG), 0, s, h->tokens, pos, (const WT*)w.embed, g.d,
+                       h->Xt, (float*)nullptr, g.m);
+    for (int l = 0; l < g.L; ++l)
+      rows_layer<WT>(h, w.layers[l], h->kc, h->vc, l, h->Xt, 1, pos, 0, h->kv_len, nullptr, -1, s);
+    const int grid = head_fixed<WT>(h, h->Xt, w.lm_head, w.final_norm, h->logits, h->parts, s);
+    hipLaunchKernelGGL(k_pick_token, dim3(1), dim3(kCtlThreads), 0, s, h->parts, grid, h->logits, h->pw, g.V,
+                       SPD_MODE_GREEDY, 1.0f, h->uni, h->tokens, pos + 1, (Ctrl*)nullptr, &h->ctrl->flags);
+  }
+  HIPCHK(h, hipGetLastError());
+  return SPD_OK;
+}
+
+int read_ctrl(spd_t* h, Ctrl* c) {
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  HIPCHK(h, hipStreamSynchronize(h->ps));
+  HIPCHK(h, hipMemcpy(c, h->ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost));
+  return SPD_OK;
+}
+
+int write_ctrl(spd_t* h, const Ctrl* c) {
+  HIPCHK(h, hipMemcpy(h->ctrl, c, sizeof(Ctrl), hipMemcpyHostToDevice));
+  return SPD_OK;
+}
+
+int set_kv_len(spd_t* h, int len) {
+  std::vector<int32_t> v(SPD_MAX_LAYERS, len);
+  HIPCHK(h, hipMemcpy(h->kv_len, v.data(), sizeof(int32_t) * SPD_MAX_LAYERS, hipMemcpyHostToDevice));
+  return SPD_OK;
+}
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+extern "C" {
+
+int spd_workspace_bytes(const spd_config* cfg, size_t* bytes) {
+  if (!valid_config(cfg) || !bytes) return SPD_EINVAL;
+  *bytes = make_layout(cfg).total;
+  return SPD_OK;
+}
+
+int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_t ws_bytes, void* stage_stream,
+             void* pdm_stream, spd_t** out) {
+  if (!out) return SPD_EINVAL;
+  *out = nullptr;
+  if (!valid_config(cfg) || !w || !workspace) return SPD_EINVAL;
+  if (stage_stream == pdm_stream) return SPD_EINVAL;
+  if (((uintptr_t)workspace) % kAlign) return SPD_EINVAL;
+  Layout L = make_layout(cfg);
+  if (ws_bytes < L.total) return SPD_EINVAL;
+  if (!w->embed || !w->final_norm || !w->lm_head || !w->pdm_final_norm || !w->pdm_lm_head) return SPD_EINVAL;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const spd_layer_weights& x = w->layers[l];
+    if (!x.attn_norm || !x.w_qkv || !x.w_o || !x.ffn_norm || !x.w_gu || !x.w_down) return SPD_EINVAL;
+  }
+  for (int l = 0; l < cfg->pdm_layers; ++l) {
+    const spd_layer_weights& x = w->pdm[l];
+    if (!x.attn_norm || !x.w_qkv || !x.w_o || !x.ffn_norm || !x.w_gu || !x.w_down) return SPD_EINVAL;
+  }
+  for (int f = 0; f < cfg->n_anchors; ++f)
+    if (!w->fc[f]) return SPD_EINVAL;
+
+  spd_t* h = new (std::nothrow) spd_handle();
+  if (!h) return SPD_EINVAL;
+  h->cfg = *cfg;
+  h->w = *w;
+  h->lay = L;
+  h->ss = (hipStream_t)stage_stream;
+  h->ps = (hipStream_t)pdm_stream;
+  Geo& g = h->g;
+  memset(&g, 0, sizeof(g));
+  g.L = cfg->n_layers;
+  g.d = cfg->d_model;
+  g.Hq = cfg->n_heads;
+  g.Hkv = cfg->n_kv_heads;
+  g.hd = cfg->head_dim;
+  g.F = cfg->d_ffn;
+  g.V = cfg->vocab;
+  g.n = cfg->n_stages;
+  g.Ls = cfg->pdm_layers;
+  g.m = cfg->n_anchors;
+  g.per = g.L / g.n;
+  g.nslots = g.n + 1;
+  g.ctx_cap = L.ctx_cap;
+  g.nsplit = L.nsplit;
+  g.qkv_rows = (g.Hq + 2 * g.Hkv) * g.hd;
+  g.max_new = cfg->max_new;
+  g.max_ctx = cfg->max_ctx;
+  g.eps = cfg->rms_eps;
+  for (int b = 0; b <= SPD_MAX_LAYERS; ++b) g.anchor_of_layer[b] = -1;
+  for (int i = 0; i < g.m; ++i) g.anchor_of_layer[cfg->anchors[i]] = i;
+  g.anchor_of_layer[0] = -1;  // anchor 0 (embedding) is written at entry
+  // f(k) = max{i : b_i <= lmax(k)}, lmax(k) = min(L, k L/n)
+  for (int k = 0; k <= g.n; ++k) {
+    const int lmax = std::min(g.L, k * g.per);
+    int f = 0;
+    for (int i = 0; i < g.m; ++i)
+      if (cfg->anchors[i] <= lmax) f = i;
+    g.fpat[k] = f;
+  }
+  char* ws = (char*)workspace;
+  h->ws = ws;
+  h->ctrl = (Ctrl*)(ws + L.ctrl);
+  h->kv_len = (int32_t*)(ws + L.kv_len);
+  h->tokens = (int32_t*)(ws + L.tokens);
+  h->dring = (int32_t*)(ws + L.dring);
+  h->qring = (float*)(ws + L.qring);
+  h->qz = (double*)(ws + L.qz);
+  h->kc = ws + L.kc;
+  h->vc = ws + L.vc;
+  h->pkc = ws + L.pkc;
+  h->pvc = ws + L.pvc;
+  h->rcos = (float*)(ws + L.rcos);
+  h->rsin = (float*)(ws + L.rsin);
+  h->hslots = (float*)(ws + L.hslots);
+  h->anchors = (float*)(ws + L.anchors);
+  h->s_q = (float*)(ws + L.s_q);
+  h->s_pacc = (float*)(ws + L.s_pacc);
+  h->s_pml = (float*)(ws + L.s_pml);
+  h->s_o = (float*)(ws + L.s_o);
+  h->s_act = (float*)(ws + L.s_act);
+  h->Xt = (float*)(ws + L.Xt);
+  h->Xp = (float*)(ws + L.Xp);
+  h->r_q = (float*)(ws + L.r_q);
+  h->r_pacc = (float*)(ws + L.r_pacc);
+  h->r_pml = (float*)(ws + L.r_pml);
+  h->r_o = (float*)(ws + L.r_o);
+  h->r_act = (float*)(ws + L.r_act);
+  h->taps = (float*)(ws + L.taps);
+  h->logits = (float*)(ws + L.logits);
+  h->plogits = (float*)(ws + L.plogits);
+  h->pw = (float*)(ws + L.pw);
+  h->parts = (ArgPair*)(ws + L.parts);
+  h->pparts = (ArgPair*)(ws + L.pparts);
+  h->ring = (spd_cycle_rec*)(ws + L.ring);
+
+  auto fail = [&](hipError_t e) {
+    h->hip_err = (int)e;
+    delete h;
+    return SPD_EHIP;
+  };
+  hipError_t e;
+  if ((e = hipEventCreateWithFlags(&h->ev_entry, hipEventDisableTiming)) != hipSuccess) return fail(e);
+  if ((e = hipEventCreateWithFlags(&h->ev_pdm, hipEventDisableTiming)) != hipSuccess) return fail(e);
+  // zero the control block and small state; RoPE table
+  Ctrl c0;
+  memset(&c0, 0, sizeof(c0));
+  c0.r_exit = -1;
+  c0.done = 1;
+  if ((e = hipMemcpy(h->ctrl, &c0, sizeof(c0), hipMemcpyHostToDevice)) != hipSuccess) return fail(e);
+  std::vector<int32_t> zl(SPD_MAX_LAYERS, 0);
+  if ((e = hipMemcpy(h->kv_len, zl.data(), sizeof(int32_t) * SPD_MAX_LAYERS, hipMemcpyHostToDevice)) != hipSuccess)
+    return fail(e);
+  hipLaunchKernelGGL(k_rope_table, dim3(512), dim3(256), 0, h->ss, h->rcos, h->rsin, L.ctx_cap, g.hd,
+                     (double)cfg->rope_base);
+  if ((e = hipGetLastError()) != hipSuccess) return fail(e);
+  if ((e = hipEventRecord(h->ev_pdm, h->ps)) != hipSuccess) return fail(e);
+  if ((e = hipStreamSynchronize(h->ss)) != hipSuccess) return fail(e);
+  *out = h;
+  return SPD_OK;
+}
+
+int spd_set_draft_policy(spd_t* h, int32_t policy, float p_accept, const int32_t* ref_tokens_dev, int32_t ref_len) {
+  if (!h) return SPD_EINVAL;
+  if (policy == SPD_DRAFT_NATURAL) {
+    h->policy = policy;
+    return SPD_OK;
+  }
+  if (policy != SPD_DRAFT_FORCED || h->cfg.mode != SPD_MODE_GREEDY) return SPD_EINVAL;
+  if (!ref_tokens_dev || ref_len < 0 || !(p_accept >= 0.f && p_accept <= 1.f) || !h->uni) return SPD_EINVAL;
+  h->policy = policy;
+  h->p_accept = p_accept;
+  h->ref = ref_tokens_dev;
+  h->ref_len = ref_len;
+  return SPD_OK;
+}
+
+int spd_set_uniforms(spd_t* h, const float* uniforms_dev, int32_t n_positions) {
+  if (!h || !uniforms_dev || n_positions < h->cfg.max_ctx) return SPD_EINVAL;
+  h->uni = uniforms_dev;
+  h->uni_len = n_positions;
+  return SPD_OK;
+}
+
+int spd_prefill(spd_t* h, const int32_t* prompt_host, int32_t len, int32_t* first_token) {
+  if (!h || !prompt_host || len < 1) return SPD_EINVAL;
+  for (int i = 0; i < len; ++i)
+    if (prompt_host[i] < 0 || prompt_host[i] >= h->g.V) return SPD_EINVAL;
+  if ((long long)len + h->cfg.max_new + h->cfg.n_stages > h->cfg.max_ctx) return SPD_ECTX;
+  if (h->cfg.mode == SPD_MODE_SAMPLE && !h->uni) return SPD_ESTATE;
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  HIPCHK(h, hipStreamSynchronize(h->ps));
+  HIPCHK(h, hipMemcpy(h->tokens, prompt_host, sizeof(int32_t) * len, hipMemcpyHostToDevice));
+  int r = set_kv_len(h, 0);
+  if (r) return r;
+  Ctrl c;
+  memset(&c, 0, sizeof(c));
+  c.t = len - 1;
+  c.a = 0;
+  c.C = len;
+  c.emitted = 1;
+  c.done = (1 >= h->cfg.max_new);
+  c.active = 0;
+  c.reseed = 1;
+  c.seed_pos = len;
+  c.pend_next = 0;
+  c.r_exit = -1;
+  c.r_accept = -1;
+  if ((r = write_ctrl(h, &c))) return r;
+  r = h->cfg.dtype == SPD_DTYPE_BF16 ? do_prefill<uint16_t>(h, len) : do_prefill<float>(h, len);
+  if (r) return r;
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  int32_t first = 0;
+  HIPCHK(h, hipMemcpy(&first, h->tokens + len, sizeof(int32_t), hipMemcpyDeviceToHost));
+  Ctrl cc;
+  if ((r = read_ctrl(h, &cc))) return r;
+  if (cc.flags) return SPD_EDEVICE;
+  if (first_token) *first_token = first;
+  h->prefilled = 1;
+  h->P = len;
+  h->needs_rollback = 0;
+  return SPD_OK;
+}
+
+int spd_cycle(spd_t* h, int32_t n_cycles, spd_cycle_rec* log_host) {
+  if (!h || n_cycles < 0) return SPD_EINVAL;
+  if (!h->prefilled || h->needs_rollback) return SPD_ESTATE;
+  if ((h->policy == SPD_DRAFT_FORCED || h->cfg.mode == SPD_MODE_SAMPLE) && !h->uni) return SPD_ESTATE;
+  if (log_host && n_cycles > h->lay.log_cap) return SPD_EINVAL;
+  const long long c0 = h->cyc;
+  for (int i = 0; i < n_cycles; ++i) {
+    const int r = h->cfg.dtype == SPD_DTYPE_BF16 ? enqueue_cycle<uint16_t>(h) : enqueue_cycle<float>(h);
+    if (r) return r;
+  }
+  if (log_host && n_cycles > 0) {
+    HIPCHK(h, hipStreamWaitEvent(h->ss, h->ev_pdm, 0));
+    const int cap = h->lay.log_cap;
+    long long done = 0;
+    while (done < n_cycles) {
+      const int slot = (int)((c0 + done) % 0x7FFFFFFF % cap);
+      const long long cnt = std::min<long long>(n_cycles - done, cap - slot);
+      HIPCHK(h, hipMemcpyAsync(log_host + done, h->ring + slot, sizeof(spd_cycle_rec) * cnt,
+                               hipMemcpyDeviceToHost, h->ss));
+      done += cnt;
+    }
+  }
+  return SPD_OK;
+}
+
+int spd_rollback(spd_t* h, int32_t keep_len, int32_t reseed_token) {
+  if (!h) return SPD_EINVAL;
+  if (!h->prefilled) return SPD_ESTATE;
+  if (reseed_token < 0 || reseed_token >= h->g.V) return SPD_EINVAL;
+  Ctrl c;
+  int r = read_ctrl(h, &c);
+  if (r) return r;
+  // leading positions whose KV is complete in every layer: up to the last
+  // verified exit (cycles), or everything the AR decoder processed
+  const int complete = h->needs_rollback ? h->ar_complete : h->P + c.emitted - 1;
+  if (keep_len < 1 || keep_len > complete || keep_len + 1 >= h->g.ctx_cap) return SPD_ESTATE;
+  int C = std::min(c.C, keep_len);
+  int pend = 0;
+  if (C == keep_len - 1) {
+    // the last verified position may stay uncommitted: its anchors are intact
+    if (!(c.C == keep_len - 1 && c.pend_next == 1 && !h->needs_rollback)) return SPD_ESTATE;
+    pend = 1;
+  } else if (C != keep_len) {
+    return SPD_ESTATE;
+  }
+  if (keep_len < h->P) h->P = keep_len;
+  Ctrl n;
+  memset(&n, 0, sizeof(n));
+  n.t = keep_len - 1;
+  n.C = C;
+  n.emitted = keep_len - h->P + 1;
+  n.done = n.emitted >= h->cfg.max_new;
+  n.cycle = c.cycle;
+  n.reseed = 1;
+  n.seed_tok = reseed_token;
+  n.seed_pos = keep_len;
+  n.pend_next = pend;
+  n.r_exit = -1;
+  n.r_accept = -1;
+  n.flags = c.flags;
+  if ((r = set_kv_len(h, keep_len))) return r;
+  HIPCHK(h, hipMemcpy(h->tokens + keep_len, &reseed_token, sizeof(int32_t), hipMemcpyHostToDevice));
+  if ((r = write_ctrl(h, &n))) return r;
+  h->needs_rollback = 0;
+  return SPD_OK;
+}
+
+int spd_generate_ar(spd_t* h, int32_t n_tokens, int32_t* tokens_host) {
+  if (!h || n_tokens < 0) return SPD_EINVAL;
+  if (!h->prefilled || h->needs_rollback) return SPD_ESTATE;
+  Ctrl c;
+  int r = read_ctrl(h, &c);
+  if (r) return r;
+  if (!c.reseed) return SPD_ESTATE;  // needs an empty pipeline (after prefill, rollback or a rejection)
+  const int s0 = c.seed_pos;
+  if (s0 + n_tokens + 1 >= h->g.ctx_cap) return SPD_ECTX;
+  r = h->cfg.dtype == SPD_DTYPE_BF16 ? do_ar<uint16_t>(h, s0, n_tokens) : do_ar<float>(h, s0, n_tokens);
+  if (r) return r;
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  if (tokens_host && n_tokens)
+    HIPCHK(h, hipMemcpy(tokens_host, h->tokens + s0 + 1, sizeof(int32_t) * n_tokens, hipMemcpyDeviceToHost));
+  if ((r = read_ctrl(h, &c))) return r;
+  h->needs_rollback = 1;
+  h->ar_complete = s0 + n_tokens;
+  if (c.flags) return SPD_EDEVICE;
+  return SPD_OK;
+}
+
+int spd_sync(spd_t* h, spd_status* st) {
+  if (!h) return SPD_EINVAL;
+  Ctrl c;
+  const int r = read_ctrl(h, &c);
+  if (r) return r;
+  if (st) {
+    st->cycles = c.cycle;
+    st->emitted = c.emitted;
+    st->done = c.done;
+    st->t = c.t;
+    st->occupancy = c.a;
+    st->pdm_len = c.C;
+    st->flags = c.flags;
+    st->hip_error = h->hip_err;
+  }
+  return c.flags ? SPD_EDEVICE : SPD_OK;
+}
+
+int spd_read_tokens(spd_t* h, int32_t first, int32_t count, int32_t* out_host) {
+  if (!h || !out_host || first < 0 || count < 0 || (long long)first + count > h->g.ctx_cap) return SPD_EINVAL;
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  HIPCHK(h, hipStreamSynchronize(h->ps));
+  if (count) HIPCHK(h, hipMemcpy(out_host, h->tokens + first, sizeof(int32_t) * count, hipMemcpyDeviceToHost));
+  return SPD_OK;
+}
+
+int spd_debug_read(spd_t* h, int32_t what, int32_t index, void* out_host, size_t bytes) {
+  if (!h || !out_host) return SPD_EINVAL;
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  HIPCHK(h, hipStreamSynchronize(h->ps));
+  const Geo& g = h->g;
+  const size_t es = h->cfg.dtype == SPD_DTYPE_BF16 ? 2 : 4;
+  if (what == SPD_DBG_ANCHORS || what == SPD_DBG_HIDDEN) {
+    if (index < 0) return SPD_EINVAL;
+    const int slot = index % g.nslots;
+    const size_t n = (what == SPD_DBG_ANCHORS) ? (size_t)g.m * g.d : (size_t)g.d;
+    if (bytes != n * sizeof(float)) return SPD_EINVAL;
+    const float* src = (what == SPD_DBG_ANCHORS) ? h->anchors + (size_t)slot * g.m * g.d : h->hslots + (size_t)slot * g.d;
+    HIPCHK(h, hipMemcpy(out_host, src, bytes, hipMemcpyDeviceToHost));
+    return SPD_OK;
+  }
+  if (what == SPD_DBG_LOGITS || what == SPD_DBG_PDM_LOGITS) {
+    if (bytes != sizeof(float) * g.V) return SPD_EINVAL;
+    HIPCHK(h, hipMemcpy(out_host, what == SPD_DBG_LOGITS ? h->logits : h->plogits, bytes, hipMemcpyDeviceToHost));
+    return SPD_OK;
+  }
+  if (what == SPD_DBG_KV_K || what == SPD_DBG_KV_V) {
+    if (index < 0 || index >= g.L) return SPD_EINVAL;
+    const int mc = h->cfg.max_ctx;
+    if (bytes != (size_t)mc * g.Hkv * g.hd * es) return SPD_EINVAL;
+    const size_t blk = (size_t)g.Hkv * g.hd * g.ctx_cap * es;
+    std::vector<char> tmp(blk);
+    const char* base = (const char*)(what == SPD_DBG_KV_K ? h->kc : h->vc) + blk * index;
+    HIPCHK(h, hipMemcpy(tmp.data(), base, blk, hipMemcpyDeviceToHost));
+    char* out = (char*)out_host;
+    for (int p = 0; p < mc; ++p)
+      for (int kvh = 0; kvh < g.Hkv; ++kvh)
+        for (int dim = 0; dim < g.hd; ++dim) {
+          size_t src;
+          if (what == SPD_DBG_KV_K)
+            src = (((size_t)kvh * (g.hd / 8) + dim / 8) * g.ctx_cap + p) * 8 + dim % 8;
+          else
+            src = ((size_t)kvh * g.ctx_cap + p) * g.hd + dim;
+          memcpy(out + (((size_t)p * g.Hkv + kvh) * g.hd + dim) * es, tmp.data() + src * es, es);
+        }
+    return SPD_OK;
+  }
+  return SPD_EINVAL;
+}
+
+int spd_timing_enable(spd_t* h, int32_t enable) {
+  if (!h) return SPD_EINVAL;
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  HIPCHK(h, hipStreamSynchronize(h->ps));
+  h->timing = enable ? 1 : 0;
+  h->cyc_ev.clear();
+  h->gu_ev.clear();
+  h->pool_next = 0;
+  return SPD_OK;
+}
+
+int spd_timing_read(spd_t* h, int32_t cap, float* cycle_ms, double* gu_ms, int32_t* gu_launches) {
+  if (!h) return SPD_EINVAL;
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  HIPCHK(h, hipStreamSynchronize(h->ps));
+  const int ncyc = (int)(h->cyc_ev.size() / 3);
+  for (int i = 0; i < ncyc && cycle_ms && i < cap; ++i) {
+    float a = 0.f, b = 0.f;
+    HIPCHK(h, hipEventElapsedTime(&a, h->cyc_ev[3 * i], h->cyc_ev[3 * i + 1]));
+    HIPCHK(h, hipEventElapsedTime(&b, h->cyc_ev[3 * i], h->cyc_ev[3 * i + 2]));
+    cycle_ms[3 * i + 0] = a;
+    cycle_ms[3 * i + 1] = b;
+    cycle_ms[3 * i + 2] = std::max(a, b);
+  }
+  double tot = 0.0;
+  const int ngu = (int)(h->gu_ev.size() / 2);
+  for (int i = 0; i < ngu; ++i) {
+    float ms = 0.f;
+    HIPCHK(h, hipEventElapsedTime(&ms, h->gu_ev[2 * i], h->gu_ev[2 * i + 1]));
+    tot += ms;
+  }
+  if (gu_ms) *gu_ms = tot;
+  if (gu_launches) *gu_launches = ngu;
+  // recorded events are consumed: the pool is reused by later cycles
+  h->cyc_ev.clear();
+  h->gu_ev.clear();
+  h->pool_next = 0;
+  return ncyc;
+}
+
+int spd_destroy(spd_t* h) {
+  if (!h) return SPD_EINVAL;
+  (void)hipStreamSynchronize(h->ss);
+  (void)hipStreamSynchronize(h->ps);
+  (void)hipEventDestroy(h->ev_entry);
+  (void)hipEventDestroy(h->ev_pdm);
+  for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
+  delete h;
+  return SPD_OK;
+}
+
+const char* spd_strerror(int code) {
+  switch (code) {
+    case SPD_OK: return "ok";
+    case SPD_EINVAL: return "invalid argument or configuration";
+    case SPD_ESTATE: return "call not valid in the engine's current state";
+    case SPD_ECTX: return "sequence would exceed max_ctx";
+    case SPD_EHIP: return "HIP runtime error";
+    case SPD_EDEVICE: return "device-side invariant check failed";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,446 @@
+// Matrix-vector kernels of the SPD cycle (gfx950, VALU, fp32 accumulation).
+//
+// y = W x for weight matrices W [N][K] (bf16 or fp32, row-major) streamed once
+// per launch with 16-byte non-temporal loads.  One wavefront owns four output
+// rows; its 64 lanes split K in 16-byte chunks (lane l reads elements
+// l*VEC .. l*VEC+VEC-1 of every 64*VEC block, in ascending order) and the four
+// partial sums are reduced with a butterfly.  Both kernels below use exactly
+// this per-row arithmetic, so a row computed by either gives the same bits.
+//
+//  * k_gemv_stage: the stage-grouped decode GEMV.  Group g is stage g; its
+//    in-flight token's input vector is normalised once per workgroup into
+//    LDS.  The grid is persistent: the tiles of all ACTIVE groups (g < a,
+//    known only on the device) are spread over every workgroup, so warm-up
+//    cycles with few tokens in flight still use the whole chip.
+//  * k_gemv_rows: up to kRowsMR activation rows share one weight stream
+//    (draft-module rows, prefill chunks, autoregressive decode); the input
+//    rows are staged through LDS in K chunks.
+#pragma once
+
+#include "common.h"
+
+namespace spd {
+
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3, EPI_STORE = 4 };
+enum GMode { GM_STAGE = 0, GM_EXIT = 1, GM_FIXED = 2, GM_PDMLAST = 3 };
+enum RMode { RM_CONTIG = 0, RM_FC = 1 };
+
+__host__ __device__ constexpr bool epi_pairs(int epi) { return epi == EPI_QKV || epi == EPI_SWIGLU; }
+
+// Rows of output unit u: QKV pairs (i, i+hd/2) of one head (rotate-half RoPE
+// partners); SwiGLU pairs (gate i, up i); otherwise one row.
+template <int EPI>
+__device__ __forceinline__ void unit_rows(const Geo& g, int N, int u, int& r0, int& r1) {
+  if (EPI == EPI_QKV) {
+    const int half = g.hd >> 1;
+    const int h = u / half, i = u - h * half;
+    r0 = h * g.hd + i;
+    r1 = r0 + half;
+  } else if (EPI == EPI_SWIGLU) {
+    r0 = u;
+    r1 = u + (N >> 1);
+  } else {
+    r0 = u;
+    r1 = -1;
+  }
+}
+
+// a[i] for a lane-dependent i without dynamic register indexing
+__device__ __forceinline__ float sel4(const float (&a)[4], int i) {
+  return i == 0 ? a[0] : (i == 1 ? a[1] : (i == 2 ? a[2] : a[3]));
+}
+
+__device__ __forceinline__ float silu_mul(float gte, float up) { return gte / (1.0f + expf(-gte)) * up; }
+
+// RoPE rotation of the pair (a, b) = (x_i, x_{i+hd/2}) at table entry (pos, i).
+__device__ __forceinline__ void rope_pair(float& a, float& b, float c, float s) {
+  const float a2 = a * c - b * s;
+  const float b2 = b * c + a * s;
+  a = a2;
+  b = b2;
+}
+
+// ---------------------------------------------------------------------------
+// Stage-grouped GEMV
+// ---------------------------------------------------------------------------
+struct StageGemv {
+  const void* W[SPD_MAX_STAGES];
+  const float* gamma[SPD_MAX_STAGES];  // RMSNorm gain of the input (nullptr: no norm)
+  int layer[SPD_MAX_STAGES];           // layer of group g (KV epilogue)
+  int anchor_idx[SPD_MAX_STAGES];      // anchor to tap after this layer, or -1
+  int N, K, units, n_groups, gmode;
+  const float* x;
+  long long x_stride;
+  int x_by_slot;  // input row = x + (slot or group) * x_stride
+  float* out;
+  long long out_stride;
+  int out_by_slot;
+  void* kc;
+  void* vc;
+  const float* rcos;
+  const float* rsin;
+  int* kv_len;
+  float* anchors;
+  ArgPair* parts;
+  Ctrl* ctrl;
+  Geo g;
+};
+
+template <typename WT, int EPI>
+__global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
+  extern __shared__ float xs[];  // [K]
+  __shared__ float red[kWG / kWave];
+  __shared__ ArgPair wbest[kWG / kWave];
+  constexpr int VEC = WVec<WT>::N;
+  constexpr int UPW = epi_pairs(EPI) ? 2 : 4;  // units per wave
+  constexpr int UPT = UPW * (kWG / kWave);     // units per tile
+  const Ctrl* __restrict__ C = A.ctrl;
+  const Geo& g = A.g;
+
+  int n_act, pos_base;
+  if (A.gmode == GM_STAGE) {
+    if (!C->active) return;
+    n_act = C->a;
+    pos_base = C->t;
+  } else if (A.gmode == GM_EXIT) {
+    if (!C->active || C->a != g.n) return;
+    n_act = 1;
+    pos_base = C->t - (g.n - 1);
+  } else if (A.gmode == GM_PDMLAST) {
+    if (!C->active) return;
+    n_act = 1;
+    pos_base = 0;
+  } else {
+    n_act = 1;
+    pos_base = 0;
+  }
+  // GM_PDMLAST reads the newest draft-module row, index a + pending - 1
+  const float* xfix = (A.gmode == GM_PDMLAST) ? A.x + (size_t)(C->a + C->pending - 1) * A.x_stride : A.x;
+  const int tpg = (A.units + UPT - 1) / UPT;
+  const long long T = (long long)n_act * tpg;
+  const long long t0 = T * blockIdx.x / gridDim.x;
+  const long long t1 = T * (blockIdx.x + 1) / gridDim.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+
+  int cur = -1, pos = 0, slot = 0;
+  const WT* W = nullptr;
+  for (long long tile = t0; tile < t1; ++tile) {
+    const int grp = (int)(tile / tpg);
+    const int ut = (int)(tile - (long long)grp * tpg);
+    if (grp != cur) {
+      cur = grp;
+      pos = pos_base - grp;
+      const bool fixed = (A.gmode == GM_FIXED || A.gmode == GM_PDMLAST);
+      slot = fixed ? 0 : pos % g.nslots;
+      const float* x = fixed ? xfix : A.x + (A.x_by_slot ? slot : grp) * A.x_stride;
+      const float* gm = A.gamma[grp];
+      __syncthreads();
+      if (gm) {
+        const float rstd = row_rstd(x, A.K, g.eps, red);
+        for (int i = threadIdx.x; i < A.K; i += kWG) xs[i] = x[i] * rstd * gm[i];
+      } else {
+        for (int i = threadIdx.x; i < A.K; i += kWG) xs[i] = x[i];
+      }
+      __syncthreads();
+      W = reinterpret_cast<const WT*>(A.W[grp]);
+      if (EPI == EPI_QKV && ut == 0 && threadIdx.x == 0 && A.kv_len) {
+        int* len = A.kv_len + A.layer[grp];
+        if (*len != pos) atomicOr(&A.ctrl->flags, SPD_FLAG_KVLEN);
+        *len = pos + 1;
+      }
+    }
+    // four rows of this wave
+    int rows[4];
+    bool ok[4];
+#pragma unroll
+    for (int j = 0; j < UPW; ++j) {
+      const int u = ut * UPT + wave * UPW + j;
+      int r0, r1;
+      unit_rows<EPI>(g, A.N, u < A.units ? u : 0, r0, r1);
+      if (epi_pairs(EPI)) {
+        rows[2 * j] = r0;
+        rows[2 * j + 1] = r1;
+        ok[2 * j] = ok[2 * j + 1] = u < A.units;
+      } else {
+        rows[j] = r0;
+        ok[j] = u < A.units;
+      }
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const WT* p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = W + (size_t)rows[r] * A.K;
+#pragma unroll 2
+    for (int k0 = lane * VEC; k0 < A.K; k0 += kWave * VEC) {
+      float wv[4][VEC];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) WVec<WT>::load(p[r] + k0, wv[r]);
+      float xv[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) xv[e] = xs[k0 + e];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[r] = fmaf(wv[r][e], xv[e], acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = wave_sum(acc[r]);
+
+    // epilogue: lane j handles unit j of the wave
+    if (lane < UPW) {
+      const int j = lane;
+      const int u = ut * UPT + wave * UPW + j;
+      if (u < A.units) {
+        if (EPI == EPI_QKV) {
+          float a = sel4(acc, 2 * j), b = sel4(acc, 2 * j + 1);
+          const int half = g.hd >> 1;
+          const int h = u / half, i = u - h * half;
+          if (h < g.Hq + g.Hkv) rope_pair(a, b, A.rcos[(size_t)pos * half + i], A.rsin[(size_t)pos * half + i]);
+          if (h < g.Hq) {
+            float* q = A.out + (size_t)grp * A.out_stride + (size_t)h * g.hd;
+            q[i] = a;
+            q[i + half] = b;
+          } else if (h < g.Hq + g.Hkv) {
+            auto* kc = reinterpret_cast<WT*>(A.kc);
+            const int kvh = h - g.Hq, ly = A.layer[grp];
+            kc[k_index(g, ly, kvh, pos, i)] = to_store<WT>(a);
+            kc[k_index(g, ly, kvh, pos, i + half)] = to_store<WT>(b);
+          } else {
+            auto* vc = reinterpret_cast<WT*>(A.vc);
+            const int kvh = h - g.Hq - g.Hkv, ly = A.layer[grp];
+            vc[v_index(g, ly, kvh, pos, i)] = to_store<WT>(a);
+            vc[v_index(g, ly, kvh, pos, i + half)] = to_store<WT>(b);
+          }
+        } else if (EPI == EPI_SWIGLU) {
+          A.out[(size_t)grp * A.out_stride + u] = silu_mul(sel4(acc, 2 * j), sel4(acc, 2 * j + 1));
+        } else if (EPI == EPI_RESID) {
+          float* o = A.out + (A.out_by_slot ? slot : grp) * A.out_stride;
+          const float hn = o[u] + sel4(acc, j);
+          o[u] = hn;
+          const int ai = A.anchor_idx[grp];
+          if (ai >= 0) A.anchors[((size_t)slot * g.m + ai) * g.d + u] = hn;
+        } else if (EPI == EPI_ARGMAX) {
+          const float y = sel4(acc, j);
+          A.out[u] = y;
+          if (better(y, u, bv, bi)) {
+            bv = y;
+            bi = u;
+          }
+        } else {
+          A.out[(size_t)grp * A.out_stride + u] = sel4(acc, j);
+        }
+      }
+    }
+  }
+  if (EPI == EPI_ARGMAX) {
+    // lanes 0..3 of each wave hold candidates; reduce in a fixed order
+    wave_argmax(bv, bi);
+    if (lane == 0) wbest[wave] = ArgPair{bv, bi};
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      ArgPair b = wbest[0];
+      for (int w = 1; w < kWG / kWave; ++w)
+        if (better(wbest[w].v, wbest[w].i, b.v, b.i)) b = wbest[w];
+      A.parts[blockIdx.x] = b;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row-batched GEMV (M <= kRowsMR rows per weight stream)
+// ---------------------------------------------------------------------------
+struct RowsGemv {
+  const void* W[SPD_MAX_ANCHORS];
+  int Kg[SPD_MAX_ANCHORS];  // K per group (FC patterns differ)
+  const float* gamma;       // RMSNorm gain of the input rows (nullptr: none)
+  int N, units, n_groups, rmode;
+  const float* x;
+  int ldx;
+  int M_arg, pos0_arg, from_ctrl;  // rows/positions from the args or (draft module) from the control block
+  int row_base;                    // first row of this pass (rows >= kRowsMR run in two passes)
+  float* out;
+  int ldo;
+  int layer;        // KV layer (QKV epilogue)
+  void* kc;
+  void* vc;
+  const float* rcos;
+  const float* rsin;
+  int* kv_len;      // length word of `layer` to check/advance, or nullptr
+  float* anchors;   // RESID: row-indexed anchor taps [row][m][d], or nullptr
+  int anchor_idx;
+  const float* slot_anchors;  // FC: anchor store [slot][m][d]
+  Ctrl* ctrl;
+  Geo g;
+};
+
+constexpr int kRowsKC = 512;  // K elements of each input row staged per pass (one 64-lane block of bf16)
+
+template <typename WT, int EPI>
+__global__ __launch_bounds__(kWG) void k_gemv_rows(const RowsGemv A) {
+  __shared__ float xs[kRowsMR][kRowsKC];
+  __shared__ float red[kWG / kWave];
+  __shared__ float rstd[kRowsMR];
+  __shared__ int rsrc[kRowsMR];  // FC: output row of input row r
+  __shared__ int rcount;
+  constexpr int VEC = WVec<WT>::N;
+  constexpr int UPW = epi_pairs(EPI) ? 2 : 4;
+  constexpr int UPT = UPW * (kWG / kWave);
+  const Geo& g = A.g;
+  const Ctrl* __restrict__ C = A.ctrl;
+  if (A.from_ctrl && !C->active) return;
+  const int grp = blockIdx.y;
+  const int ut = blockIdx.x;
+  const int K = A.Kg[grp];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+
+  // rows of this pass
+  int Mtot = A.from_ctrl ? (C->a + C->pending) : A.M_arg;
+  const int pos0 = A.from_ctrl ? C->C : A.pos0_arg;
+  int M = Mtot - A.row_base;
+  if (M > kRowsMR) M = kRowsMR;
+  if (A.rmode == RM_FC) {
+    // rows whose depth uses pattern `grp`: trailing row i is at position C+i,
+    // depth n for the committed-next row, else t - position
+    if (threadIdx.x == 0) {
+      int cnt = 0;
+      for (int i = 0; i < Mtot; ++i) {
+        const int p = pos0 + i;
+        const int dep = (C->pending && i == 0) ? g.n : (C->t - p);
+        if (g.fpat[dep] == grp && cnt < kRowsMR) rsrc[cnt++] = i;
+      }
+      rcount = cnt;
+    }
+    __syncthreads();
+    M = rcount;
+  }
+  if (M <= 0) return;
+  if (A.kv_len && EPI == EPI_QKV && ut == 0 && threadIdx.x == 0 && A.row_base == 0) {
+    int* len = A.kv_len + A.layer;
+    if (*len != pos0) atomicOr(&A.ctrl->flags, SPD_FLAG_KVLEN);
+    *len = pos0 + Mtot;
+  }
+  auto in_row = [&](int r) -> const float* {
+    if (A.rmode == RM_FC) {
+      const int i = rsrc[r];
+      const int slot = (pos0 + i) % g.nslots;
+      return A.slot_anchors + (size_t)slot * g.m * g.d;
+    }
+    return A.x + (size_t)(A.row_base + r) * A.ldx;
+  };
+  if (A.gamma) {
+    for (int r = 0; r < M; ++r) {
+      const float s = row_rstd(in_row(r), K, g.eps, red);
+      if (threadIdx.x == 0) rstd[r] = s;
+    }
+  }
+  __syncthreads();
+
+  int rows[4];
+  bool ok[4];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    const int u = ut * UPT + wave * UPW + j;
+    int r0, r1;
+    unit_rows<EPI>(g, A.N, u < A.units ? u : 0, r0, r1);
+    if (epi_pairs(EPI)) {
+      rows[2 * j] = r0;
+      rows[2 * j + 1] = r1;
+      ok[2 * j] = ok[2 * j + 1] = u < A.units;
+    } else {
+      rows[j] = r0;
+      ok[j] = u < A.units;
+    }
+  }
+  const WT* W = reinterpret_cast<const WT*>(A.W[grp]);
+  const WT* p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = W + (size_t)rows[r] * K;
+  float acc[4][kRowsMR];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int m = 0; m < kRowsMR; ++m) acc[r][m] = 0.f;
+
+  for (int kc = 0; kc < K; kc += kRowsKC) {
+    const int kn = min(kRowsKC, K - kc);
+    __syncthreads();
+    for (int r = 0; r < M; ++r) {
+      const float* x = in_row(r) + kc;
+      if (A.gamma) {
+        const float s = rstd[r];
+        for (int i = threadIdx.x; i < kn; i += kWG) xs[r][i] = x[i] * s * A.gamma[kc + i];
+      } else {
+        for (int i = threadIdx.x; i < kn; i += kWG) xs[r][i] = x[i];
+      }
+    }
+    __syncthreads();
+    for (int k0 = lane * VEC; k0 < kn; k0 += kWave * VEC) {
+      float wv[4][VEC];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) WVec<WT>::load(p[r] + kc + k0, wv[r]);
+#pragma unroll
+      for (int m = 0; m < kRowsMR; ++m) {
+        if (m < M) {
+          float xv[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) xv[e] = xs[m][k0 + e];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[r][m] = fmaf(wv[r][e], xv[e], acc[r][m]);
+        }
+      }
+    }
+  }
+  const int half = g.hd >> 1;
+#pragma unroll
+  for (int m = 0; m < kRowsMR; ++m) {
+    if (m >= M) continue;
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = wave_sum(acc[r][m]);
+    if (lane < UPW) {
+      const int j = lane;
+      const int u = ut * UPT + wave * UPW + j;
+      if (u < A.units) {
+        const int orow = (A.rmode == RM_FC) ? rsrc[m] : (A.row_base + m);
+        const int pos = pos0 + orow;
+        if (EPI == EPI_QKV) {
+          float a = sel4(v, 2 * j), b = sel4(v, 2 * j + 1);
+          const int h = u / half, i = u - h * half;
+          if (h < g.Hq + g.Hkv) rope_pair(a, b, A.rcos[(size_t)pos * half + i], A.rsin[(size_t)pos * half + i]);
+          if (h < g.Hq) {
+            float* q = A.out + (size_t)orow * A.ldo + (size_t)h * g.hd;
+            q[i] = a;
+            q[i + half] = b;
+          } else if (h < g.Hq + g.Hkv) {
+            auto* kc = reinterpret_cast<WT*>(A.kc);
+            const int kvh = h - g.Hq;
+            kc[k_index(g, A.layer, kvh, pos, i)] = to_store<WT>(a);
+            kc[k_index(g, A.layer, kvh, pos, i + half)] = to_store<WT>(b);
+          } else {
+            auto* vc = reinterpret_cast<WT*>(A.vc);
+            const int kvh = h - g.Hq - g.Hkv;
+            vc[v_index(g, A.layer, kvh, pos, i)] = to_store<WT>(a);
+            vc[v_index(g, A.layer, kvh, pos, i + half)] = to_store<WT>(b);
+          }
+        } else if (EPI == EPI_SWIGLU) {
+          A.out[(size_t)orow * A.ldo + u] = silu_mul(sel4(v, 2 * j), sel4(v, 2 * j + 1));
+        } else if (EPI == EPI_RESID) {
+          float* o = A.out + (size_t)orow * A.ldo;
+          const float hn = o[u] + sel4(v, j);
+          o[u] = hn;
+          if (A.anchors && A.anchor_idx >= 0) A.anchors[((size_t)orow * g.m + A.anchor_idx) * g.d + u] = hn;
+        } else {
+          A.out[(size_t)orow * A.ldo + u] = sel4(v, j);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace spd

@@ -1,0 +1,83 @@
+"""The C-ABI library loads and exports every symbol include/spd.h declares;
+host-only calls validate configurations (CPU only, no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import seeded_inputs as si
+from pipelined_draft_verify_amd import _abi as A
+from pipelined_draft_verify_amd.engine import REC_DTYPE, make_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spd.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:SPD_API\s+)?(?:const\s+)?\w+\s*\*?\s*(spd_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("spd_workspace_bytes", "spd_init", "spd_prefill", "spd_cycle", "spd_rollback", "spd_destroy",
+              "spd_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = A.lib()
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing
+    assert sorted(n for n, _, _ in A.SIGNATURES) == _declared()
+
+
+def test_struct_sizes_match_header_layout():
+    # spd_cycle_rec: 12 words + 64 KV lengths
+    assert ctypes.sizeof(A.spd_cycle_rec) == 4 * (12 + A.SPD_MAX_LAYERS) == REC_DTYPE.itemsize
+    assert ctypes.sizeof(A.spd_config) == 4 * (10 + A.SPD_MAX_ANCHORS + 4 + 3)
+    assert ctypes.sizeof(A.spd_weights) == 8 * (1 + 6 * A.SPD_MAX_LAYERS + 2 + A.SPD_MAX_ANCHORS
+                                                + 6 * A.SPD_MAX_PDM_LAYERS + 2)
+
+
+def test_strerror_and_workspace_sizing_on_host():
+    assert A.spd_strerror(0) == "ok"
+    assert "state" in A.spd_strerror(A.SPD_ESTATE)
+    w = si.workload("4b_n8")
+    n = A.spd_workspace_bytes(make_config(w))
+    # KV caches (target + draft) dominate: (L + Ls) * 2 * Hkv * hd * ctx * 2 bytes
+    kv = (w.L + w.Ls) * 2 * w.Hkv * w.hd * 1024 * 2
+    assert kv < n < kv * 3
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_stages", 3),        # does not divide 32
+    ("pdm_layers", 5),      # deeper than one stage (32/8 = 4)
+    ("head_dim", 96),
+    ("n_kv_heads", 3),      # 20 % 3 != 0
+    ("d_model", 2500),      # not a multiple of 256
+    ("max_new", 0),
+])
+def test_invalid_configs_are_rejected(field, value):
+    c = make_config(si.workload("4b_n8"))
+    setattr(c, field, value)
+    with pytest.raises(A.SPDError) as e:
+        A.spd_workspace_bytes(c)
+    assert e.value.code == A.SPD_EINVAL
+
+
+def test_anchor_constraints_are_checked():
+    c = make_config(si.workload("4b_n8"))
+    c.anchors[0] = 1
+    with pytest.raises(A.SPDError):
+        A.spd_workspace_bytes(c)
+    c = make_config(si.workload("4b_n8"))
+    c.anchors[2] = c.anchors[1]
+    with pytest.raises(A.SPDError):
+        A.spd_workspace_bytes(c)
+    c = make_config(si.workload("4b_n8"))
+    c.anchors[4] = 33
+    with pytest.raises(A.SPDError):
+        A.spd_workspace_bytes(c)

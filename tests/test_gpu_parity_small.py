@@ -1,0 +1,201 @@
+"""GPU parity on small workloads the oracle runs completely (seconds).
+
+The HIP path and the oracle run the same seeded weights, prompt, uniforms and
+draft policy.  Token ids, drafts, accept decisions, KV lengths, occupancy and
+the draft module's committed length must agree bit for bit every cycle.
+Where floating point decides an integer (an argmax), a near-tie is the only
+allowed difference: the oracle adopts the GPU's choice when that choice's
+logit is within the tolerance of the oracle's maximum (1e-4 in fp32,
+0.05 in bf16), and the test counts such adoptions (expected: none or a few).
+Hidden states, anchors and logits must match within rel-L2 1e-4 (fp32) and
+2e-2 (bf16).
+"""
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from oracle import ForcedPolicy, SPDOracle, ar_greedy
+from tests.gpu_common import compare_logs, gpu_workload_tiny, rel_l2, run_gpu, teacher_of
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 0.05}
+RTOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _inputs(w):
+    T = si.make_weights(w, "cpu")
+    W = si.nest_weights(si.weights_numpy_f32(T), w)
+    return T, W, si.make_prompt(w), si.make_uniforms(w)
+
+
+def _oracle(w, W, prompt, uni, recs, first, ref=None, p=None):
+    pol = ForcedPolicy(ref, p, uni, w.V) if ref is not None else None
+    o = SPDOracle(w, W, policy=pol, uniforms=uni, teacher=teacher_of(recs, first), tol=TOL[w.dtype])
+    toks, logs = o.run(prompt, w.G)
+    return o, toks, logs
+
+
+def test_tiny_fp32_workload_matches_oracle():
+    """The tiny fp32 workload (L=8, d=256, n=4, natural drafts), all 64 tokens."""
+    w = si.workload("tiny_fp32")
+    T, W, prompt, uni = _inputs(w)
+    eng, first, recs, toks = run_gpu(w, T, prompt)
+    eng.close()
+    o, otoks, ologs = _oracle(w, W, prompt, uni, recs, first)
+    assert not o.dec.mismatch
+    assert len(o.dec.adopted) == 0, o.dec.adopted
+    assert toks == otoks
+    compare_logs(recs, ologs, w.L)
+
+
+VARIANTS = {
+    "gqa_f32_forced": dict(dtype="f32", p=0.6),
+    "bf16_gqa_forced": dict(dtype="bf16", L=6, n=3, Hq=8, Hkv=2, F=768, V=500, anchors=[0, 2, 5], Ls=2, p=0.5,
+                            seed=32),
+    "deep_n8": dict(L=8, n=8, Ls=1, anchors=[0, 3, 8], G=20, p=0.7, seed=33),
+    "hd128_bf16": dict(dtype="bf16", Hq=2, Hkv=1, hd=128, F=512, V=700, p=0.8, seed=34, norm_gain="random"),
+    "mha_n4_long_prompt": dict(L=4, n=4, Hq=4, Hkv=4, anchors=[0, 1, 2, 3, 4], P=300, G=16, p=0.5, seed=35),
+    "g5_gqa_bf16": dict(dtype="bf16", d=256, Hq=20, Hkv=4, hd=64, F=512, V=1000, L=4, n=4, Ls=1,
+                        anchors=[0, 2, 3], P=40, G=20, p=0.8, seed=36),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VARIANTS))
+def test_variant_matches_oracle(name):
+    kw = dict(VARIANTS[name])
+    p = kw.pop("p")
+    w = gpu_workload_tiny(**kw)
+    T, W, prompt, uni = _inputs(w)
+    ref, _ = ar_greedy(w, W, prompt, w.G)
+    eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni, ref=ref, p_accept=p)
+    eng.close()
+    o, otoks, ologs = _oracle(w, W, prompt, uni, recs, first, ref=ref, p=p)
+    assert not o.dec.mismatch, o.dec.mismatch
+    assert len(o.dec.adopted) <= 2, o.dec.adopted
+    assert toks == otoks
+    compare_logs(recs, ologs, w.L)
+    # the acceptance structure is exercised
+    acc = recs["accepted"]
+    assert (acc == 1).any() and (acc == 0).any()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hidden_states_anchors_and_logits(dtype):
+    """Per-cycle anchors of every in-flight token and the verification logits."""
+    w = gpu_workload_tiny(dtype=dtype, L=4, n=2, G=12, seed=37)
+    T, W, prompt, uni = _inputs(w)
+    ref, _ = ar_greedy(w, W, prompt, w.G)
+    gpu = {}
+
+    def hook(eng, r):
+        c = int(r["cycle"])
+        t, a = int(r["t"]), int(r["occupancy"])
+        # in-flight tokens after the stage step (the exiting one is still in its slot)
+        gpu[c] = {"anchors": {p: eng.anchors(p) for p in range(t - a + 1, t + 1)}}
+        if r["exit_pos"] >= 0:
+            gpu[c]["logits"] = eng.logits()
+        gpu[c]["pdm_logits"] = eng.pdm_logits()
+
+    eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni, ref=ref, p_accept=0.5, per_cycle_hook=hook)
+    eng.close()
+    pol = ForcedPolicy(ref, 0.5, uni, w.V)
+    o = SPDOracle(w, W, policy=pol, uniforms=uni, teacher=teacher_of(recs, first), tol=TOL[dtype])
+    seen = {"exit": 0, "pdm": 0, "anch": 0}
+
+    def ohook(kind, info):
+        c = info["cycle"]
+        if kind == "exit":
+            assert rel_l2(gpu[c]["logits"], info["logits"]) <= RTOL[dtype]
+            seen["exit"] += 1
+        elif kind == "pdm":
+            assert rel_l2(gpu[c]["pdm_logits"], info["logits"]) <= RTOL[dtype]
+            seen["pdm"] += 1
+
+    o.hook = ohook
+    o.prefill(prompt)
+    while o.emitted < w.G:
+        rec = o.cycle()
+        c = rec["cycle"]
+        for p, ga in gpu[c]["anchors"].items():
+            taps = o.anchors.get(p)
+            if taps is None:
+                continue
+            for i, a in enumerate(taps):
+                if a is not None:
+                    assert rel_l2(ga[i], a) <= RTOL[dtype], (c, p, i)
+                    seen["anch"] += 1
+    assert seen["exit"] > 3 and seen["pdm"] == len(recs) and seen["anch"] > 10
+
+
+def test_lossless_forced_natural_and_autoregressive_agree():
+    """On the GPU alone: natural drafts, forced drafts and plain AR decoding
+    emit bit-identical tokens (the method is lossless for any draft policy)."""
+    w = gpu_workload_tiny(dtype="bf16", L=4, n=4, anchors=[0, 1, 2, 3, 4], G=30, seed=38)
+    T, W, prompt, uni = _inputs(w)
+    import torch
+    from pipelined_draft_verify_amd import SPDEngine
+
+    eng = SPDEngine(w, {k: v.to("cuda:0") for k, v in T.items()})
+    eng.set_uniforms(uni)
+    first = eng.prefill(prompt)
+    ar = eng.generate_ar(w.G - 1)
+    eng.rollback(w.P, first)
+    nat = eng.run()
+    tok_nat = eng.tokens(w.P, w.G)
+    ref = list(prompt) + [first] + ar
+    for p in (0.0, 0.5, 1.0):
+        eng.rollback(w.P, first)
+        eng.set_forced(ref, p)
+        recs = eng.run()
+        assert eng.tokens(w.P, w.G) == [first] + ar, p
+        if p == 1.0:
+            assert (recs["accepted"][recs["exit_pos"] >= 0] == 1).all()
+            assert len(recs) == w.n + w.G - 2
+    eng.close()
+    assert tok_nat == [first] + ar
+
+
+def test_rollback_to_prefix_equals_fresh_prefill():
+    w = gpu_workload_tiny(dtype="f32", L=4, n=2, G=16, seed=39)
+    T, W, prompt, uni = _inputs(w)
+    from pipelined_draft_verify_amd import SPDEngine
+
+    eng = SPDEngine(w, {k: v.to("cuda:0") for k, v in T.items()})
+    first = eng.prefill(prompt)
+    eng.run()
+    toks = eng.tokens(0, w.P + w.G)
+    keep = w.P + 5
+    eng.rollback(keep, toks[keep])
+    st = eng.sync()
+    assert st.emitted == keep - w.P + 1
+    recs = eng.run()
+    assert eng.tokens(0, w.P + w.G) == toks
+    kv_a = eng.kv(1, "k")[:keep]
+    eng.close()
+    # a fresh engine prefilled with the kept prefix holds the same KV entries
+    w2 = w.replace(P=keep)
+    eng2 = SPDEngine(w2, {k: v.to("cuda:0") for k, v in T.items()})
+    eng2.prefill(toks[:keep])
+    kv_b = eng2.kv(1, "k")[:keep]
+    eng2.close()
+    np.testing.assert_allclose(kv_a, kv_b, rtol=1e-5, atol=1e-6)
+
+
+def test_error_paths_from_the_host():
+    w = gpu_workload_tiny()
+    T, W, prompt, uni = _inputs(w)
+    from pipelined_draft_verify_amd import SPDEngine, SPDError
+
+    eng = SPDEngine(w, {k: v.to("cuda:0") for k, v in T.items()})
+    with pytest.raises(SPDError):      # cycles before prefill
+        eng.enqueue(1, log=False)
+    with pytest.raises(SPDError):      # prompt too long for max_ctx
+        eng.prefill([1] * (w.max_ctx))
+    first = eng.prefill(prompt)
+    with pytest.raises(SPDError):      # rollback beyond the verified prefix
+        eng.rollback(w.P + 3, first)
+    with pytest.raises(SPDError):      # token out of range
+        eng.rollback(w.P, w.V)
+    eng.run()
+    eng.close()
