@@ -97,6 +97,44 @@ def layer_rows(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache) -> np.ndarr
     return out
 
 
+def layer_matrix(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache) -> np.ndarray:
+    """`layer_rows` written with matrix products over all M rows at once.
+
+    The same definition (row i attends to cached positions and rows <= i);
+    only the order of floating-point operations differs.  Used for long
+    prompts, where the row-at-a-time form is too slow.
+    """
+    M = X.shape[0]
+    Hq, Hkv, hd = s.Hq, s.Hkv, s.hd
+    U = np.stack([rmsnorm(X[i], lw["attn_norm"], s.eps) for i in range(M)])
+    QKV = U @ lw["w_qkv"].T
+    Q = QKV[:, : Hq * hd].reshape(M, Hq, hd)
+    Kn = QKV[:, Hq * hd:(Hq + Hkv) * hd].reshape(M, Hkv, hd)
+    Vn = QKV[:, (Hq + Hkv) * hd:].reshape(M, Hkv, hd)
+    for i in range(M):
+        c, sn = rope_cos_sin(pos0 + i, hd, s.base)
+        Q[i] = apply_rope(Q[i], c, sn)
+        kv.write(pos0 + i, apply_rope(Kn[i], c, sn), Vn[i])
+    T = pos0 + M
+    grp = Hq // Hkv
+    scale = F32(1.0 / np.sqrt(hd))
+    mask = np.arange(T)[None, :] > (pos0 + np.arange(M))[:, None]
+    O = np.empty((M, Hq, hd), dtype=F32)
+    for h in range(Hq):
+        k_ = kv.K[:T, h // grp, :]
+        v_ = kv.V[:T, h // grp, :]
+        S = (Q[:, h, :] @ k_.T) * scale
+        S[mask] = -np.inf
+        S = S - S.max(axis=1, keepdims=True)
+        Pm = np.exp(S)
+        Pm = Pm / Pm.sum(axis=1, keepdims=True, dtype=F32)
+        O[:, h, :] = Pm @ v_
+    H = X + O.reshape(M, Hq * hd) @ lw["w_o"].T
+    U2 = np.stack([rmsnorm(H[i], lw["ffn_norm"], s.eps) for i in range(M)])
+    GU = U2 @ lw["w_gu"].T
+    return (H + (silu(GU[:, : s.F]) * GU[:, s.F:]) @ lw["w_down"].T).astype(F32)
+
+
 class Target:
     """The L-layer target decoder with per-layer KV caches and anchor taps."""
 
@@ -139,6 +177,26 @@ class Target:
         for kv in self.kv:
             kv.length = length
 
+    def prefill_matrix(self, tokens: Sequence[int]):
+        """Whole prompt through every layer at once (matrix form of forward_token).
+
+        Returns (final hidden of the last position, anchors [P][m] lists).
+        """
+        P = len(tokens)
+        H = np.stack([self.embed(int(t)) for t in tokens])
+        taps = [[None] * len(self.s.anchors) for _ in range(P)]
+        for p in range(P):
+            taps[p][0] = H[p].copy()
+        for l in range(self.s.L):
+            kv = self.kv[l]
+            assert kv.length == 0
+            H = layer_matrix(self.s, self.W["layers"][l], H, 0, kv)
+            kv.length = P
+            if (l + 1) in self.anchor_at:
+                for p in range(P):
+                    taps[p][self.anchor_at[l + 1]] = H[p].copy()
+        return H[-1].copy(), taps
+
 
 class PDM:
     """Pipeline draft module: FC fusion of anchors, Ls causal decoder layers, own head.
@@ -164,12 +222,13 @@ class PDM:
         x = np.concatenate([taps[i] for i in range(f + 1)]).astype(F32)
         return self.W["fc"][f] @ x
 
-    def run_rows(self, G: np.ndarray, pos0: int) -> np.ndarray:
+    def run_rows(self, G: np.ndarray, pos0: int, matrix: bool = False) -> np.ndarray:
         """All Ls layers over feature rows at positions pos0.. (pos0 == C)."""
         assert pos0 == self.C, "trailing rows must start at the committed length"
         X = G.astype(F32)
+        f = layer_matrix if matrix else layer_rows
         for l in range(self.s.Ls):
-            X = layer_rows(self.s, self.W["pdm_layers"][l], X, pos0, self.kv[l])
+            X = f(self.s, self.W["pdm_layers"][l], X, pos0, self.kv[l])
         return X
 
     def logits(self, x: np.ndarray) -> np.ndarray:

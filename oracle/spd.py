@@ -162,14 +162,18 @@ class SPDOracle:
         self.hook = None  # optional callable(kind, info) for inspection in tests
 
     # -- prefill -------------------------------------------------------------
-    def prefill(self, prompt: Sequence[int]) -> int:
+    def prefill(self, prompt: Sequence[int], matrix: bool = False) -> int:
+        """matrix=True runs the same prefill with matrix products (long prompts)."""
         n = self.n
         self.P = len(prompt)
         full = []
         h = None
-        for p, tok in enumerate(prompt):
-            h, taps = self.target.forward_token(int(tok), p)
-            full.append(taps)
+        if matrix:
+            h, full = self.target.prefill_matrix([int(t) for t in prompt])
+        else:
+            for p, tok in enumerate(prompt):
+                h, taps = self.target.forward_token(int(tok), p)
+                full.append(taps)
         lg = self.target.logits(h)
         if self.sample:
             pw, _ = sampling.softmax_weights(lg, self.T)
@@ -177,7 +181,7 @@ class SPDOracle:
         else:
             first = self.dec.argmax(("first", 0), lg)
         G = np.stack([self.pdm.feature(full[p], n) for p in range(self.P)])
-        self.pdm.run_rows(G, 0)
+        self.pdm.run_rows(G, 0, matrix=matrix)
         self.pdm.commit(self.P)
         self.tokens = [int(x) for x in prompt] + [int(first)]
         self.seed = (int(first), self.P)
@@ -290,6 +294,22 @@ class SPDOracle:
                 break
             self.cycle()
         return self.tokens[: self.P + self.emitted], self.logs
+
+
+def ar_continue(o: "SPDOracle", n_tokens: int) -> List[int]:
+    """Greedy AR continuation from a prefilled oracle's state (its KV copied).
+
+    Returns the token list of positions 0 .. P + n_tokens (prompt, the
+    prefill token and n_tokens more).
+    """
+    import copy
+
+    tgt = copy.deepcopy(o.target)
+    toks = list(o.tokens[: o.P + 1])
+    while len(toks) < o.P + 1 + n_tokens:
+        h, _ = tgt.forward_token(toks[-1], len(toks) - 1)
+        toks.append(int(np.argmax(tgt.logits(h))))
+    return toks
 
 
 def ar_greedy(w, W, prompt: Sequence[int], G: int):

@@ -138,3 +138,46 @@ def test_kv_length_assertion_guards_append_order():
     M.layer_step(s, W["layers"][0], h, 0, kv)
     with pytest.raises(AssertionError):
         M.layer_step(s, W["layers"][0], h, 2, kv)
+
+
+def test_matrix_layer_equals_row_layer():
+    w = si.tiny(Hq=4, Hkv=2, norm_gain="random", L=2, n=1, Ls=1, anchors=[0, 1], dtype="bf16")
+    W = si.nest_weights(si.weights_numpy_f32(si.make_weights(w)), w)
+    s = M._Shape(w)
+    X = rng.standard_normal((7, w.d)).astype(np.float32)
+    kv1 = M.KVCache(w.max_ctx, w.Hkv, w.hd, True)
+    kv2 = M.KVCache(w.max_ctx, w.Hkv, w.hd, True)
+    # a committed prefix of 3 positions, then 7 rows
+    pre = rng.standard_normal((3, w.d)).astype(np.float32)
+    M.layer_rows(s, W["layers"][0], pre, 0, kv1)
+    M.layer_rows(s, W["layers"][0], pre, 0, kv2)
+    a = M.layer_rows(s, W["layers"][0], X, 3, kv1)
+    b = M.layer_matrix(s, W["layers"][0], X, 3, kv2)
+    np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-6)
+
+
+def test_matrix_prefill_gives_same_spd_run():
+    from oracle import SPDOracle
+    w = si.tiny(L=4, n=2, G=10, P=9, seed=17)
+    W = si.nest_weights(si.weights_numpy_f32(si.make_weights(w)), w)
+    prompt = si.make_prompt(w)
+    a = SPDOracle(w, W)
+    ta, la = a.run(prompt, w.G)
+    b = SPDOracle(w, W)
+    b.prefill(prompt, matrix=True)
+    while b.emitted < w.G:
+        b.cycle()
+    assert b.tokens[: w.P + w.G] == ta
+    assert [l["kv_len"] for l in b.logs] == [l["kv_len"] for l in la]
+
+
+def test_ar_continue_matches_ar_greedy():
+    from oracle import SPDOracle, ar_greedy
+    from oracle.spd import ar_continue
+    w = si.tiny(L=4, n=2, G=10, P=6, seed=18)
+    W = si.nest_weights(si.weights_numpy_f32(si.make_weights(w)), w)
+    prompt = si.make_prompt(w)
+    ref, _ = ar_greedy(w, W, prompt, 8)
+    o = SPDOracle(w, W)
+    o.prefill(prompt, matrix=True)
+    assert ar_continue(o, 7) == ref
