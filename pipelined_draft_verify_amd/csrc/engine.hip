@@ -22,6 +22,7 @@
 #include "common.h"
 #include "control.h"
 #include "gemv.h"
+#include "mfma.h"
 
 using namespace spd;
 
@@ -38,6 +39,7 @@ struct Layout {
   size_t s_q, s_pacc, s_pml, s_o, s_act;
   size_t Xt, Xp, r_q, r_pacc, r_pml, r_o, r_act, taps;
   size_t logits, plogits, pw, parts, pparts, ring;
+  size_t cnt_s, cnt_r, xh, xl, ah, al;
   size_t total;
   int ctx_cap, nsplit, mr, log_cap, nparts_max;
 };
@@ -55,7 +57,7 @@ bool valid_config(const spd_config* c) {
   if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return false;
   if (c->head_dim != 64 && c->head_dim != 128) return false;
   const int G = c->n_heads / c->n_kv_heads;
-  if (G > kMaxQ) return false;
+  if (G > kAttnQ) return false;
   if (c->d_model % 256 || c->d_ffn % 256 || (c->n_heads * c->head_dim) % 256) return false;
   if (c->d_model * c->n_anchors > 64 * 1024) return false;
   if (c->d_ffn > 12288 || c->d_model > 12288 || c->n_heads * c->head_dim > 12288) return false;
@@ -121,6 +123,13 @@ Layout make_layout(const spd_config* c) {
   L.parts = take(sizeof(ArgPair) * L.nparts_max);
   L.pparts = take(sizeof(ArgPair) * L.nparts_max);
   L.ring = take(sizeof(spd_cycle_rec) * (size_t)L.log_cap);
+  L.cnt_s = take(sizeof(int32_t) * (size_t)n * Hkv);
+  L.cnt_r = take(sizeof(int32_t) * (size_t)L.mr * Hkv);
+  const size_t xk = (size_t)std::max(d, Hq * hd);
+  L.xh = take(sizeof(uint16_t) * L.mr * xk);
+  L.xl = take(sizeof(uint16_t) * L.mr * xk);
+  L.ah = take(sizeof(uint16_t) * L.mr * (size_t)F);
+  L.al = take(sizeof(uint16_t) * L.mr * (size_t)F);
   L.total = off;
   return L;
 }
@@ -146,6 +155,8 @@ struct spd_handle {
   float *logits, *plogits, *pw;
   ArgPair *parts, *pparts;
   spd_cycle_rec* ring;
+  int32_t *cnt_s, *cnt_r;
+  uint16_t *xh, *xl, *ah, *al;
   int policy = SPD_DRAFT_NATURAL;
   float p_accept = 0.f;
   const int32_t* ref = nullptr;
@@ -232,8 +243,45 @@ RowsGemv rows_base(spd_t* h) {
   return a;
 }
 
-// One decoder layer over row-batched activations X (target prefill chunk,
-// autoregressive token, or the draft module's trailing rows).
+// Attention over row-batched queries (prefill chunk, AR token or the draft
+// module's trailing rows) with the split merge fused; output fp32 o or, for
+// the matrix-core path, its bf16 hi/lo split.
+template <typename WT>
+void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, int from_ctrl, int max_rows,
+                    bool split_out, hipStream_t s) {
+  const Geo& g = h->g;
+  Attn t;
+  memset(&t, 0, sizeof(t));
+  t.pmode = PM_ROWS;
+  t.layer[0] = layer;
+  t.kc = kc;
+  t.vc = vc;
+  t.q = h->r_q;
+  t.pacc = h->r_pacc;
+  t.pml = h->r_pml;
+  t.o = h->r_o;
+  if (split_out) {
+    t.oh = h->xh;
+    t.ol = h->xl;
+  }
+  t.counters = h->cnt_r;
+  t.from_ctrl = from_ctrl;
+  t.pos0_arg = pos0;
+  t.nrows_arg = M;
+  t.QB = std::max(1, kAttnQ / (g.Hq / g.Hkv));
+  t.qblocks = (max_rows + t.QB - 1) / t.QB;
+  t.ctrl = h->ctrl;
+  t.g = g;
+  const dim3 grid(g.nsplit, g.Hkv * t.qblocks, 1);
+  if (g.hd == 128)
+    hipLaunchKernelGGL((k_attn<WT, 128>), grid, dim3(kWG), 0, s, t);
+  else
+    hipLaunchKernelGGL((k_attn<WT, 64>), grid, dim3(kWG), 0, s, t);
+}
+
+// One decoder layer over row-batched activations X on the VALU row GEMV
+// (fp32 models, and the autoregressive decoder, whose per-row arithmetic
+// matches the stage kernels bit for bit).
 template <typename WT>
 void rows_layer(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int layer, float* X, int M,
                 int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s) {
@@ -259,26 +307,7 @@ void rows_layer(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int l
   a.vc = vc;
   a.kv_len = kv_len;
   launch_rows<WT, EPI_QKV>(h, a, max_rows, s);
-  // attention
-  Attn t;
-  memset(&t, 0, sizeof(t));
-  t.pmode = PM_ROWS;
-  t.layer[0] = layer;
-  t.kc = kc;
-  t.vc = vc;
-  t.q = h->r_q;
-  t.pacc = h->r_pacc;
-  t.pml = h->r_pml;
-  t.o = h->r_o;
-  t.from_ctrl = from_ctrl;
-  t.pos0_arg = pos0;
-  t.nrows_arg = M;
-  t.QB = std::max(1, kMaxQ / (g.Hq / g.Hkv));
-  t.ctrl = h->ctrl;
-  t.g = g;
-  const int qblocks = (max_rows + t.QB - 1) / t.QB;
-  hipLaunchKernelGGL((k_attn<WT>), dim3(g.nsplit, g.Hkv * qblocks, 1), dim3(kWG), 0, s, t);
-  hipLaunchKernelGGL(k_attn_combine, dim3(g.Hq, max_rows), dim3(128), 0, s, t);
+  rows_attention<WT>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, false, s);
   // output projection + residual
   a = rows_base(h);
   a.from_ctrl = from_ctrl;
@@ -317,6 +346,87 @@ void rows_layer(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int l
   a.anchors = taps;
   a.anchor_idx = anchor_idx;
   launch_rows<WT, EPI_RESID>(h, a, max_rows, s);
+}
+
+template <int EPI>
+void launch_mfma(const MfmaGemv& a, int tiles, int max_rows, hipStream_t s) {
+  if (max_rows <= 16)
+    hipLaunchKernelGGL((k_gemv_mfma<EPI, 1>), dim3(tiles), dim3(kWG), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemv_mfma<EPI, 2>), dim3(tiles), dim3(kWG), 0, s, a);
+}
+
+// The same layer on the matrix cores (bf16 weights): the draft module's
+// trailing rows and prefill chunks.
+void rows_layer_mfma(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int layer, float* X, int M,
+                     int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s) {
+  const Geo& g = h->g;
+  const int max_rows = from_ctrl ? g.n + 1 : M;
+  const int qd = g.Hq * g.hd;
+  MfmaGemv a;
+  memset(&a, 0, sizeof(a));
+  a.M_arg = M;
+  a.pos0_arg = pos0;
+  a.from_ctrl = from_ctrl;
+  a.ctrl = h->ctrl;
+  a.g = g;
+  a.rcos = h->rcos;
+  a.rsin = h->rsin;
+  a.anchor_idx = -1;
+  // norm + split, q/k/v + RoPE + cache append
+  hipLaunchKernelGGL(k_split_rows, dim3(max_rows), dim3(kWG), 0, s, X, g.d, M, from_ctrl, g.d,
+                     (const float*)lw.attn_norm, g.eps, h->xh, h->xl, h->ctrl);
+  a.W = (const uint16_t*)lw.w_qkv;
+  a.N = g.qkv_rows;
+  a.K = g.d;
+  a.xh = h->xh;
+  a.xl = h->xl;
+  a.out = h->r_q;
+  a.ldo = qd;
+  a.layer = layer;
+  a.kc = kc;
+  a.vc = vc;
+  a.kv_len = kv_len;
+  launch_mfma<EPI_QKV>(a, g.qkv_rows / 16, max_rows, s);
+  // attention, output split for the next product
+  rows_attention<uint16_t>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, true, s);
+  // output projection + residual
+  a.W = (const uint16_t*)lw.w_o;
+  a.N = g.d;
+  a.K = qd;
+  a.out = X;
+  a.ldo = g.d;
+  a.kv_len = nullptr;
+  launch_mfma<EPI_RESID>(a, g.d / 16, max_rows, s);
+  // norm + split, gate/up + SwiGLU (activation written split)
+  hipLaunchKernelGGL(k_split_rows, dim3(max_rows), dim3(kWG), 0, s, X, g.d, M, from_ctrl, g.d,
+                     (const float*)lw.ffn_norm, g.eps, h->xh, h->xl, h->ctrl);
+  a.W = (const uint16_t*)lw.w_gu;
+  a.N = 2 * g.F;
+  a.K = g.d;
+  a.oh = h->ah;
+  a.ol = h->al;
+  launch_mfma<EPI_SWIGLU>(a, g.F / 8, max_rows, s);
+  // down + residual (+ anchor taps)
+  a.W = (const uint16_t*)lw.w_down;
+  a.N = g.d;
+  a.K = g.F;
+  a.xh = h->ah;
+  a.xl = h->al;
+  a.out = X;
+  a.ldo = g.d;
+  a.anchors = taps;
+  a.anchor_idx = anchor_idx;
+  launch_mfma<EPI_RESID>(a, g.d / 16, max_rows, s);
+}
+
+template <typename WT>
+void layer_rows_any(spd_t* h, bool mfma, const spd_layer_weights& lw, void* kc, void* vc, int layer, float* X,
+                    int M, int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s) {
+  if (mfma && sizeof(WT) == 2)
+    rows_layer_mfma(h, lw, kc, vc, layer, X, M, pos0, from_ctrl, kv_len, taps, anchor_idx, s);
+  else
+    rows_layer<WT>(h, lw, kc, vc, layer, X, M, pos0, from_ctrl, kv_len, taps, anchor_idx, s);
 }
 
 // Head GEMV (final norm + LM head + per-workgroup argmax) on a fixed input row.
@@ -375,7 +485,7 @@ int enqueue_cycle(spd_t* h) {
     a.slot_anchors = h->anchors;
     launch_rows<WT, EPI_STORE>(h, a, g.n + 1, ps);
     for (int l = 0; l < g.Ls; ++l)
-      rows_layer<WT>(h, w.pdm[l], h->pkc, h->pvc, l, h->Xp, 0, 0, 1, nullptr, nullptr, -1, ps);
+      layer_rows_any<WT>(h, true, w.pdm[l], h->pkc, h->pvc, l, h->Xp, 0, 0, 1, nullptr, nullptr, -1, ps);
     StageGemv hd = stage_base(h);
     hd.W[0] = w.pdm_lm_head;
     hd.gamma[0] = (const float*)w.pdm_final_norm;
@@ -450,10 +560,13 @@ int enqueue_cycle(spd_t* h) {
     t.pacc = h->s_pacc;
     t.pml = h->s_pml;
     t.o = h->s_o;
+    t.counters = h->cnt_s;
     t.ctrl = h->ctrl;
     t.g = g;
-    hipLaunchKernelGGL((k_attn<WT>), dim3(g.nsplit, g.Hkv, g.n), dim3(kWG), 0, ss, t);
-    hipLaunchKernelGGL(k_attn_combine, dim3(g.Hq, g.n), dim3(128), 0, ss, t);
+    if (g.hd == 128)
+      hipLaunchKernelGGL((k_attn<WT, 128>), dim3(g.nsplit, g.Hkv, g.n), dim3(kWG), 0, ss, t);
+    else
+      hipLaunchKernelGGL((k_attn<WT, 64>), dim3(g.nsplit, g.Hkv, g.n), dim3(kWG), 0, ss, t);
     // output projection + residual
     StageGemv o = stage_base(h);
     o.n_groups = g.n;
@@ -577,8 +690,8 @@ int do_prefill(spd_t* h, int P) {
     hipLaunchKernelGGL((k_embed_rows<WT>), dim3(M), dim3(kWG), 0, s, h->tokens, s0, (const WT*)w.embed, g.d, h->Xt,
                        h->taps, g.m);
     for (int l = 0; l < g.L; ++l)
-      rows_layer<WT>(h, w.layers[l], h->kc, h->vc, l, h->Xt, M, s0, 0, h->kv_len, h->taps,
-                     g.anchor_of_layer[l + 1], s);
+      layer_rows_any<WT>(h, true, w.layers[l], h->kc, h->vc, l, h->Xt, M, s0, 0, h->kv_len, h->taps,
+                         g.anchor_of_layer[l + 1], s);
     // draft module prefill on the full-depth features of the chunk
     RowsGemv a = rows_base(h);
     a.M_arg = M;
@@ -593,7 +706,7 @@ int do_prefill(spd_t* h, int P) {
     a.ldo = g.d;
     launch_rows<WT, EPI_STORE>(h, a, M, s);
     for (int l = 0; l < g.Ls; ++l)
-      rows_layer<WT>(h, w.pdm[l], h->pkc, h->pvc, l, h->Xp, M, s0, 0, nullptr, nullptr, -1, s);
+      layer_rows_any<WT>(h, true, w.pdm[l], h->pkc, h->pvc, l, h->Xp, M, s0, 0, nullptr, nullptr, -1, s);
     if (s0 + M == P) {
       const int grid = head_fixed<WT>(h, h->Xt + (size_t)(M - 1) * g.d, w.lm_head, w.final_norm, h->logits,
                                       h->parts, s);
@@ -749,6 +862,12 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   h->parts = (ArgPair*)(ws + L.parts);
   h->pparts = (ArgPair*)(ws + L.pparts);
   h->ring = (spd_cycle_rec*)(ws + L.ring);
+  h->cnt_s = (int32_t*)(ws + L.cnt_s);
+  h->cnt_r = (int32_t*)(ws + L.cnt_r);
+  h->xh = (uint16_t*)(ws + L.xh);
+  h->xl = (uint16_t*)(ws + L.xl);
+  h->ah = (uint16_t*)(ws + L.ah);
+  h->al = (uint16_t*)(ws + L.al);
 
   auto fail = [&](hipError_t e) {
     h->hip_err = (int)e;
@@ -767,6 +886,10 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   std::vector<int32_t> zl(SPD_MAX_LAYERS, 0);
   if ((e = hipMemcpy(h->kv_len, zl.data(), sizeof(int32_t) * SPD_MAX_LAYERS, hipMemcpyHostToDevice)) != hipSuccess)
     return fail(e);
+  // arrival counters start at zero (each merging workgroup resets its own);
+  // the bf16 split buffers are cleared so rows past M hold finite values
+  if ((e = hipMemset(ws + L.cnt_s, 0, L.xh - L.cnt_s)) != hipSuccess) return fail(e);
+  if ((e = hipMemset(ws + L.xh, 0, L.total - L.xh)) != hipSuccess) return fail(e);
   hipLaunchKernelGGL(k_rope_table, dim3(512), dim3(256), 0, h->ss, h->rcos, h->rsin, L.ctx_cap, g.hd,
                      (double)cfg->rope_base);
   if ((e = hipGetLastError()) != hipSuccess) return fail(e);
