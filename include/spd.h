@@ -201,6 +201,17 @@ SPD_API int spd_init(const spd_config *cfg, const spd_weights *w, void *workspac
 SPD_API int spd_set_draft_policy(spd_t *h, int32_t policy, float p_accept, const int32_t *ref_tokens_dev,
                          int32_t ref_len);
 
+/* How spd_cycle submits work.  SPD_LAUNCH_GRAPH (the default): each
+ * stream's chain of one cycle is captured once as a HIP graph (on the first
+ * spd_cycle after the policy or uniforms changed) and replayed; a cycle then
+ * costs one entry launch, two graph launches and four event calls on the
+ * host.  SPD_LAUNCH_EAGER: every kernel is launched individually (needed for
+ * the per-launch gate/up timing of spd_timing_*).  Waits for both streams.
+ * Errors: SPD_EINVAL. */
+#define SPD_LAUNCH_EAGER 0
+#define SPD_LAUNCH_GRAPH 1
+SPD_API int spd_set_launch_mode(spd_t *h, int32_t mode);
+
 /* Per-position uniforms, device fp32 [n_positions][SPD_U_COUNT], values in
  * [0,1); row p is used for the decisions about position p (draft draw,
  * acceptance, residual redraw, prefill draw, forced-acceptance test).
@@ -268,8 +279,8 @@ SPD_API int spd_debug_read(spd_t *h, int32_t what, int32_t index, void *out_host
 
 /* Timing instrumentation.  spd_timing_enable(h, 1) makes every later cycle
  * record HIP events: at the start of the cycle, after the stage step +
- * verification, after the PDM, and around every launch of the stage-grouped
- * gate/up projection (the largest weight stream).  spd_timing_read waits,
+ * verification, after the PDM, and (eager launch mode only) around every
+ * launch of the stage-grouped gate/up projection (the largest weight stream).  spd_timing_read waits,
  * returns the number of cycles timed and fills (each may be NULL):
  *   cycle_ms[3*i+0..2]  end of stage work, end of PDM work, cycle end (max of
  *                       both) of cycle i, in ms after that cycle's start;

@@ -75,6 +75,7 @@ SIGNATURES = [
     ("spd_init", c_int32, [POINTER(spd_config), POINTER(spd_weights), c_void_p, c_size_t, c_void_p, c_void_p,
                            POINTER(c_void_p)]),
     ("spd_set_draft_policy", c_int32, [c_void_p, c_int32, c_float, c_void_p, c_int32]),
+    ("spd_set_launch_mode", c_int32, [c_void_p, c_int32]),
     ("spd_set_uniforms", c_int32, [c_void_p, c_void_p, c_int32]),
     ("spd_prefill", c_int32, [c_void_p, POINTER(c_int32), c_int32, POINTER(c_int32)]),
     ("spd_cycle", c_int32, [c_void_p, c_int32, c_void_p]),
@@ -142,6 +143,13 @@ def spd_init(cfg, weights, workspace_ptr, ws_bytes, stage_stream, pdm_stream):
 
 def spd_set_draft_policy(h, policy, p_accept, ref_ptr, ref_len):
     return check("spd_set_draft_policy", lib().spd_set_draft_policy(h, policy, p_accept, c_void_p(ref_ptr), ref_len))
+
+
+SPD_LAUNCH_EAGER, SPD_LAUNCH_GRAPH = 0, 1
+
+
+def spd_set_launch_mode(h, mode):
+    return check("spd_set_launch_mode", lib().spd_set_launch_mode(h, mode))
 
 
 def spd_set_uniforms(h, uni_ptr, n_positions):

@@ -40,7 +40,9 @@ struct Ctrl {
   int32_t r_raw;      // last cycle: PDM argmax / draw
   uint32_t flags;     // accumulated SPD_FLAG_*
   int32_t ar_pos;     // position of the token the AR decoder processes next
-  int32_t pad[13];
+  int32_t launches;   // cycles enqueued (executed or idle): selects the record slot
+  int32_t rec_slot;   // record slot of the current cycle
+  int32_t pad[11];
 };
 
 struct ArgPair {

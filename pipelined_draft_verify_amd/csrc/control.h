@@ -151,10 +151,15 @@ __global__ void k_rope_table(float* cosv, float* sinv, int ctx, int hd, double b
 template <typename WT>
 __global__ __launch_bounds__(kWG) void k_entry(Ctrl* C, const Geo g, int32_t* tokens, const WT* embed,
                                                float* hslots, float* anchors, spd_cycle_rec* ring,
-                                               int log_cap, int cyc) {
+                                               int log_cap) {
   __shared__ int s_tok, s_pos, s_ok;
   if (threadIdx.x == 0) {
-    spd_cycle_rec* r = ring + (cyc % log_cap);
+    // every enqueued cycle takes the next record slot, idle or not, so the
+    // host knows where the records of its calls are
+    const int cyc = C->launches;
+    C->launches = cyc + 1;
+    C->rec_slot = cyc % log_cap;
+    spd_cycle_rec* r = ring + C->rec_slot;
     r->cycle = cyc;
     r->pdm_argmax = r->draft = r->exit_pos = r->target_token = -1;
     r->accepted = -1;
@@ -228,7 +233,6 @@ struct VerifyArgs {
   int32_t* tokens;
   int32_t* kv_len;
   spd_cycle_rec* ring;
-  int log_cap, cyc;
   Ctrl* ctrl;
   Geo g;
 };
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
   Ctrl* C = A.ctrl;
   const Geo& g = A.g;
   if (!C->active) return;
-  spd_cycle_rec* rec = A.ring + (A.cyc % A.log_cap);
+  spd_cycle_rec* rec = A.ring + C->rec_slot;
   const bool exit = (C->a == g.n);
   if (!exit) {
     __syncthreads();
@@ -333,7 +337,6 @@ struct FinalizeArgs {
   const int32_t* ref;
   int ref_len;
   spd_cycle_rec* ring;
-  int log_cap, cyc;
   Ctrl* ctrl;
   Geo g;
 };
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(kCtlThreads) void k_pdm_finalize(const FinalizeArgs
     C->r_draft = d;
     C->r_raw = raw;
     C->C += C->pending;  // the just-verified row's key/values stay cached
-    spd_cycle_rec* rec = A.ring + (A.cyc % A.log_cap);
+    spd_cycle_rec* rec = A.ring + C->rec_slot;
     rec->pdm_argmax = raw;
     rec->draft = d;
     rec->pdm_len = C->C;

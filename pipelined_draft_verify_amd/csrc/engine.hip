@@ -168,6 +168,9 @@ struct spd_handle {
   int hip_err = 0;
   // timing
   int timing = 0;
+  int launch_mode = 1;  // 0: every kernel launched from the host; 1: per-stream graphs
+  int graphs_valid = 0;
+  hipGraphExec_t gx_stage = nullptr, gx_pdm = nullptr;
   std::vector<hipEvent_t> pool;
   size_t pool_next = 0;
   std::vector<hipEvent_t> cyc_ev;   // 3 per timed cycle: start, stage end, pdm end
@@ -449,25 +452,12 @@ int head_fixed(spd_t* h, const float* x, const void* W, const void* gamma, float
   return grid;
 }
 
+// Draft-module chain of one cycle (draft stream): anchor gather + FC, Ls
+// layers over the trailing rows, draft head, finalisation.
 template <typename WT>
-int enqueue_cycle(spd_t* h) {
+int pdm_chain(spd_t* h, hipStream_t ps) {
   const Geo& g = h->g;
   const spd_weights& w = h->w;
-  hipStream_t ss = h->ss, ps = h->ps;
-  const int c = (int)(h->cyc % 0x7FFFFFFF);
-  hipEvent_t e_start = nullptr, e_stage = nullptr, e_pdm_t = nullptr;
-  if (h->timing) {
-    e_start = pool_event(h);
-    e_stage = pool_event(h);
-    e_pdm_t = pool_event(h);
-  }
-  HIPCHK(h, hipStreamWaitEvent(ss, h->ev_pdm, 0));
-  if (e_start) HIPCHK(h, hipEventRecord(e_start, ss));
-  hipLaunchKernelGGL((k_entry<WT>), dim3(1), dim3(kWG), 0, ss, h->ctrl, g, h->tokens, (const WT*)w.embed,
-                     h->hslots, h->anchors, h->ring, h->lay.log_cap, c);
-  HIPCHK(h, hipEventRecord(h->ev_entry, ss));
-  HIPCHK(h, hipStreamWaitEvent(ps, h->ev_entry, 0));
-
   // ---------------- draft module (pre-step) on the draft stream ----------------
   {
     RowsGemv a = rows_base(h);
@@ -516,15 +506,20 @@ int enqueue_cycle(spd_t* h) {
     f.ref = h->ref;
     f.ref_len = h->ref_len;
     f.ring = h->ring;
-    f.log_cap = h->lay.log_cap;
-    f.cyc = c;
     f.ctrl = h->ctrl;
     f.g = g;
     hipLaunchKernelGGL(k_pdm_finalize, dim3(1), dim3(kCtlThreads), 0, ps, f);
-    if (e_pdm_t) HIPCHK(h, hipEventRecord(e_pdm_t, ps));
-    HIPCHK(h, hipEventRecord(h->ev_pdm, ps));
   }
+  return hipGetLastError() == hipSuccess ? SPD_OK : SPD_EHIP;
+}
 
+// Stage chain of one cycle (stage stream): L/n stage-grouped layer
+// sub-steps, verification head, verify / rollback.  With timing_gu, every
+// gate/up launch is bracketed by HIP events on this stream.
+template <typename WT>
+int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
+  const Geo& g = h->g;
+  const spd_weights& w = h->w;
   // ---------------- stage step on the stage stream ----------------
   const int qd = g.Hq * g.hd;
   for (int j = 0; j < g.per; ++j) {
@@ -602,7 +597,7 @@ int enqueue_cycle(spd_t* h) {
     u.out = h->s_act;
     u.out_stride = g.F;
     hipEvent_t g0 = nullptr, g1 = nullptr;
-    if (h->timing) {
+    if (timing_gu) {
       g0 = pool_event(h);
       g1 = pool_event(h);
       HIPCHK(h, hipEventRecord(g0, ss));
@@ -664,11 +659,64 @@ int enqueue_cycle(spd_t* h) {
   v.tokens = h->tokens;
   v.kv_len = h->kv_len;
   v.ring = h->ring;
-  v.log_cap = h->lay.log_cap;
-  v.cyc = c;
   v.ctrl = h->ctrl;
   v.g = g;
   hipLaunchKernelGGL(k_verify, dim3(1), dim3(kCtlThreads), 0, ss, v);
+  return hipGetLastError() == hipSuccess ? SPD_OK : SPD_EHIP;
+}
+
+// Capture each stream's chain once as a HIP graph (the chains read every
+// per-cycle value from device memory, so one graph serves every cycle).
+template <typename WT>
+int capture_graphs(spd_t* h) {
+  if (h->graphs_valid) return SPD_OK;
+  if (h->gx_stage) (void)hipGraphExecDestroy(h->gx_stage);
+  if (h->gx_pdm) (void)hipGraphExecDestroy(h->gx_pdm);
+  h->gx_stage = h->gx_pdm = nullptr;
+  hipGraph_t gs = nullptr, gp = nullptr;
+  HIPCHK(h, hipStreamBeginCapture(h->ps, hipStreamCaptureModeThreadLocal));
+  int r = pdm_chain<WT>(h, h->ps);
+  HIPCHK(h, hipStreamEndCapture(h->ps, &gp));
+  if (r) return r;
+  HIPCHK(h, hipStreamBeginCapture(h->ss, hipStreamCaptureModeThreadLocal));
+  r = stage_chain<WT>(h, h->ss, false);
+  HIPCHK(h, hipStreamEndCapture(h->ss, &gs));
+  if (r) return r;
+  HIPCHK(h, hipGraphInstantiate(&h->gx_pdm, gp, nullptr, nullptr, 0));
+  HIPCHK(h, hipGraphInstantiate(&h->gx_stage, gs, nullptr, nullptr, 0));
+  (void)hipGraphDestroy(gp);
+  (void)hipGraphDestroy(gs);
+  h->graphs_valid = 1;
+  return SPD_OK;
+}
+
+template <typename WT>
+int enqueue_cycle(spd_t* h) {
+  const Geo& g = h->g;
+  hipStream_t ss = h->ss, ps = h->ps;
+  const bool graph = h->launch_mode == 1;
+  hipEvent_t e_start = nullptr, e_stage = nullptr, e_pdm_t = nullptr;
+  if (h->timing) {
+    e_start = pool_event(h);
+    e_stage = pool_event(h);
+    e_pdm_t = pool_event(h);
+    if (!e_start || !e_stage || !e_pdm_t) return SPD_EHIP;
+  }
+  // join: the previous cycle's draft is done
+  HIPCHK(h, hipStreamWaitEvent(ss, h->ev_pdm, 0));
+  if (e_start) HIPCHK(h, hipEventRecord(e_start, ss));
+  hipLaunchKernelGGL((k_entry<WT>), dim3(1), dim3(kWG), 0, ss, h->ctrl, g, h->tokens, (const WT*)h->w.embed,
+                     h->hslots, h->anchors, h->ring, h->lay.log_cap);
+  // fork
+  HIPCHK(h, hipEventRecord(h->ev_entry, ss));
+  HIPCHK(h, hipStreamWaitEvent(ps, h->ev_entry, 0));
+  int r = graph ? (hipGraphLaunch(h->gx_pdm, ps) == hipSuccess ? SPD_OK : SPD_EHIP) : pdm_chain<WT>(h, ps);
+  if (r) return r;
+  if (e_pdm_t) HIPCHK(h, hipEventRecord(e_pdm_t, ps));
+  HIPCHK(h, hipEventRecord(h->ev_pdm, ps));
+  r = graph ? (hipGraphLaunch(h->gx_stage, ss) == hipSuccess ? SPD_OK : SPD_EHIP)
+            : stage_chain<WT>(h, ss, h->timing != 0);
+  if (r) return r;
   if (e_stage) {
     HIPCHK(h, hipEventRecord(e_stage, ss));
     h->cyc_ev.push_back(e_start);
@@ -901,6 +949,7 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
 
 int spd_set_draft_policy(spd_t* h, int32_t policy, float p_accept, const int32_t* ref_tokens_dev, int32_t ref_len) {
   if (!h) return SPD_EINVAL;
+  h->graphs_valid = 0;
   if (policy == SPD_DRAFT_NATURAL) {
     h->policy = policy;
     return SPD_OK;
@@ -914,10 +963,19 @@ int spd_set_draft_policy(spd_t* h, int32_t policy, float p_accept, const int32_t
   return SPD_OK;
 }
 
+int spd_set_launch_mode(spd_t* h, int32_t mode) {
+  if (!h || (mode != SPD_LAUNCH_EAGER && mode != SPD_LAUNCH_GRAPH)) return SPD_EINVAL;
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  HIPCHK(h, hipStreamSynchronize(h->ps));
+  h->launch_mode = mode;
+  return SPD_OK;
+}
+
 int spd_set_uniforms(spd_t* h, const float* uniforms_dev, int32_t n_positions) {
   if (!h || !uniforms_dev || n_positions < h->cfg.max_ctx) return SPD_EINVAL;
   h->uni = uniforms_dev;
   h->uni_len = n_positions;
+  h->graphs_valid = 0;
   return SPD_OK;
 }
 
@@ -945,6 +1003,7 @@ int spd_prefill(spd_t* h, const int32_t* prompt_host, int32_t len, int32_t* firs
   c.pend_next = 0;
   c.r_exit = -1;
   c.r_accept = -1;
+  c.launches = (int32_t)(h->cyc % 0x40000000);
   if ((r = write_ctrl(h, &c))) return r;
   r = h->cfg.dtype == SPD_DTYPE_BF16 ? do_prefill<uint16_t>(h, len) : do_prefill<float>(h, len);
   if (r) return r;
@@ -967,6 +1026,10 @@ int spd_cycle(spd_t* h, int32_t n_cycles, spd_cycle_rec* log_host) {
   if ((h->policy == SPD_DRAFT_FORCED || h->cfg.mode == SPD_MODE_SAMPLE) && !h->uni) return SPD_ESTATE;
   if (log_host && n_cycles > h->lay.log_cap) return SPD_EINVAL;
   const long long c0 = h->cyc;
+  if (h->launch_mode == 1 && n_cycles > 0) {
+    const int r = h->cfg.dtype == SPD_DTYPE_BF16 ? capture_graphs<uint16_t>(h) : capture_graphs<float>(h);
+    if (r) return r;
+  }
   for (int i = 0; i < n_cycles; ++i) {
     const int r = h->cfg.dtype == SPD_DTYPE_BF16 ? enqueue_cycle<uint16_t>(h) : enqueue_cycle<float>(h);
     if (r) return r;
@@ -976,7 +1039,7 @@ int spd_cycle(spd_t* h, int32_t n_cycles, spd_cycle_rec* log_host) {
     const int cap = h->lay.log_cap;
     long long done = 0;
     while (done < n_cycles) {
-      const int slot = (int)((c0 + done) % 0x7FFFFFFF % cap);
+      const int slot = (int)((c0 + done) % cap);
       const long long cnt = std::min<long long>(n_cycles - done, cap - slot);
       HIPCHK(h, hipMemcpyAsync(log_host + done, h->ring + slot, sizeof(spd_cycle_rec) * cnt,
                                hipMemcpyDeviceToHost, h->ss));
@@ -1021,6 +1084,7 @@ int spd_rollback(spd_t* h, int32_t keep_len, int32_t reseed_token) {
   n.r_exit = -1;
   n.r_accept = -1;
   n.flags = c.flags;
+  n.launches = c.launches;
   if ((r = set_kv_len(h, keep_len))) return r;
   HIPCHK(h, hipMemcpy(h->tokens + keep_len, &reseed_token, sizeof(int32_t), hipMemcpyHostToDevice));
   if ((r = write_ctrl(h, &n))) return r;
@@ -1166,6 +1230,8 @@ int spd_destroy(spd_t* h) {
   (void)hipEventDestroy(h->ev_entry);
   (void)hipEventDestroy(h->ev_pdm);
   for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
+  if (h->gx_stage) (void)hipGraphExecDestroy(h->gx_stage);
+  if (h->gx_pdm) (void)hipGraphExecDestroy(h->gx_pdm);
   delete h;
   return SPD_OK;
 }
