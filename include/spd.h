@@ -58,7 +58,7 @@ extern "C" {
 #define SPD_MAX_LAYERS 64
 #define SPD_MAX_PDM_LAYERS 8
 #define SPD_MAX_ANCHORS 8
-#define SPD_MAX_STAGES 32
+#define SPD_MAX_STAGES 16
 
 /* return codes */
 #define SPD_OK 0
@@ -103,7 +103,8 @@ extern "C" {
  * residual, RMSNorm (ffn_norm), SwiGLU (silu(gate) * up), down projection +
  * residual; no biases.  The PDM layers have the same shape with their own
  * weights.  Constraints checked by spd_init ([RB] core method): n_stages
- * divides n_layers; pdm_layers <= n_layers / n_stages; anchors strictly
+ * divides n_layers and is at most SPD_MAX_STAGES (the draft module batches
+ * up to n_stages + 1 rows); pdm_layers <= n_layers / n_stages; anchors strictly
  * increasing with anchors[0] == 0 and anchors[n_anchors-1] <= n_layers;
  * n_heads % n_kv_heads == 0; head_dim in {64, 128}; d_model, d_ffn and
  * n_heads*head_dim multiples of 256.

@@ -44,6 +44,17 @@ def rope_cos_sin(pos: int, hd: int, base: float):
     return np.cos(ang).astype(F32), np.sin(ang).astype(F32)
 
 
+def rope_tables(positions, hd: int, base: float):
+    """`rope_cos_sin` for many positions at once: cos, sin [len(positions), hd/2].
+
+    The same fp64 operations per element, so the values are identical.
+    """
+    i = np.arange(hd // 2, dtype=np.float64)
+    theta = np.power(np.float64(base), -2.0 * i / hd)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang).astype(F32), np.sin(ang).astype(F32)
+
+
 def apply_rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
     """Rotate-half RoPE on the last axis: pairs (i, i + hd/2) rotate by angle i."""
     h = x.shape[-1] // 2

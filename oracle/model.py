@@ -5,7 +5,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from .layers import F32, apply_rope, attention, bf16_round, rmsnorm, rope_cos_sin, silu
+from .layers import F32, apply_rope, attention, bf16_round, rmsnorm, rope_cos_sin, rope_tables, silu
 from .schedule import pattern, stage_layers
 
 
@@ -100,10 +100,15 @@ def layer_rows(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache) -> np.ndarr
 def layer_matrix(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache) -> np.ndarray:
     """`layer_rows` written with matrix products over all M rows at once.
 
-    The same definition (row i attends to cached positions and rows <= i);
-    only the order of floating-point operations differs.  Used for long
-    prompts, where the row-at-a-time form is too slow.
+    The same definition (row i attends to cached positions and rows <= i,
+    masked scores are -inf before the softmax); only the order of
+    floating-point operations differs.  Used for long sequences, where the
+    row-at-a-time form is too slow; the softmax and SiLU of the big score and
+    gate matrices use torch's (multi-threaded) CPU functions as library steps.
+    Pinned against `layer_rows` in the CPU tests.
     """
+    import torch
+
     M = X.shape[0]
     Hq, Hkv, hd = s.Hq, s.Hkv, s.hd
     U = np.stack([rmsnorm(X[i], lw["attn_norm"], s.eps) for i in range(M)])
@@ -111,28 +116,28 @@ def layer_matrix(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache) -> np.nda
     Q = QKV[:, : Hq * hd].reshape(M, Hq, hd)
     Kn = QKV[:, Hq * hd:(Hq + Hkv) * hd].reshape(M, Hkv, hd)
     Vn = QKV[:, (Hq + Hkv) * hd:].reshape(M, Hkv, hd)
+    cos, sin = rope_tables(np.arange(pos0, pos0 + M), hd, s.base)
+    cos, sin = cos[:, None, :], sin[:, None, :]
+    Q = apply_rope(Q, cos, sin)
+    Kr = apply_rope(Kn, cos, sin)
     for i in range(M):
-        c, sn = rope_cos_sin(pos0 + i, hd, s.base)
-        Q[i] = apply_rope(Q[i], c, sn)
-        kv.write(pos0 + i, apply_rope(Kn[i], c, sn), Vn[i])
+        kv.write(pos0 + i, Kr[i], Vn[i])
     T = pos0 + M
     grp = Hq // Hkv
     scale = F32(1.0 / np.sqrt(hd))
-    mask = np.arange(T)[None, :] > (pos0 + np.arange(M))[:, None]
+    mask = torch.from_numpy(np.arange(T)[None, :] > (pos0 + np.arange(M))[:, None])
     O = np.empty((M, Hq, hd), dtype=F32)
     for h in range(Hq):
-        k_ = kv.K[:T, h // grp, :]
-        v_ = kv.V[:T, h // grp, :]
-        S = (Q[:, h, :] @ k_.T) * scale
-        S[mask] = -np.inf
-        S = S - S.max(axis=1, keepdims=True)
-        Pm = np.exp(S)
-        Pm = Pm / Pm.sum(axis=1, keepdims=True, dtype=F32)
-        O[:, h, :] = Pm @ v_
+        k_ = torch.from_numpy(np.ascontiguousarray(kv.K[:T, h // grp, :]))
+        v_ = torch.from_numpy(np.ascontiguousarray(kv.V[:T, h // grp, :]))
+        S = (torch.from_numpy(np.ascontiguousarray(Q[:, h, :])) @ k_.T) * float(scale)
+        S.masked_fill_(mask, float("-inf"))
+        O[:, h, :] = (torch.softmax(S, dim=1) @ v_).numpy()
     H = X + O.reshape(M, Hq * hd) @ lw["w_o"].T
     U2 = np.stack([rmsnorm(H[i], lw["ffn_norm"], s.eps) for i in range(M)])
-    GU = U2 @ lw["w_gu"].T
-    return (H + (silu(GU[:, : s.F]) * GU[:, s.F:]) @ lw["w_down"].T).astype(F32)
+    GU = torch.from_numpy(np.ascontiguousarray(U2 @ lw["w_gu"].T))
+    act = (torch.nn.functional.silu(GU[:, : s.F]) * GU[:, s.F:]).numpy()
+    return (H + act @ lw["w_down"].T).astype(F32)
 
 
 class Target:
@@ -165,6 +170,11 @@ class Target:
         """Full-depth logits W_lm * rmsnorm(h^(L)) (float32)."""
         return self.W["lm_head"] @ rmsnorm(h, self.W["final_norm"], self.s.eps)
 
+    def logits_rows(self, H: np.ndarray) -> np.ndarray:
+        """`logits` of every row of H [M, d] with one matrix product: [M, V]."""
+        U = np.stack([rmsnorm(h, self.W["final_norm"], self.s.eps) for h in H])
+        return (U @ self.W["lm_head"].T).astype(F32)
+
     def forward_token(self, tok: int, pos: int):
         """Whole-model pass for one token: (final hidden, anchors)."""
         taps = [None] * len(self.s.anchors)
@@ -177,10 +187,11 @@ class Target:
         for kv in self.kv:
             kv.length = length
 
-    def prefill_matrix(self, tokens: Sequence[int]):
+    def prefill_matrix(self, tokens: Sequence[int], all_rows: bool = False):
         """Whole prompt through every layer at once (matrix form of forward_token).
 
-        Returns (final hidden of the last position, anchors [P][m] lists).
+        Returns (final hidden of the last position -- of every position [P, d]
+        if `all_rows` --, anchors [P][m] lists).
         """
         P = len(tokens)
         H = np.stack([self.embed(int(t)) for t in tokens])
@@ -195,7 +206,7 @@ class Target:
             if (l + 1) in self.anchor_at:
                 for p in range(P):
                     taps[p][self.anchor_at[l + 1]] = H[p].copy()
-        return H[-1].copy(), taps
+        return (H.copy() if all_rows else H[-1].copy()), taps
 
 
 class PDM:
@@ -221,6 +232,12 @@ class PDM:
         f = pattern(k, self.s.anchors, self.s.L, self.s.n)
         x = np.concatenate([taps[i] for i in range(f + 1)]).astype(F32)
         return self.W["fc"][f] @ x
+
+    def feature_rows(self, taps_rows: Sequence[Sequence[np.ndarray]], k: int) -> np.ndarray:
+        """`feature` of many positions at one depth k with one matrix product: [M, d_pdm]."""
+        f = pattern(k, self.s.anchors, self.s.L, self.s.n)
+        X = np.stack([np.concatenate([taps[i] for i in range(f + 1)]) for taps in taps_rows]).astype(F32)
+        return (X @ self.W["fc"][f].T).astype(F32)
 
     def run_rows(self, G: np.ndarray, pos0: int, matrix: bool = False) -> np.ndarray:
         """All Ls layers over feature rows at positions pos0.. (pos0 == C)."""

@@ -92,18 +92,20 @@ class Decisions:
     Greedy argmax picks the lowest id among equal maxima.  With a teacher (the
     decisions another implementation took, keyed by (kind, cycle)), a differing
     choice is adopted when it is also valid within `tol` -- a logit within tol
-    of the maximum, or a uniform within tol (relative) of a sampling boundary
-    -- and recorded; otherwise it is recorded as a mismatch.  Without a
-    teacher nothing is adopted.
+    of the maximum (`tol`, logit units), or a sampling threshold within
+    `sample_tol` of the boundary it falls on (as a fraction of the total mass,
+    or for the accept test of Q(x)) -- and recorded; otherwise it is recorded
+    as a mismatch.  Without a teacher nothing is adopted.
     """
 
-    def __init__(self, teacher: Optional[Dict] = None, tol: float = 0.0):
+    def __init__(self, teacher: Optional[Dict] = None, tol: float = 0.0, sample_tol: Optional[float] = None):
         self.teacher = teacher
         self.tol = tol
+        self.sample_tol = tol if sample_tol is None else sample_tol
         self.adopted: List[tuple] = []
         self.mismatch: List[tuple] = []
 
-    def _teach(self, key, mine, valid_fn):
+    def _teach(self, key, mine, valid_fn, tol):
         if self.teacher is None or key not in self.teacher:
             return mine
         theirs = self.teacher[key]
@@ -111,12 +113,12 @@ class Decisions:
             return mine
         gap = valid_fn(theirs)
         rec = (key, mine, theirs, gap)
-        (self.adopted if gap <= self.tol else self.mismatch).append(rec)
+        (self.adopted if gap <= tol else self.mismatch).append(rec)
         return theirs
 
     def argmax(self, key, logits: np.ndarray) -> int:
         y = int(np.argmax(logits))
-        return self._teach(key, y, lambda t: float(logits[y] - logits[t]))
+        return self._teach(key, y, lambda t: float(logits[y] - logits[t]), self.tol)
 
     def sample(self, key, weights: np.ndarray, u: float) -> int:
         i, _ = sampling.inverse_cdf(weights, u)
@@ -126,18 +128,18 @@ class Decisions:
         def gap(t):
             lo = c[t - 1] if t > 0 else 0.0
             return float(max(lo - thr, thr - c[t], 0.0) / c[-1])
-        return self._teach(key, i, gap)
+        return self._teach(key, i, gap, self.sample_tol)
 
     def accept(self, key, p_w, p_Z, q_w, q_Z, x, u) -> bool:
         acc, g = sampling.accept_test(p_w, p_Z, q_w, q_Z, x, u)
-        return bool(self._teach(key, acc, lambda t: g))
+        return bool(self._teach(key, acc, lambda t: g, self.sample_tol))
 
 
 class SPDOracle:
     """Runs prefill and SPD cycles, logging every cycle's integer state."""
 
     def __init__(self, w, W, policy=None, uniforms: Optional[np.ndarray] = None,
-                 teacher: Optional[Dict] = None, tol: float = 0.0):
+                 teacher: Optional[Dict] = None, tol: float = 0.0, sample_tol: Optional[float] = None):
         self.w = w
         self.n, self.L, self.V = w.n, w.L, w.V
         self.target = Target(w, W)
@@ -148,7 +150,7 @@ class SPDOracle:
         self.u = uniforms
         if self.sample:
             assert uniforms is not None, "sampling needs the uniform table"
-        self.dec = Decisions(teacher, tol)
+        self.dec = Decisions(teacher, tol, sample_tol)
         self.tokens: List[int] = []
         self.inflight: List[list] = []      # [pos, depth, h], oldest first
         self.anchors: Dict[int, list] = {}  # pos -> [h^(b_i) or None]

@@ -219,7 +219,6 @@ void launch_rows(spd_t* h, RowsGemv a, int max_rows, hipStream_t s) {
   for (int rb = 0; rb < max_rows; rb += kRowsMR) {
     a.row_base = rb;
     hipLaunchKernelGGL((k_gemv_rows<WT, EPI>), dim3(tiles, a.n_groups), dim3(kWG), 0, s, a);
-    if (a.rmode == RM_FC) break;
   }
 }
 

@@ -306,11 +306,15 @@ __global__ __launch_bounds__(kWG) void k_gemv_rows(const RowsGemv A) {
     // rows whose depth uses pattern `grp`: trailing row i is at position C+i,
     // depth n for the committed-next row, else t - position
     if (threadIdx.x == 0) {
-      int cnt = 0;
+      // pass `row_base / kRowsMR` takes the matching rows row_base .. row_base + kRowsMR - 1
+      int cnt = 0, seen = 0;
       for (int i = 0; i < Mtot; ++i) {
         const int p = pos0 + i;
         const int dep = (C->pending && i == 0) ? g.n : (C->t - p);
-        if (g.fpat[dep] == grp && cnt < kRowsMR) rsrc[cnt++] = i;
+        if (g.fpat[dep] == grp) {
+          if (seen >= A.row_base && cnt < kRowsMR) rsrc[cnt++] = i;
+          ++seen;
+        }
       }
       rcount = cnt;
     }

@@ -1,0 +1,262 @@
+"""Full-size runs of the HIP path and the oracle checks that scale to them.
+
+A full-size generation is too long for the oracle to run cycle by cycle, so
+it is checked in pieces that together cover every integer a cycle produces,
+plus floating-point state at two stopping points:
+
+1. integer replay (oracle.replay) of every cycle from the integers that
+   floating point decided; under greedy decoding the output must also equal
+   the GPU's own autoregressive decode (losslessness holds at any size);
+2. every verification: one oracle target forward (matrix form) over the
+   final sequence gives the logits at every exiting position, so the target
+   token of every exit is compared with the oracle's argmax (a differing
+   choice must be a near-tie: its oracle logit within the tolerance of the
+   maximum);
+3. the draft module at sampled cycles whose in-flight tokens all survived
+   (so that the forward's anchors are theirs): the oracle rebuilds the
+   trailing rows' features at their depths, runs its layers over the
+   committed prefix (one matrix pass over every position's full-depth
+   feature) plus those rows, and its head.  Under sampling, each checked
+   verification recomputes Q at the cycle that drafted the verified position
+   and retakes the draw, the accept test and the residual redraw with the
+   same seeded uniforms.
+
+The GPU side runs exactly as the benchmark times it: weights generated on the
+device, graph-launched cycles, the forced-acceptance reference from the
+GPU's own autoregressive decode.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import seeded_inputs as si
+from oracle import sampling, schedule
+from oracle.model import PDM, Target
+from oracle.replay import Replay
+from oracle.spd import Decisions, ForcedPolicy
+from seeded_inputs import U_ACCEPT, U_DRAFT, U_RESAMPLE, U_TARGET
+
+IDLE = 8  # record flag of a cycle enqueued after the generation ended
+TOL = {"f32": 1e-4, "bf16": 0.05}       # near-tie margin of an argmax (logit units)
+STOL = {"f32": 1e-5, "bf16": 2e-4}      # near-tie of a draw (fraction of the mass)
+RTOL = {"f32": 1e-4, "bf16": 2e-2}      # rel-L2 of hidden states, anchors, logits, KV
+INT_FIELDS = [("t", "t"), ("occupancy", "a"), ("pending_row", "pending_row"), ("draft", "draft"),
+              ("exit_pos", "exit_pos"), ("target_token", "y"), ("accepted", "accept"),
+              ("pdm_len", "pdm_len"), ("emitted", "emitted")]
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def _snapshot(eng, recs):
+    last = recs[-1]
+    t, a = int(last["t"]), int(last["occupancy"])
+    snap = dict(index=len(recs) - 1, pdm_logits=eng.pdm_logits(),
+                anchors={p: eng.anchors(p) for p in range(t - a + 1, t + 1)})
+    ex = np.flatnonzero(recs["exit_pos"] >= 0)
+    if len(ex):
+        snap["exit_index"] = int(ex[-1])
+        snap["logits"] = eng.logits()
+    return snap
+
+
+def gpu_run(name: str) -> dict:
+    """One full generation of workload `name` on cuda:0 (graph launch mode)."""
+    import torch
+    from pipelined_draft_verify_amd import SPDEngine
+
+    w = si.workload(name)
+    T = si.make_weights(w, "cuda:0")
+    eng = SPDEngine(w, T)
+    eng.set_launch_mode(True)
+    uni = si.make_uniforms(w)
+    eng.set_uniforms(uni)
+    prompt = si.make_prompt(w)
+    first = int(eng.prefill(prompt))
+    ref = None
+    if w.mode == "greedy":
+        ar = eng.generate_ar(w.G - 1)
+        ref = [int(x) for x in prompt] + [first] + [int(x) for x in ar]
+        eng.rollback(w.P, first)
+        if w.policy == "forced":
+            eng.set_forced(ref, w.p_accept)
+    k0 = 3 * w.n + 2
+    buf = eng.enqueue(k0)
+    eng.sync()
+    head = eng.records_of(buf)
+    head = head[(head["flags"] & IDLE) == 0]
+    mid = _snapshot(eng, head)
+    rest = eng.run(batch=256)
+    recs = np.concatenate([head, rest])
+    toks = eng.tokens(0, w.P + w.G)
+    end = _snapshot(eng, recs)
+    end["kv"] = {l: (eng.kv(l, "k"), eng.kv(l, "v")) for l in sorted({0, w.L // 2, w.L - 1})}
+    eng.close()
+    del eng
+    flat = si.weights_numpy_f32(T)
+    del T
+    torch.cuda.empty_cache()
+    return dict(w=w, W=si.nest_weights(flat, w), prompt=prompt, uni=uni, first=first, ref=ref,
+                recs=recs, toks=[int(x) for x in toks], mid=mid, end=end)
+
+
+def replay(run: dict):
+    """Integer replay of every cycle; returns the replay records."""
+    w, recs = run["w"], run["recs"]
+    pol = None
+    if w.mode == "greedy" and w.policy == "forced":
+        pol = ForcedPolicy(run["ref"], w.p_accept, run["uni"], w.V)
+    rp = Replay(w.n, w.L, w.P, run["first"], policy=pol, sample=(w.mode == "sample"))
+    out = []
+    for i, r in enumerate(recs):
+        ex = int(r["exit_pos"]) >= 0
+        q = rp.step(int(r["pdm_argmax"]), int(r["target_token"]) if ex else None,
+                    int(r["accepted"]) if ex else None)
+        for gf, of in INT_FIELDS:
+            assert int(r[gf]) == q[of], (i, gf, int(r[gf]), q[of])
+        assert list(map(int, r["kv_len"][: w.L])) == q["kv_len"], (i, "kv_len")
+        assert int(r["flags"]) == 0, (i, "flags", int(r["flags"]))
+        out.append(q)
+    return out, rp
+
+
+class OracleView:
+    """The oracle's target forward over the final sequence and the draft
+    module's KV over every position's full-depth feature."""
+
+    def __init__(self, run: dict):
+        w, W = run["w"], run["W"]
+        self.w = w
+        self.toks = run["toks"]
+        self.N = w.P + w.G - 1  # positions 0 .. P+G-2: every exiting position
+        self.tgt = Target(w, W)
+        H, self.taps = self.tgt.prefill_matrix(self.toks[: self.N], all_rows=True)
+        self.LG = self.tgt.logits_rows(H[w.P - 1:])
+        del H
+        self.pdm = PDM(w, W)
+        self.pdm.run_rows(self.pdm.feature_rows(self.taps, w.n), 0, matrix=True)
+
+    def logits_at(self, j: int) -> np.ndarray:
+        return self.LG[j - (self.w.P - 1)]
+
+    def survived(self, q: dict, upto: int = None) -> bool:
+        """All in-flight tokens of replay record q (at positions <= upto) are final."""
+        return all(p < self.N and self.toks[p] == tk for p, tk in q["inflight_tokens"]
+                   if upto is None or p <= upto)
+
+    def pdm_logits(self, q: dict) -> np.ndarray:
+        """Draft-module logits of the cycle of replay record q (rows row0..t)."""
+        w, pdm = self.w, self.pdm
+        row0, t = q["row0"], q["t"]
+        depths = schedule.depth_layout(q["a"], bool(q["pending_row"]), w.n)
+        G = np.stack([pdm.feature(self.taps[p], k) for p, k in zip(range(row0, t + 1), depths)])
+        saved = [(kv.K[row0:t + 1].copy(), kv.V[row0:t + 1].copy()) for kv in pdm.kv]
+        C0 = pdm.C
+        pdm.C = row0
+        try:
+            X = pdm.run_rows(G, row0, matrix=True)
+        finally:
+            pdm.C = C0
+            for kv, (K, V) in zip(pdm.kv, saved):
+                kv.K[row0:t + 1] = K
+                kv.V[row0:t + 1] = V
+        return pdm.logits(X[-1])
+
+
+def check_verifications(run: dict, view: OracleView, reps) -> Decisions:
+    """Greedy: the first token and the target token of every exit."""
+    w, recs = run["w"], run["recs"]
+    teacher = {("first", 0): run["first"]}
+    dec = Decisions(teacher, TOL[w.dtype])
+    dec.argmax(("first", 0), view.logits_at(w.P - 1))
+    for i, r in enumerate(recs):
+        if int(r["exit_pos"]) < 0:
+            continue
+        teacher[("y", i)] = int(r["target_token"])
+        dec.argmax(("y", i), view.logits_at(int(r["exit_pos"])))
+    return dec
+
+
+def sample_indices(cands, k: int):
+    cands = list(cands)
+    if len(cands) <= k:
+        return cands
+    return sorted({cands[int(round(x))] for x in np.linspace(0, len(cands) - 1, k)})
+
+
+def check_draft_module(run: dict, view: OracleView, reps, k: int = 32) -> Decisions:
+    """Greedy: the draft module's argmax at sampled cycles whose inputs survived."""
+    w, recs = run["w"], run["recs"]
+    cands = [i for i, q in enumerate(reps) if q["t"] < view.N and view.survived(q)]
+    assert len(cands) >= min(k, 8), len(cands)
+    teacher = {}
+    dec = Decisions(teacher, TOL[w.dtype])
+    for i in sample_indices(cands, k):
+        teacher[("pdm", i)] = int(recs[i]["pdm_argmax"])
+        dec.argmax(("pdm", i), view.pdm_logits(reps[i]))
+    dec.checked = len(sample_indices(cands, k))
+    return dec
+
+
+def check_sampling(run: dict, view: OracleView, reps, k: int = 32) -> Decisions:
+    """Sampling: the first token, and at sampled verifications the draft draw
+    from Q, the accept test u*Q(x) < P(x) and the residual redraw."""
+    w, recs, uni = run["w"], run["recs"], run["uni"]
+    T = w.temperature
+    teacher = {("first", 0): run["first"]}
+    dec = Decisions(teacher, TOL[w.dtype], STOL[w.dtype])
+    pw0, _ = sampling.softmax_weights(view.logits_at(w.P - 1), T)
+    dec.sample(("first", 0), pw0, float(uni[w.P, U_TARGET]))
+    exits = [i for i, q in enumerate(reps) if q["exit_pos"] >= 0]
+    chosen = sample_indices(exits, k)
+    for i in chosen:
+        q = reps[i]
+        j, c2 = q["exit_pos"], q["drafted_at"]
+        qd = reps[c2]
+        assert qd["t"] == j and view.survived(qd)
+        qw, qZ = sampling.softmax_weights(view.pdm_logits(qd), T)
+        teacher[("draft", c2)] = int(recs[c2]["pdm_argmax"])
+        dec.sample(("draft", c2), qw, float(uni[j + 1, U_DRAFT]))
+        pw, pZ = sampling.softmax_weights(view.logits_at(j), T)
+        teacher[("accept", i)] = bool(recs[i]["accepted"])
+        ok = dec.accept(("accept", i), pw, pZ, qw, qZ, qd["draft"], float(uni[j + 1, U_ACCEPT]))
+        if not ok:
+            teacher[("resample", i)] = int(recs[i]["target_token"])
+            dec.sample(("resample", i), sampling.residual(pw, pZ, qw, qZ), float(uni[j + 1, U_RESAMPLE]))
+    dec.checked = len(chosen)
+    return dec
+
+
+def check_floats(run: dict, view: OracleView, reps) -> dict:
+    """rel-L2 of the GPU's logits, draft logits, anchors and KV entries at the
+    two stopping points against the oracle's; returns the worst of each."""
+    w = run["w"]
+    worst = {"logits": 0.0, "pdm_logits": 0.0, "anchors": 0.0, "kv": 0.0}
+    seen = {k: 0 for k in worst}
+    for snap in (run["mid"], run["end"]):
+        if "logits" in snap:
+            j = reps[snap["exit_index"]]["exit_pos"]
+            worst["logits"] = max(worst["logits"], rel_l2(snap["logits"], view.logits_at(j)))
+            seen["logits"] += 1
+        q = reps[snap["index"]]
+        if q["t"] < view.N and view.survived(q):
+            worst["pdm_logits"] = max(worst["pdm_logits"], rel_l2(snap["pdm_logits"], view.pdm_logits(q)))
+            seen["pdm_logits"] += 1
+        t, a = q["t"], q["a"]
+        for i, p in enumerate(range(t, t - a, -1)):  # newest first; depth after the step = i + 1
+            if p >= view.N or not view.survived(q, upto=p):
+                continue
+            f = schedule.pattern(i + 1, w.anchors, w.L, w.n)
+            for b in range(f + 1):
+                worst["anchors"] = max(worst["anchors"], rel_l2(snap["anchors"][p][b], view.taps[p][b]))
+                seen["anchors"] += 1
+    kvlen = run["recs"][-1]["kv_len"]
+    for l, (K, V) in run["end"]["kv"].items():
+        m = min(int(kvlen[l]), view.N)
+        worst["kv"] = max(worst["kv"], rel_l2(K[:m], view.tgt.kv[l].K[:m]), rel_l2(V[:m], view.tgt.kv[l].V[:m]))
+        seen["kv"] += 1
+    worst["seen"] = seen
+    return worst

@@ -81,3 +81,13 @@ def test_anchor_constraints_are_checked():
     c.anchors[4] = 33
     with pytest.raises(A.SPDError):
         A.spd_workspace_bytes(c)
+
+
+def test_stage_count_limit():
+    """n_stages beyond SPD_MAX_STAGES is rejected even when it divides n_layers."""
+    c = make_config(si.workload("4b_n16"))
+    assert A.spd_workspace_bytes(c) > 0
+    c.n_stages, c.pdm_layers = 32, 1
+    with pytest.raises(A.SPDError) as e:
+        A.spd_workspace_bytes(c)
+    assert e.value.code == A.SPD_EINVAL

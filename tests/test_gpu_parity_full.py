@@ -1,0 +1,95 @@
+"""GPU parity at the full sizes of the four large workloads.
+
+4B-class n=8 (forced acceptance 0.8), 9B-class n=8 (0.7), 4B-class n=16
+(0.5, rollback stress) and 9B-class T=1 rejection sampling, each generated
+completely on the GPU in graph launch mode, as the benchmark times it.  The
+checks (tests/full_size.py) cover every integer of every cycle -- by integer
+replay, by comparing each verification with the oracle's forward over the
+final sequence, and the draft module at sampled cycles -- and the floating
+point state (logits, draft logits, anchors, KV entries) at two stopping
+points, to the same tolerances as the small workloads.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+from oracle import schedule
+from tests import full_size as fs
+
+pytestmark = pytest.mark.gpu
+
+WORKLOADS = ["4b_n8", "9b_n8", "4b_n16", "9b_sample"]
+PARTS = ["replay", "verifications", "draft_module_and_floats"]
+_C = {}
+
+
+def _get(name):
+    if _C.get("name") != name:
+        _C.clear()
+        gc.collect()
+        _C["name"] = name
+        _C["run"] = fs.gpu_run(name)
+    return _C
+
+
+def _reps(c):
+    if "reps" not in c:
+        c["reps"], _ = fs.replay(c["run"])
+    return c["reps"]
+
+
+def _view(c):
+    if "view" not in c:
+        c["view"] = fs.OracleView(c["run"])
+    return c["view"]
+
+
+def _assert_decisions(dec, n_checked, what):
+    print(f"{what}: {n_checked} checked, {len(dec.adopted)} near-ties adopted, {len(dec.mismatch)} mismatches")
+    assert not dec.mismatch, dec.mismatch[:5]
+    assert len(dec.adopted) <= max(2, n_checked // 50), dec.adopted[:10]
+
+
+@pytest.mark.parametrize("name,part", [(n, p) for n in WORKLOADS for p in PARTS])
+def test_full_size(name, part):
+    c = _get(name)
+    run = c["run"]
+    w, recs = run["w"], run["recs"]
+    if part == "replay":
+        reps = _reps(c)
+        ex = recs[recs["exit_pos"] >= 0]
+        R = int((ex["accepted"][: w.G - 2] == 0).sum())
+        print(f"{name}: {len(recs)} cycles, {len(ex)} verifications, {R} rejections")
+        assert len(ex) == w.G - 1
+        assert len(recs) == schedule.cycle_count(w.n, w.G, R)
+        assert (ex["accepted"] == 1).any() and (ex["accepted"] == 0).any()
+        # each exit verifies the next position: the output is the first token and the exits' tokens
+        assert [q["exit_pos"] for q in reps if q["exit_pos"] >= 0] == list(range(w.P, w.P + w.G - 1))
+        assert run["toks"][w.P:w.P + w.G] == [run["first"]] + [q["y"] for q in reps if q["exit_pos"] >= 0]
+        if w.mode == "greedy":
+            # lossless: the pipeline emits the target's own greedy continuation
+            assert run["toks"][w.P:w.P + w.G] == run["ref"][w.P:w.P + w.G]
+    elif part == "verifications":
+        reps = _reps(c)
+        view = _view(c)
+        if w.mode == "greedy":
+            dec = fs.check_verifications(run, view, reps)
+            _assert_decisions(dec, w.G, f"{name} target tokens")
+        else:
+            dec = fs.check_sampling(run, view, reps)
+            _assert_decisions(dec, dec.checked, f"{name} draws, accept tests and redraws")
+    else:
+        reps = _reps(c)
+        view = _view(c)
+        if w.mode == "greedy":
+            dec = fs.check_draft_module(run, view, reps)
+            _assert_decisions(dec, dec.checked, f"{name} draft-module predictions")
+        worst = fs.check_floats(run, view, reps)
+        print(f"{name} worst rel-L2: {worst}")
+        seen = worst.pop("seen")
+        assert seen["logits"] >= 1 and seen["anchors"] >= 1 and seen["kv"] >= 1, seen
+        for k, v in worst.items():
+            assert v <= fs.RTOL[w.dtype], (k, v)
+        if name == WORKLOADS[-1]:
+            _C.clear()

@@ -58,6 +58,9 @@ VARIANTS = {
     "mha_n4_long_prompt": dict(L=4, n=4, Hq=4, Hkv=4, anchors=[0, 1, 2, 3, 4], P=300, G=16, p=0.5, seed=35),
     "g5_gqa_bf16": dict(dtype="bf16", d=256, Hq=20, Hkv=4, hd=64, F=512, V=1000, L=4, n=4, Ls=1,
                         anchors=[0, 2, 3], P=40, G=20, p=0.8, seed=36),
+    # n = 16: up to 17 draft-module rows (two row tiles), all in one fusion pattern
+    "n16_one_anchor_bf16": dict(dtype="bf16", L=16, n=16, Ls=1, anchors=[0], G=40, p=0.7, seed=43),
+    "n16_one_anchor_f32": dict(dtype="f32", L=16, n=16, Ls=1, anchors=[0], G=40, p=0.7, seed=44),
 }
 
 
@@ -78,6 +81,62 @@ def test_variant_matches_oracle(name):
     # the acceptance structure is exercised
     acc = recs["accepted"]
     assert (acc == 1).any() and (acc == 0).any()
+
+
+# temperature sampling with rejection-sampling verification
+SAMPLE_VARIANTS = {
+    "f32_T1": dict(dtype="f32", temperature=1.0, seed=40),
+    "f32_T0.3": dict(dtype="f32", temperature=0.3, seed=40),
+    "bf16_n4_T0.3": dict(dtype="bf16", temperature=0.3, L=4, n=4, anchors=[0, 1, 2, 3, 4], G=30, seed=41),
+    "bf16_gqa_T0.5": dict(dtype="bf16", temperature=0.5, L=6, n=3, Hq=8, Hkv=2, F=768, V=500,
+                          anchors=[0, 2, 5], Ls=2, seed=42),
+}
+# a differing draw is a near-tie only if the threshold lies this close (as a
+# fraction of the total mass, or of Q(x) for the accept test) to its boundary
+STOL = {"f32": 1e-5, "bf16": 2e-4}
+
+
+@pytest.mark.parametrize("name", sorted(SAMPLE_VARIANTS))
+def test_sampling_matches_oracle(name):
+    """Draws from Q, accept tests u*Q(x) < P(x) and residual redraws from
+    max(0, P - Q) use the same seeded uniforms on both sides; every integer
+    of every cycle must agree."""
+    w = gpu_workload_tiny(mode="sample", **SAMPLE_VARIANTS[name])
+    T, W, prompt, uni = _inputs(w)
+    eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni)
+    eng.close()
+    o = SPDOracle(w, W, uniforms=uni, teacher=teacher_of(recs, first), tol=TOL[w.dtype],
+                  sample_tol=STOL[w.dtype])
+    otoks, ologs = o.run(prompt, w.G)
+    print(name, "adopted", o.dec.adopted)
+    assert not o.dec.mismatch, o.dec.mismatch
+    assert len(o.dec.adopted) <= 2, o.dec.adopted
+    assert toks == otoks
+    compare_logs(recs, ologs, w.L)
+    acc = recs["accepted"][recs["exit_pos"] >= 0]
+    assert (acc == 1).any() and (acc == 0).any()
+
+
+def test_eager_and_graph_launch_agree():
+    """Host-launched and graph-replayed cycles give bit-identical records and tokens."""
+    w = gpu_workload_tiny(dtype="bf16", L=4, n=4, anchors=[0, 1, 2, 3, 4], G=30, seed=45)
+    T, W, prompt, uni = _inputs(w)
+    ref, _ = ar_greedy(w, W, prompt, w.G)
+    from pipelined_draft_verify_amd import SPDEngine
+
+    eng = SPDEngine(w, {k: v.to("cuda:0") for k, v in T.items()})
+    eng.set_uniforms(uni)
+    eng.set_forced(ref, 0.6)
+    first = eng.prefill(prompt)
+    out = {}
+    for mode in (False, True, False):
+        eng.rollback(w.P, first)
+        eng.set_launch_mode(mode)
+        recs = eng.run(batch=16)
+        recs["cycle"] -= recs["cycle"][0]   # the record counter runs on across generations
+        out.setdefault(mode, []).append((recs.tobytes(), eng.tokens(0, w.P + w.G)))
+    eng.close()
+    assert out[False][0] == out[True][0] == out[False][1]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

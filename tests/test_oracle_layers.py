@@ -181,3 +181,47 @@ def test_ar_continue_matches_ar_greedy():
     o = SPDOracle(w, W)
     o.prefill(prompt, matrix=True)
     assert ar_continue(o, 7) == ref
+
+
+def test_matrix_forward_all_rows_and_logits_rows_equal_token_forward():
+    """The matrix forward over a whole sequence gives every position's final
+    hidden state, anchors and logits of the row-at-a-time forward."""
+    from oracle.model import Target
+    w = si.tiny(L=4, n=2, P=11, seed=19, dtype="bf16", norm_gain="random")
+    W = si.nest_weights(si.weights_numpy_f32(si.make_weights(w)), w)
+    toks = [int(t) for t in si.make_prompt(w)]
+    a, b = Target(w, W), Target(w, W)
+    rows, taps_a = [], []
+    for p, t in enumerate(toks):
+        h, tp = a.forward_token(t, p)
+        rows.append(h)
+        taps_a.append(tp)
+    H, taps_b = b.prefill_matrix(toks, all_rows=True)
+    np.testing.assert_allclose(H, np.stack(rows), rtol=1e-4, atol=1e-5)
+    for p in range(len(toks)):
+        for x, y in zip(taps_a[p], taps_b[p]):
+            np.testing.assert_allclose(x, y, rtol=1e-4, atol=1e-5)
+    LG = b.logits_rows(H)
+    for p in range(len(toks)):
+        np.testing.assert_allclose(LG[p], a.logits(rows[p]), rtol=1e-4, atol=1e-5)
+        assert int(np.argmax(LG[p])) == int(np.argmax(a.logits(rows[p])))
+
+
+def test_feature_rows_equals_feature():
+    from oracle.model import PDM
+    w = si.tiny(L=8, n=4, anchors=[0, 2, 5, 8], seed=20)
+    W = si.nest_weights(si.weights_numpy_f32(si.make_weights(w)), w)
+    pdm = PDM(w, W)
+    taps = [[rng.standard_normal(w.d).astype(np.float32) for _ in w.anchors] for _ in range(5)]
+    for k in range(w.n + 1):
+        a = np.stack([pdm.feature(t, k) for t in taps])
+        np.testing.assert_allclose(pdm.feature_rows(taps, k), a, rtol=1e-5, atol=1e-6)
+
+
+def test_rope_tables_equal_rope_cos_sin_exactly():
+    from oracle.layers import rope_tables
+    pos = np.arange(0, 5000, 7)
+    c, s_ = rope_tables(pos, 128, 10000.0)
+    for r, p in enumerate(pos):
+        cp, sp = Lr.rope_cos_sin(int(p), 128, 10000.0)
+        assert np.array_equal(c[r], cp) and np.array_equal(s_[r], sp), p
