@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--cpu-cycles", type=int, default=64)
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host in the timed region (no HIP graphs)")
+    ap.add_argument("--serialized", action="store_true",
+                    help="run the draft module on the stage stream ahead of the stage step (no overlap)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -135,7 +137,7 @@ def main():
         eng.sync()
 
     # timed region: graph launch mode, per-cycle HIP events for cycle times / bubble
-    eng.set_launch_mode(not args.eager)
+    eng.set_launch_mode(not args.eager, args.serialized)
     torch.cuda.synchronize()
     eng.timing(True)
     cyc_times = []
@@ -156,7 +158,7 @@ def main():
 
     # dominant-kernel timing: one more step, each gate/up launch bracketed by
     # HIP events on the stage stream (eager launch mode)
-    eng.set_launch_mode(False)
+    eng.set_launch_mode(False, args.serialized)
     eng.timing(True)
     eng.rollback(w.P, first)
     t_e = time.perf_counter()
@@ -165,7 +167,7 @@ def main():
     eager_s = time.perf_counter() - t_e
     _, _, gu_ms, gu_n = eng.timing_read(K_c)
     eng.timing(False)
-    eng.set_launch_mode(not args.eager)
+    eng.set_launch_mode(not args.eager, args.serialized)
     log(f"eager instrumented step: {eager_s * 1e3:.1f} ms")
     cycles = args.steps * K_c
     value = cycles / elapsed
@@ -206,7 +208,8 @@ def main():
                         f"Ls={w.Ls} anchors={w.anchors} prompt {w.P} gen {w.G} "
                         f"{w.mode} {w.policy}{' p=' + str(w.p_accept) if w.policy == 'forced' else ''}",
             "cycles_per_step": K_c,
-            "parallelism": "single GPU, two HIP streams",
+            "parallelism": "single GPU, " + ("one stream (draft module serialized)" if args.serialized
+                                             else "two HIP streams"),
             "launch": "eager" if args.eager else "hip graphs",
         },
         "tokens_per_s": round(tokens_per_s, 3),

@@ -207,10 +207,16 @@ SPD_API int spd_set_draft_policy(spd_t *h, int32_t policy, float p_accept, const
  * spd_cycle after the policy or uniforms changed) and replayed; a cycle then
  * costs one entry launch, two graph launches and four event calls on the
  * host.  SPD_LAUNCH_EAGER: every kernel is launched individually (needed for
- * the per-launch gate/up timing of spd_timing_*).  Waits for both streams.
- * Errors: SPD_EINVAL. */
+ * the per-launch gate/up timing of spd_timing_*).  Either may be or-ed with
+ * SPD_LAUNCH_SERIALIZED: the draft module is then enqueued on the stage
+ * stream ahead of the stage step instead of running beside it on the draft
+ * stream -- the same results (the draft module reads only the state from
+ * before the stage step, [RB] method step 4), no overlap; it measures each
+ * kernel alone and the draft module's marginal cost.  Waits for both
+ * streams.  Errors: SPD_EINVAL. */
 #define SPD_LAUNCH_EAGER 0
 #define SPD_LAUNCH_GRAPH 1
+#define SPD_LAUNCH_SERIALIZED 2
 SPD_API int spd_set_launch_mode(spd_t *h, int32_t mode);
 
 /* Per-position uniforms, device fp32 [n_positions][SPD_U_COUNT], values in

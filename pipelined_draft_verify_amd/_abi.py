@@ -145,7 +145,7 @@ def spd_set_draft_policy(h, policy, p_accept, ref_ptr, ref_len):
     return check("spd_set_draft_policy", lib().spd_set_draft_policy(h, policy, p_accept, c_void_p(ref_ptr), ref_len))
 
 
-SPD_LAUNCH_EAGER, SPD_LAUNCH_GRAPH = 0, 1
+SPD_LAUNCH_EAGER, SPD_LAUNCH_GRAPH, SPD_LAUNCH_SERIALIZED = 0, 1, 2
 
 
 def spd_set_launch_mode(h, mode):

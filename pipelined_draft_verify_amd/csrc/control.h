@@ -209,6 +209,12 @@ __global__ __launch_bounds__(kWG) void k_entry(Ctrl* C, const Geo g, int32_t* to
     }
   }
   __syncthreads();
+  // the record's per-layer lengths beyond L stay zero (the verification
+  // kernel fills the first L), so records never carry stale ring contents
+  {
+    spd_cycle_rec* r = ring + C->rec_slot;
+    for (int l = threadIdx.x; l < SPD_MAX_LAYERS; l += kWG) r->kv_len[l] = 0;
+  }
   if (!s_ok) return;
   const int slot = s_pos % g.nslots;
   const WT* e = embed + (size_t)s_tok * g.d;

@@ -169,6 +169,7 @@ struct spd_handle {
   // timing
   int timing = 0;
   int launch_mode = 1;  // 0: every kernel launched from the host; 1: per-stream graphs
+  int serialized = 0;   // the draft module runs on the stage stream before the stage step
   int graphs_valid = 0;
   hipGraphExec_t gx_stage = nullptr, gx_pdm = nullptr;
   std::vector<hipEvent_t> pool;
@@ -694,6 +695,9 @@ int enqueue_cycle(spd_t* h) {
   const Geo& g = h->g;
   hipStream_t ss = h->ss, ps = h->ps;
   const bool graph = h->launch_mode == 1;
+  // serialized: the draft module is enqueued on the stage stream ahead of the
+  // stage step (it reads only pre-step state, so the result is unchanged)
+  if (h->serialized) ps = ss;
   hipEvent_t e_start = nullptr, e_stage = nullptr, e_pdm_t = nullptr;
   if (h->timing) {
     e_start = pool_event(h);
@@ -707,8 +711,10 @@ int enqueue_cycle(spd_t* h) {
   hipLaunchKernelGGL((k_entry<WT>), dim3(1), dim3(kWG), 0, ss, h->ctrl, g, h->tokens, (const WT*)h->w.embed,
                      h->hslots, h->anchors, h->ring, h->lay.log_cap);
   // fork
-  HIPCHK(h, hipEventRecord(h->ev_entry, ss));
-  HIPCHK(h, hipStreamWaitEvent(ps, h->ev_entry, 0));
+  if (ps != ss) {
+    HIPCHK(h, hipEventRecord(h->ev_entry, ss));
+    HIPCHK(h, hipStreamWaitEvent(ps, h->ev_entry, 0));
+  }
   int r = graph ? (hipGraphLaunch(h->gx_pdm, ps) == hipSuccess ? SPD_OK : SPD_EHIP) : pdm_chain<WT>(h, ps);
   if (r) return r;
   if (e_pdm_t) HIPCHK(h, hipEventRecord(e_pdm_t, ps));
@@ -963,10 +969,13 @@ int spd_set_draft_policy(spd_t* h, int32_t policy, float p_accept, const int32_t
 }
 
 int spd_set_launch_mode(spd_t* h, int32_t mode) {
-  if (!h || (mode != SPD_LAUNCH_EAGER && mode != SPD_LAUNCH_GRAPH)) return SPD_EINVAL;
+  if (!h) return SPD_EINVAL;
+  const int base = mode & ~SPD_LAUNCH_SERIALIZED;
+  if (base != SPD_LAUNCH_EAGER && base != SPD_LAUNCH_GRAPH) return SPD_EINVAL;
   HIPCHK(h, hipStreamSynchronize(h->ss));
   HIPCHK(h, hipStreamSynchronize(h->ps));
-  h->launch_mode = mode;
+  h->launch_mode = base;
+  h->serialized = (mode & SPD_LAUNCH_SERIALIZED) ? 1 : 0;
   return SPD_OK;
 }
 

@@ -96,8 +96,11 @@ class SPDEngine:
         self.ref = t
         A.spd_set_draft_policy(self.h, A.SPD_DRAFT_FORCED, float(p_accept), t.data_ptr(), t.numel())
 
-    def set_launch_mode(self, graph: bool) -> None:
-        A.spd_set_launch_mode(self.h, A.SPD_LAUNCH_GRAPH if graph else A.SPD_LAUNCH_EAGER)
+    def set_launch_mode(self, graph: bool, serialized: bool = False) -> None:
+        mode = A.SPD_LAUNCH_GRAPH if graph else A.SPD_LAUNCH_EAGER
+        if serialized:
+            mode |= A.SPD_LAUNCH_SERIALIZED
+        A.spd_set_launch_mode(self.h, mode)
 
     def set_natural(self) -> None:
         A.spd_set_draft_policy(self.h, A.SPD_DRAFT_NATURAL, 0.0, 0, 0)
