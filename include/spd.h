@@ -107,7 +107,7 @@ extern "C" {
  * up to n_stages + 1 rows); pdm_layers <= n_layers / n_stages; anchors strictly
  * increasing with anchors[0] == 0 and anchors[n_anchors-1] <= n_layers;
  * n_heads % n_kv_heads == 0; head_dim in {64, 128}; d_model, d_ffn and
- * n_heads*head_dim multiples of 256.
+ * n_heads*head_dim multiples of 256; max_ctx <= 32768.
  */
 typedef struct spd_config {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab;

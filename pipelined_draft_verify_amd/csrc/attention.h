@@ -21,7 +21,8 @@
 namespace spd {
 
 enum PMode { PM_STAGE = 0, PM_ROWS = 1 };
-constexpr int kAttnQ = 8;  // query vectors per workgroup
+constexpr int kAttnQ = 8;      // query vectors per workgroup
+constexpr int kMaxSplit = 128;  // splits of kSplit positions per context (max_ctx <= 32768)
 
 struct Attn {
   int pmode;
@@ -86,18 +87,31 @@ __device__ __forceinline__ void unpack8<float>(const u32x4* r, float* o) {
   o[6] = __uint_as_float(r[1].z); o[7] = __uint_as_float(r[1].w);
 }
 
+// Relaxed agent-scope load: a value another workgroup published before the
+// arrival counter said so (the merge reads the other splits' partials).
+__device__ __forceinline__ float load_published(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename KT, int HD>
 __device__ __forceinline__ void attn_body(const Attn& A, int pos0, int nrows, int layer) {
-  __shared__ float qs[kAttnQ][HD];
+  __shared__ __align__(16) float qs[kAttnQ][HD];
   __shared__ float ps[kAttnQ][kSplit];
   __shared__ float rmax[kWG / kWave][kAttnQ];
   __shared__ float rsum[kWG / kWave][kAttnQ];
   __shared__ float racc[kWG / kWave][kAttnQ][HD];
+  __shared__ float sml[kAttnQ][kMaxSplit][2];
   __shared__ int last;
   constexpr int NC = HD / 8;        // 8-element chunks per row
   constexpr int DL = HD / 8;        // lanes per value row
   constexpr int PG = kWave / DL;    // positions per wave instruction
   constexpr int NPG = PG * (kWG / kWave);
+  constexpr int NI = kSplit / NPG;  // value rows per thread
+  constexpr int VPC = sizeof(KT) * 8 / 16;  // 16-byte vectors per 8-element chunk
+  // bf16: every key and value vector of the split is requested before any
+  // arithmetic (one memory round trip); fp32: values after the scores
+  constexpr bool kPrefetchV = sizeof(KT) == 2;
+  constexpr int NVR = kPrefetchV ? NI * VPC : 1;
   const Geo& g = A.g;
   const int G = g.Hq / g.Hkv;
   const int kvh = blockIdx.y % g.Hkv;
@@ -113,45 +127,83 @@ __device__ __forceinline__ void attn_body(const Attn& A, int pos0, int nrows, in
   const int prow0 = (A.pmode == PM_STAGE) ? blockIdx.z : r0;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-
-  for (int idx = threadIdx.x; idx < nq * HD; idx += kWG) {
-    const int qi = idx / HD, dim = idx - qi * HD;
-    const int r = qi / G, head = kvh * G + (qi - r * G);
-    qs[qi][dim] = A.q[(size_t)(prow0 + r) * g.Hq * HD + (size_t)head * HD + dim];
-  }
-  __syncthreads();
-
-  // ---- scores ----
-  const int pos = s0 + threadIdx.x;
+  const int dl = lane % DL, pg = lane / DL;
+  const int gp = wave * PG + pg;
   const KT* K = reinterpret_cast<const KT*>(A.kc);
-  float s[kAttnQ];
+  const KT* Vc = reinterpret_cast<const KT*>(A.vc);
+
+  // ---- loads: queries first (needed first), then keys, then values ----
+  constexpr int QPT = (kAttnQ * HD + kWG - 1) / kWG;
+  float qv[QPT];
 #pragma unroll
-  for (int qi = 0; qi < kAttnQ; ++qi) s[qi] = 0.f;
-  if (pos <= maxpos) {
-    // up to 16 x 16-byte vectors of the key in flight per batch
-    constexpr int VPC = sizeof(KT) * 8 / 16;           // vectors per 8-element chunk
-    constexpr int CB = (NC * VPC <= 16) ? NC : 16 / VPC;  // chunks per batch
+  for (int u = 0; u < QPT; ++u) {
+    const int idx = threadIdx.x + u * kWG;
+    qv[u] = 0.f;
+    if (idx < nq * HD) {
+      const int qi = idx / HD, dim = idx - qi * HD;
+      const int r = qi / G, head = kvh * G + (qi - r * G);
+      qv[u] = A.q[(size_t)(prow0 + r) * g.Hq * HD + (size_t)head * HD + dim];
+    }
+  }
+  const int pos = s0 + threadIdx.x;
+  const bool have_key = pos <= maxpos;
+  u32x4 rk[NC * VPC];
+  if (have_key) {
     const size_t kbase = k_index(g, layer, kvh, pos, 0);
     const size_t cstride = (size_t)g.ctx_cap * 8;
 #pragma unroll
-    for (int cb = 0; cb < NC; cb += CB) {
-      u32x4 raw[CB * VPC];
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
+      for (int h = 0; h < VPC; ++h)
+        rk[c * VPC + h] = *reinterpret_cast<const u32x4*>(K + kbase + c * cstride + h * 4);
+  }
+  u32x4 rv[NVR];
+  if (kPrefetchV) {
 #pragma unroll
-        for (int h = 0; h < VPC; ++h)
-          raw[c * VPC + h] = *reinterpret_cast<const u32x4*>(K + kbase + (cb + c) * cstride + h * 4);
+    for (int i = 0; i < NI; ++i) {
+      const int jj = gp + i * NPG;
+#pragma unroll
+      for (int h = 0; h < VPC; ++h) {
+        if (s0 + jj <= maxpos)
+          rv[i * VPC + h] = *reinterpret_cast<const u32x4*>(Vc + v_index(g, layer, kvh, s0 + jj, dl * 8) + h * 4);
+        else
+          rv[i * VPC + h] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int idx = threadIdx.x + u * kWG;
+    if (idx < kAttnQ * HD) qs[idx / HD][idx % HD] = qv[u];
+  }
+  __syncthreads();
+
+  // ---- scores: thread j owns position s0 + j ----
+  // chunk-major: the queries' independent FMA chains interleave and each
+  // query chunk is one broadcast 16-byte LDS read; per query the order is
+  // still dims 0..HD-1
+  float s[kAttnQ];
+#pragma unroll
+  for (int qi = 0; qi < kAttnQ; ++qi) s[qi] = 0.f;
+  if (have_key) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float kf[8];
+      unpack8<KT>(&rk[c * VPC], kf);
 #pragma unroll
       for (int qi = 0; qi < kAttnQ; ++qi) {
         if (qi < nq) {
+          const f32x4 qa = *reinterpret_cast<const f32x4*>(&qs[qi][c * 8]);
+          const f32x4 qb = *reinterpret_cast<const f32x4*>(&qs[qi][c * 8 + 4]);
           float acc = s[qi];
-#pragma unroll
-          for (int c = 0; c < CB; ++c) {
-            float kf[8];
-            unpack8<KT>(&raw[c * VPC], kf);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf(qs[qi][(cb + c) * 8 + e], kf[e], acc);
-          }
+          acc = fmaf(qa.x, kf[0], acc);
+          acc = fmaf(qa.y, kf[1], acc);
+          acc = fmaf(qa.z, kf[2], acc);
+          acc = fmaf(qa.w, kf[3], acc);
+          acc = fmaf(qb.x, kf[4], acc);
+          acc = fmaf(qb.y, kf[5], acc);
+          acc = fmaf(qb.z, kf[6], acc);
+          acc = fmaf(qb.w, kf[7], acc);
           s[qi] = acc;
         }
       }
@@ -191,30 +243,29 @@ __device__ __forceinline__ void attn_body(const Attn& A, int pos0, int nrows, in
   }
   __syncthreads();
 
-  // ---- weighted values ----
-  const KT* Vc = reinterpret_cast<const KT*>(A.vc);
-  const int dl = lane % DL, pg = lane / DL;
-  const int gp = wave * PG + pg;
+  // ---- weighted values: lanes (dl, pg) hold dims dl*8.. of rows gp + i*NPG ----
   float acc[kAttnQ][8];
 #pragma unroll
   for (int qi = 0; qi < kAttnQ; ++qi)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[qi][e] = 0.f;
-  constexpr int NI = kSplit / NPG;  // positions per thread
-  constexpr int VPC = sizeof(KT) * 8 / 16;
-  constexpr int IB = 4;             // positions per batch of loads
+  constexpr int IB = kPrefetchV ? NI : 4;  // value rows per batch of loads
 #pragma unroll
   for (int ib = 0; ib < NI; ib += IB) {
     u32x4 raw[IB * VPC];
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
-      const int jj = gp + (ib + i) * NPG;
 #pragma unroll
       for (int h = 0; h < VPC; ++h) {
-        if (s0 + jj <= maxpos)
-          raw[i * VPC + h] = *reinterpret_cast<const u32x4*>(Vc + v_index(g, layer, kvh, s0 + jj, dl * 8) + h * 4);
-        else
-          raw[i * VPC + h] = u32x4{0u, 0u, 0u, 0u};
+        if (kPrefetchV) {
+          raw[i * VPC + h] = rv[(ib + i) * VPC + h];
+        } else {
+          const int jj = gp + (ib + i) * NPG;
+          if (s0 + jj <= maxpos)
+            raw[i * VPC + h] = *reinterpret_cast<const u32x4*>(Vc + v_index(g, layer, kvh, s0 + jj, dl * 8) + h * 4);
+          else
+            raw[i * VPC + h] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
 #pragma unroll
@@ -274,26 +325,43 @@ __device__ __forceinline__ void attn_body(const Attn& A, int pos0, int nrows, in
   __syncthreads();
   if (!last) return;
   __threadfence();
+  // every split's (max, sum) of every query, fetched in parallel
+  for (int idx = threadIdx.x; idx < nq * nsp; idx += kWG) {
+    const int qi = idx / nsp, sp = idx - qi * nsp;
+    const int r = qi / G, head = kvh * G + (qi - r * G);
+    const size_t b = ((size_t)(prow0 + r) * g.Hq + head) * g.nsplit + sp;
+    sml[qi][sp][0] = load_published(A.pml + b * 2);
+    sml[qi][sp][1] = load_published(A.pml + b * 2 + 1);
+  }
+  __syncthreads();
   for (int idx = threadIdx.x; idx < nq * HD; idx += kWG) {
     const int qi = idx / HD, dim = idx - qi * HD;
     const int r = qi / G, head = kvh * G + (qi - r * G);
     const int ns = (pos0 + r0 + r) / kSplit + 1;  // splits covering this row
     const size_t base = ((size_t)(prow0 + r) * g.Hq + head) * g.nsplit;
-    const volatile float* pml = A.pml;
-    const volatile float* pacc = A.pacc;
     float M = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, pml[(base + sp) * 2]);
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, sml[qi][sp][0]);
     float num = 0.f, den = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
-      const float w = expf(pml[(base + sp) * 2] - M);
-      num = fmaf(w, pacc[(base + sp) * HD + dim], num);
-      den = fmaf(w, pml[(base + sp) * 2 + 1], den);
+    constexpr int MB = 8;  // partial rows fetched per batch
+    for (int sb = 0; sb < ns; sb += MB) {
+      float pv[MB];
+#pragma unroll
+      for (int u = 0; u < MB; ++u) pv[u] = (sb + u < ns) ? load_published(A.pacc + (base + sb + u) * HD + dim) : 0.f;
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        if (sb + u < ns) {
+          const float w = expf(sml[qi][sb + u][0] - M);
+          num = fmaf(w, pv[u], num);
+          den = fmaf(w, sml[qi][sb + u][1], den);
+        }
+      }
     }
     const float ov = num / den;
     const size_t oi = (size_t)(prow0 + r) * g.Hq * HD + (size_t)head * HD + dim;
     if (A.oh) {
-      A.oh[oi] = f32_to_bf16_rne(ov);
-      A.ol[oi] = f32_to_bf16_rne(ov - bf16_bits_to_f32(A.oh[oi]));
+      const uint16_t hi = f32_to_bf16_rne(ov);
+      A.oh[oi] = hi;
+      A.ol[oi] = f32_to_bf16_rne(ov - bf16_bits_to_f32(hi));
     } else {
       A.o[oi] = ov;
     }

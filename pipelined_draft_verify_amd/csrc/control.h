@@ -389,10 +389,12 @@ __global__ __launch_bounds__(kCtlThreads) void k_pdm_finalize(const FinalizeArgs
 }
 
 // ---- prefill / autoregressive helpers --------------------------------------
-// X[r] = embed[tokens[pos0 + r]] for r < M; optional anchor-0 taps [r][m][d].
+// X[r] = embed[tokens[pos0 + r]] for r < M; optional anchor-0 taps [r][m][d]
+// and per-row partial sums of squares over 64-column groups [r][d/64] (the
+// fused-norm input of the matrix-core path).
 template <typename WT>
 __global__ __launch_bounds__(kWG) void k_embed_rows(const int32_t* tokens, int pos0, const WT* embed, int d,
-                                                    float* X, float* taps, int m) {
+                                                    float* X, float* taps, int m, float* ssq) {
   const int r = blockIdx.x;
   const int tok = tokens[pos0 + r];
   const WT* e = embed + (size_t)tok * d;
@@ -400,6 +402,14 @@ __global__ __launch_bounds__(kWG) void k_embed_rows(const int32_t* tokens, int p
     const float v = from_store(e[i]);
     X[(size_t)r * d + i] = v;
     if (taps) taps[((size_t)r * m + 0) * d + i] = v;
+  }
+  if (ssq) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    for (int cg = wave; cg < d / kWave; cg += kWG / kWave) {
+      const float v = from_store(e[cg * kWave + lane]);
+      const float sq = wave_sum(v * v);
+      if (lane == 0) ssq[(size_t)r * (d / kWave) + cg] = sq;
+    }
   }
 }
 

@@ -39,7 +39,7 @@ struct Layout {
   size_t s_q, s_pacc, s_pml, s_o, s_act;
   size_t Xt, Xp, r_q, r_pacc, r_pml, r_o, r_act, taps;
   size_t logits, plogits, pw, parts, pparts, ring;
-  size_t cnt_s, cnt_r, xh, xl, ah, al;
+  size_t cnt_s, cnt_r, ssq_t, ssq_p, mpart;
   size_t total;
   int ctx_cap, nsplit, mr, log_cap, nparts_max;
 };
@@ -66,8 +66,33 @@ bool valid_config(const spd_config* c) {
   if (c->mode != SPD_MODE_GREEDY && c->mode != SPD_MODE_SAMPLE) return false;
   if (c->mode == SPD_MODE_SAMPLE && !(c->temperature > 0.f)) return false;
   if (c->max_new < 1 || c->max_ctx < c->n_stages + 2) return false;
+  if (align_up((size_t)c->max_ctx, kSplit) / kSplit > (size_t)kMaxSplit) return false;
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 1.f)) return false;
   return true;
+}
+
+// K ranges of one matrix-core product (N weight rows, K inputs): the divisor
+// of K / kMKC that gives closest to ~640 workgroups in total.
+int mfma_splits(int N, int K) {
+  const int groups = N / kMGroup;
+  const int chunks = K / kMKC;
+  const int target = (640 + groups - 1) / groups;
+  int best = 1;
+  for (int s = 1; s <= std::min(chunks, kMMaxSplit); ++s) {
+    if (chunks % s) continue;
+    if (std::abs(s - target) < std::abs(best - target)) best = s;
+  }
+  return best;
+}
+
+// Partial-tile floats a product set needs (0 when no K is split).
+size_t mfma_part_floats(int N, const int* Ks, int nprob, int rows) {
+  size_t slabs = 0;
+  for (int p = 0; p < nprob; ++p) {
+    const int S = mfma_splits(N, Ks[p]);
+    if (S > 1) slabs += S;
+  }
+  return slabs * rows * (size_t)N;
 }
 
 Layout make_layout(const spd_config* c) {
@@ -125,11 +150,25 @@ Layout make_layout(const spd_config* c) {
   L.ring = take(sizeof(spd_cycle_rec) * (size_t)L.log_cap);
   L.cnt_s = take(sizeof(int32_t) * (size_t)n * Hkv);
   L.cnt_r = take(sizeof(int32_t) * (size_t)L.mr * Hkv);
-  const size_t xk = (size_t)std::max(d, Hq * hd);
-  L.xh = take(sizeof(uint16_t) * L.mr * xk);
-  L.xl = take(sizeof(uint16_t) * L.mr * xk);
-  L.ah = take(sizeof(uint16_t) * L.mr * (size_t)F);
-  L.al = take(sizeof(uint16_t) * L.mr * (size_t)F);
+  // matrix-core path (bf16): per-row partial sums of squares of the prefill
+  // rows and the draft-module rows, and the split-K partial tiles
+  L.ssq_t = take(sizeof(float) * L.mr * (size_t)(d / kSsqCols));
+  L.ssq_p = take(sizeof(float) * L.mr * (size_t)(d / kSsqCols));
+  size_t pf = 0;
+  if (c->dtype == SPD_DTYPE_BF16) {
+    const int rows = L.mr;  // 16 * MT of the largest pass
+    const int qk[1] = {(int)qd}, dd[1] = {d}, ff[1] = {F};
+    pf = std::max(pf, mfma_part_floats((Hq + 2 * Hkv) * hd, dd, 1, rows));
+    pf = std::max(pf, mfma_part_floats(d, qk, 1, rows));
+    pf = std::max(pf, mfma_part_floats(2 * F, dd, 1, rows));
+    pf = std::max(pf, mfma_part_floats(d, ff, 1, rows));
+    int fk[SPD_MAX_ANCHORS];
+    for (int f = 0; f < m; ++f) fk[f] = (f + 1) * d;
+    pf = std::max(pf, mfma_part_floats(d, fk, m, rows));
+    const int full[1] = {m * d};
+    pf = std::max(pf, mfma_part_floats(d, full, 1, rows));
+  }
+  L.mpart = take(sizeof(float) * std::max<size_t>(pf, 1));
   L.total = off;
   return L;
 }
@@ -156,7 +195,7 @@ struct spd_handle {
   ArgPair *parts, *pparts;
   spd_cycle_rec* ring;
   int32_t *cnt_s, *cnt_r;
-  uint16_t *xh, *xl, *ah, *al;
+  float *ssq_t, *ssq_p, *mpart;
   int policy = SPD_DRAFT_NATURAL;
   float p_accept = 0.f;
   const int32_t* ref = nullptr;
@@ -247,11 +286,10 @@ RowsGemv rows_base(spd_t* h) {
 }
 
 // Attention over row-batched queries (prefill chunk, AR token or the draft
-// module's trailing rows) with the split merge fused; output fp32 o or, for
-// the matrix-core path, its bf16 hi/lo split.
+// module's trailing rows) with the split merge fused; output fp32 rows r_o.
 template <typename WT>
 void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, int from_ctrl, int max_rows,
-                    bool split_out, hipStream_t s) {
+                    hipStream_t s) {
   const Geo& g = h->g;
   Attn t;
   memset(&t, 0, sizeof(t));
@@ -263,10 +301,6 @@ void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, in
   t.pacc = h->r_pacc;
   t.pml = h->r_pml;
   t.o = h->r_o;
-  if (split_out) {
-    t.oh = h->xh;
-    t.ol = h->xl;
-  }
   t.counters = h->cnt_r;
   t.from_ctrl = from_ctrl;
   t.pos0_arg = pos0;
@@ -310,7 +344,7 @@ void rows_layer(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int l
   a.vc = vc;
   a.kv_len = kv_len;
   launch_rows<WT, EPI_QKV>(h, a, max_rows, s);
-  rows_attention<WT>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, false, s);
+  rows_attention<WT>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, s);
   // output projection + residual
   a = rows_base(h);
   a.from_ctrl = from_ctrl;
@@ -351,83 +385,122 @@ void rows_layer(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int l
   launch_rows<WT, EPI_RESID>(h, a, max_rows, s);
 }
 
+MfmaArgs mfma_base(spd_t* h) {
+  MfmaArgs a;
+  memset(&a, 0, sizeof(a));
+  a.anchor_idx = -1;
+  a.rmode = RM_CONTIG;
+  a.ctrl = h->ctrl;
+  a.g = h->g;
+  a.rcos = h->rcos;
+  a.rsin = h->rsin;
+  a.part = h->mpart;
+  return a;
+}
+
+// One matrix-core product set (nprob products of N rows): the GEMV, then the
+// split-K reduction + epilogue if any product's K is split.
 template <int EPI>
-void launch_mfma(const MfmaGemv& a, int tiles, int max_rows, hipStream_t s) {
-  if (max_rows <= 16)
-    hipLaunchKernelGGL((k_gemv_mfma<EPI, 1>), dim3(tiles), dim3(kWG), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_gemv_mfma<EPI, 2>), dim3(tiles), dim3(kWG), 0, s, a);
+void launch_mfma(spd_t* h, MfmaArgs a, int nprob, int max_rows, hipStream_t s) {
+  int smax = 1, off = 0;
+  bool split = false;
+  for (int p = 0; p < nprob; ++p) {
+    a.S[p] = mfma_splits(a.N, a.K[p]);
+    a.poff[p] = off;
+    if (a.S[p] > 1) {
+      off += a.S[p];
+      split = true;
+    }
+    smax = std::max(smax, a.S[p]);
+  }
+  const dim3 grid(a.N / kMGroup, smax, nprob);
+  if (max_rows <= 16) {
+    hipLaunchKernelGGL((k_mfma_gemv<EPI, 1>), grid, dim3(kWG), 0, s, a);
+    if (split)
+      hipLaunchKernelGGL((k_mfma_reduce<EPI, 1>), dim3(a.N / kMGroup, 16, nprob), dim3(kWave), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_mfma_gemv<EPI, 2>), grid, dim3(kWG), 0, s, a);
+    if (split)
+      hipLaunchKernelGGL((k_mfma_reduce<EPI, 2>), dim3(a.N / kMGroup, 32, nprob), dim3(kWave), 0, s, a);
+  }
 }
 
 // The same layer on the matrix cores (bf16 weights): the draft module's
-// trailing rows and prefill chunks.
-void rows_layer_mfma(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int layer, float* X, int M,
-                     int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s) {
+// trailing rows and prefill chunks.  X rows are updated in place; ssqX holds
+// their per-row partial sums of squares (written by whoever wrote X).
+void rows_layer_mfma(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int layer, float* X, float* ssqX,
+                     int M, int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s) {
   const Geo& g = h->g;
   const int max_rows = from_ctrl ? g.n + 1 : M;
   const int qd = g.Hq * g.hd;
-  MfmaGemv a;
-  memset(&a, 0, sizeof(a));
+  MfmaArgs a = mfma_base(h);
   a.M_arg = M;
   a.pos0_arg = pos0;
   a.from_ctrl = from_ctrl;
-  a.ctrl = h->ctrl;
-  a.g = g;
-  a.rcos = h->rcos;
-  a.rsin = h->rsin;
-  a.anchor_idx = -1;
-  // norm + split, q/k/v + RoPE + cache append
-  hipLaunchKernelGGL(k_split_rows, dim3(max_rows), dim3(kWG), 0, s, X, g.d, M, from_ctrl, g.d,
-                     (const float*)lw.attn_norm, g.eps, h->xh, h->xl, h->ctrl);
-  a.W = (const uint16_t*)lw.w_qkv;
+  // norm + q/k/v + RoPE + cache append
+  a.W[0] = (const uint16_t*)lw.w_qkv;
+  a.K[0] = g.d;
   a.N = g.qkv_rows;
-  a.K = g.d;
-  a.xh = h->xh;
-  a.xl = h->xl;
+  a.x = X;
+  a.ldx = g.d;
+  a.gamma = (const float*)lw.attn_norm;
+  a.ssq = ssqX;
+  a.ssq_parts = g.d / kSsqCols;
   a.out = h->r_q;
   a.ldo = qd;
   a.layer = layer;
   a.kc = kc;
   a.vc = vc;
   a.kv_len = kv_len;
-  launch_mfma<EPI_QKV>(a, g.qkv_rows / 16, max_rows, s);
-  // attention, output split for the next product
-  rows_attention<uint16_t>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, true, s);
+  launch_mfma<EPI_QKV>(h, a, 1, max_rows, s);
+  rows_attention<uint16_t>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, s);
   // output projection + residual
-  a.W = (const uint16_t*)lw.w_o;
-  a.N = g.d;
-  a.K = qd;
-  a.out = X;
-  a.ldo = g.d;
   a.kv_len = nullptr;
-  launch_mfma<EPI_RESID>(a, g.d / 16, max_rows, s);
-  // norm + split, gate/up + SwiGLU (activation written split)
-  hipLaunchKernelGGL(k_split_rows, dim3(max_rows), dim3(kWG), 0, s, X, g.d, M, from_ctrl, g.d,
-                     (const float*)lw.ffn_norm, g.eps, h->xh, h->xl, h->ctrl);
-  a.W = (const uint16_t*)lw.w_gu;
-  a.N = 2 * g.F;
-  a.K = g.d;
-  a.oh = h->ah;
-  a.ol = h->al;
-  launch_mfma<EPI_SWIGLU>(a, g.F / 8, max_rows, s);
-  // down + residual (+ anchor taps)
-  a.W = (const uint16_t*)lw.w_down;
+  a.W[0] = (const uint16_t*)lw.w_o;
+  a.K[0] = qd;
   a.N = g.d;
-  a.K = g.F;
-  a.xh = h->ah;
-  a.xl = h->al;
+  a.x = h->r_o;
+  a.ldx = qd;
+  a.gamma = nullptr;
+  a.ssq = nullptr;
   a.out = X;
   a.ldo = g.d;
+  a.ssq_out = ssqX;
+  launch_mfma<EPI_RESID>(h, a, 1, max_rows, s);
+  // norm + gate/up + SwiGLU
+  a.W[0] = (const uint16_t*)lw.w_gu;
+  a.K[0] = g.d;
+  a.N = 2 * g.F;
+  a.x = X;
+  a.ldx = g.d;
+  a.gamma = (const float*)lw.ffn_norm;
+  a.ssq = ssqX;
+  a.out = h->r_act;
+  a.ldo = g.F;
+  a.ssq_out = nullptr;
+  launch_mfma<EPI_SWIGLU>(h, a, 1, max_rows, s);
+  // down + residual (+ anchor taps)
+  a.W[0] = (const uint16_t*)lw.w_down;
+  a.K[0] = g.F;
+  a.N = g.d;
+  a.x = h->r_act;
+  a.ldx = g.F;
+  a.gamma = nullptr;
+  a.ssq = nullptr;
+  a.out = X;
+  a.ldo = g.d;
+  a.ssq_out = ssqX;
   a.anchors = taps;
   a.anchor_idx = anchor_idx;
-  launch_mfma<EPI_RESID>(a, g.d / 16, max_rows, s);
+  launch_mfma<EPI_RESID>(h, a, 1, max_rows, s);
 }
 
 template <typename WT>
 void layer_rows_any(spd_t* h, bool mfma, const spd_layer_weights& lw, void* kc, void* vc, int layer, float* X,
-                    int M, int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s) {
+                    float* ssqX, int M, int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx,
+                    hipStream_t s) {
   if (mfma && sizeof(WT) == 2)
-    rows_layer_mfma(h, lw, kc, vc, layer, X, M, pos0, from_ctrl, kv_len, taps, anchor_idx, s);
+    rows_layer_mfma(h, lw, kc, vc, layer, X, ssqX, M, pos0, from_ctrl, kv_len, taps, anchor_idx, s);
   else
     rows_layer<WT>(h, lw, kc, vc, layer, X, M, pos0, from_ctrl, kv_len, taps, anchor_idx, s);
 }
@@ -460,22 +533,40 @@ int pdm_chain(spd_t* h, hipStream_t ps) {
   const spd_weights& w = h->w;
   // ---------------- draft module (pre-step) on the draft stream ----------------
   {
-    RowsGemv a = rows_base(h);
-    a.rmode = RM_FC;
-    a.from_ctrl = 1;
-    a.n_groups = g.m;
-    for (int f = 0; f < g.m; ++f) {
-      a.W[f] = w.fc[f];
-      a.Kg[f] = (f + 1) * g.d;
+    // anchor gather + concat + FC: one product per fusion pattern f, over the
+    // trailing rows whose depth uses it
+    if (sizeof(WT) == 2) {
+      MfmaArgs a = mfma_base(h);
+      a.rmode = RM_FC;
+      a.from_ctrl = 1;
+      for (int f = 0; f < g.m; ++f) {
+        a.W[f] = (const uint16_t*)w.fc[f];
+        a.K[f] = (f + 1) * g.d;
+      }
+      a.N = g.d;
+      a.slot_anchors = h->anchors;
+      a.out = h->Xp;
+      a.ldo = g.d;
+      a.ssq_out = h->ssq_p;
+      launch_mfma<EPI_STORE>(h, a, g.m, g.n + 1, ps);
+    } else {
+      RowsGemv a = rows_base(h);
+      a.rmode = RM_FC;
+      a.from_ctrl = 1;
+      a.n_groups = g.m;
+      for (int f = 0; f < g.m; ++f) {
+        a.W[f] = w.fc[f];
+        a.Kg[f] = (f + 1) * g.d;
+      }
+      a.N = g.d;
+      a.units = g.d;
+      a.out = h->Xp;
+      a.ldo = g.d;
+      a.slot_anchors = h->anchors;
+      launch_rows<WT, EPI_STORE>(h, a, g.n + 1, ps);
     }
-    a.N = g.d;
-    a.units = g.d;
-    a.out = h->Xp;
-    a.ldo = g.d;
-    a.slot_anchors = h->anchors;
-    launch_rows<WT, EPI_STORE>(h, a, g.n + 1, ps);
     for (int l = 0; l < g.Ls; ++l)
-      layer_rows_any<WT>(h, true, w.pdm[l], h->pkc, h->pvc, l, h->Xp, 0, 0, 1, nullptr, nullptr, -1, ps);
+      layer_rows_any<WT>(h, true, w.pdm[l], h->pkc, h->pvc, l, h->Xp, h->ssq_p, 0, 0, 1, nullptr, nullptr, -1, ps);
     StageGemv hd = stage_base(h);
     hd.W[0] = w.pdm_lm_head;
     hd.gamma[0] = (const float*)w.pdm_final_norm;
@@ -741,25 +832,40 @@ int do_prefill(spd_t* h, int P) {
   for (int s0 = 0; s0 < P; s0 += kRowsMR) {
     const int M = std::min(kRowsMR, P - s0);
     hipLaunchKernelGGL((k_embed_rows<WT>), dim3(M), dim3(kWG), 0, s, h->tokens, s0, (const WT*)w.embed, g.d, h->Xt,
-                       h->taps, g.m);
+                       h->taps, g.m, h->ssq_t);
     for (int l = 0; l < g.L; ++l)
-      layer_rows_any<WT>(h, true, w.layers[l], h->kc, h->vc, l, h->Xt, M, s0, 0, h->kv_len, h->taps,
+      layer_rows_any<WT>(h, true, w.layers[l], h->kc, h->vc, l, h->Xt, h->ssq_t, M, s0, 0, h->kv_len, h->taps,
                          g.anchor_of_layer[l + 1], s);
     // draft module prefill on the full-depth features of the chunk
-    RowsGemv a = rows_base(h);
-    a.M_arg = M;
-    a.pos0_arg = s0;
-    a.W[0] = w.fc[g.m - 1];
-    a.Kg[0] = g.m * g.d;
-    a.N = g.d;
-    a.units = g.d;
-    a.x = h->taps;
-    a.ldx = g.m * g.d;
-    a.out = h->Xp;
-    a.ldo = g.d;
-    launch_rows<WT, EPI_STORE>(h, a, M, s);
+    if (sizeof(WT) == 2) {
+      MfmaArgs a = mfma_base(h);
+      a.M_arg = M;
+      a.pos0_arg = s0;
+      a.W[0] = (const uint16_t*)w.fc[g.m - 1];
+      a.K[0] = g.m * g.d;
+      a.N = g.d;
+      a.x = h->taps;
+      a.ldx = g.m * g.d;
+      a.out = h->Xp;
+      a.ldo = g.d;
+      a.ssq_out = h->ssq_p;
+      launch_mfma<EPI_STORE>(h, a, 1, M, s);
+    } else {
+      RowsGemv a = rows_base(h);
+      a.M_arg = M;
+      a.pos0_arg = s0;
+      a.W[0] = w.fc[g.m - 1];
+      a.Kg[0] = g.m * g.d;
+      a.N = g.d;
+      a.units = g.d;
+      a.x = h->taps;
+      a.ldx = g.m * g.d;
+      a.out = h->Xp;
+      a.ldo = g.d;
+      launch_rows<WT, EPI_STORE>(h, a, M, s);
+    }
     for (int l = 0; l < g.Ls; ++l)
-      layer_rows_any<WT>(h, true, w.pdm[l], h->pkc, h->pvc, l, h->Xp, M, s0, 0, nullptr, nullptr, -1, s);
+      layer_rows_any<WT>(h, true, w.pdm[l], h->pkc, h->pvc, l, h->Xp, h->ssq_p, M, s0, 0, nullptr, nullptr, -1, s);
     if (s0 + M == P) {
       const int grid = head_fixed<WT>(h, h->Xt + (size_t)(M - 1) * g.d, w.lm_head, w.final_norm, h->logits,
                                       h->parts, s);
@@ -779,7 +885,7 @@ int do_ar(spd_t* h, int s0, int n) {
   for (int i = 0; i < n; ++i) {
     const int pos = s0 + i;
     hipLaunchKernelGGL((k_embed_rows<WT>), dim3(1), dim3(kWG), 0, s, h->tokens, pos, (const WT*)w.embed, g.d,
-                       h->Xt, (float*)nullptr, g.m);
+                       h->Xt, (float*)nullptr, g.m, (float*)nullptr);
     for (int l = 0; l < g.L; ++l)
       rows_layer<WT>(h, w.layers[l], h->kc, h->vc, l, h->Xt, 1, pos, 0, h->kv_len, nullptr, -1, s);
     const int grid = head_fixed<WT>(h, h->Xt, w.lm_head, w.final_norm, h->logits, h->parts, s);
@@ -917,10 +1023,9 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   h->ring = (spd_cycle_rec*)(ws + L.ring);
   h->cnt_s = (int32_t*)(ws + L.cnt_s);
   h->cnt_r = (int32_t*)(ws + L.cnt_r);
-  h->xh = (uint16_t*)(ws + L.xh);
-  h->xl = (uint16_t*)(ws + L.xl);
-  h->ah = (uint16_t*)(ws + L.ah);
-  h->al = (uint16_t*)(ws + L.al);
+  h->ssq_t = (float*)(ws + L.ssq_t);
+  h->ssq_p = (float*)(ws + L.ssq_p);
+  h->mpart = (float*)(ws + L.mpart);
 
   auto fail = [&](hipError_t e) {
     h->hip_err = (int)e;
@@ -940,9 +1045,8 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   if ((e = hipMemcpy(h->kv_len, zl.data(), sizeof(int32_t) * SPD_MAX_LAYERS, hipMemcpyHostToDevice)) != hipSuccess)
     return fail(e);
   // arrival counters start at zero (each merging workgroup resets its own);
-  // the bf16 split buffers are cleared so rows past M hold finite values
-  if ((e = hipMemset(ws + L.cnt_s, 0, L.xh - L.cnt_s)) != hipSuccess) return fail(e);
-  if ((e = hipMemset(ws + L.xh, 0, L.total - L.xh)) != hipSuccess) return fail(e);
+  // scratch is cleared once so that nothing reads uninitialised memory
+  if ((e = hipMemset(ws + L.cnt_s, 0, L.total - L.cnt_s)) != hipSuccess) return fail(e);
   hipLaunchKernelGGL(k_rope_table, dim3(512), dim3(256), 0, h->ss, h->rcos, h->rsin, L.ctx_cap, g.hd,
                      (double)cfg->rope_base);
   if ((e = hipGetLastError()) != hipSuccess) return fail(e);
