@@ -193,14 +193,16 @@ struct Geo {
   int fpat[SPD_MAX_STAGES + 1];             // f(k) for k = 0..n
 };
 
-// KV-cache addressing.  K is stored [layer][kvh][hd/8][ctx][8] so that
-// consecutive positions are consecutive 16-byte chunks (one position per
-// lane in the score loop); V is [layer][kvh][ctx][hd].
+// KV-cache addressing.  K is stored [layer][kvh][hd/8][ctx][8]: eight
+// consecutive head dims of one position are a 16-byte chunk and consecutive
+// positions are consecutive chunks.  V is stored [layer][kvh][ctx/8][hd][8]:
+// eight consecutive positions of one head dim are a 16-byte chunk.  These are
+// the operand layouts of the attention kernels' 16-byte loads.
 __device__ __forceinline__ size_t k_index(const Geo& g, int layer, int kvh, int pos, int dim) {
   return ((((size_t)layer * g.Hkv + kvh) * (g.hd / 8) + (dim >> 3)) * g.ctx_cap + pos) * 8 + (dim & 7);
 }
 __device__ __forceinline__ size_t v_index(const Geo& g, int layer, int kvh, int pos, int dim) {
-  return (((size_t)layer * g.Hkv + kvh) * g.ctx_cap + pos) * g.hd + dim;
+  return ((((size_t)layer * g.Hkv + kvh) * (g.ctx_cap / 8) + (pos >> 3)) * g.hd + dim) * 8 + (pos & 7);
 }
 
 }  // namespace spd

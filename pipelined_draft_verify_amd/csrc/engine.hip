@@ -39,7 +39,7 @@ struct Layout {
   size_t s_q, s_pacc, s_pml, s_o, s_act;
   size_t Xt, Xp, r_q, r_pacc, r_pml, r_o, r_act, taps;
   size_t logits, plogits, pw, parts, pparts, ring;
-  size_t cnt_s, cnt_r, ssq_t, ssq_p, mpart;
+  size_t ssq_t, ssq_p, mpart;
   size_t total;
   int ctx_cap, nsplit, mr, log_cap, nparts_max;
 };
@@ -148,8 +148,6 @@ Layout make_layout(const spd_config* c) {
   L.parts = take(sizeof(ArgPair) * L.nparts_max);
   L.pparts = take(sizeof(ArgPair) * L.nparts_max);
   L.ring = take(sizeof(spd_cycle_rec) * (size_t)L.log_cap);
-  L.cnt_s = take(sizeof(int32_t) * (size_t)n * Hkv);
-  L.cnt_r = take(sizeof(int32_t) * (size_t)L.mr * Hkv);
   // matrix-core path (bf16): per-row partial sums of squares of the prefill
   // rows and the draft-module rows, and the split-K partial tiles
   L.ssq_t = take(sizeof(float) * L.mr * (size_t)(d / kSsqCols));
@@ -194,7 +192,6 @@ struct spd_handle {
   float *logits, *plogits, *pw;
   ArgPair *parts, *pparts;
   spd_cycle_rec* ring;
-  int32_t *cnt_s, *cnt_r;
   float *ssq_t, *ssq_p, *mpart;
   int policy = SPD_DRAFT_NATURAL;
   float p_accept = 0.f;
@@ -285,12 +282,51 @@ RowsGemv rows_base(spd_t* h) {
   return a;
 }
 
+// Split attention + split merge.  Matrix cores for bf16 caches (query tiles
+// of 16: QT = 1 for one token, up to 4 for blocks of rows), VALU for fp32.
+template <typename WT, int HD>
+void attention_launch(const Attn& t, dim3 grid, int QT, int merge_rows, hipStream_t s) {
+  if (sizeof(WT) == 2) {
+    switch (QT) {
+      case 1: hipLaunchKernelGGL((k_attn_mfma<HD, 1>), grid, dim3(kWG), attn_mfma_lds(HD, 1), s, t); break;
+      case 2: hipLaunchKernelGGL((k_attn_mfma<HD, 2>), grid, dim3(kWG), attn_mfma_lds(HD, 2), s, t); break;
+      case 3: hipLaunchKernelGGL((k_attn_mfma<HD, 3>), grid, dim3(kWG), attn_mfma_lds(HD, 3), s, t); break;
+      default: hipLaunchKernelGGL((k_attn_mfma<HD, 4>), grid, dim3(kWG), attn_mfma_lds(HD, 4), s, t); break;
+    }
+  } else {
+    hipLaunchKernelGGL((k_attn_valu<WT, HD>), grid, dim3(kWG), 0, s, t);
+  }
+  hipLaunchKernelGGL((k_attn_merge<HD>), dim3(merge_rows, t.g.Hq), dim3(HD), 0, s, t);
+}
+
+template <typename WT>
+void attention_any(const Attn& t, dim3 grid, int QT, int merge_rows, hipStream_t s) {
+  if (t.g.hd == 128)
+    attention_launch<WT, 128>(t, grid, QT, merge_rows, s);
+  else
+    attention_launch<WT, 64>(t, grid, QT, merge_rows, s);
+}
+
+// Dynamic LDS above the default limit for the matrix-core attention kernels.
+hipError_t attn_lds_limits() {
+  hipError_t e = hipSuccess;
+#define SPD_ATTN_LDS(HD, QT)                                                                              \
+  if (e == hipSuccess)                                                                                    \
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma<HD, QT>),                         \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)attn_mfma_lds(HD, QT));
+  SPD_ATTN_LDS(128, 1) SPD_ATTN_LDS(128, 2) SPD_ATTN_LDS(128, 3) SPD_ATTN_LDS(128, 4)
+  SPD_ATTN_LDS(64, 1) SPD_ATTN_LDS(64, 2) SPD_ATTN_LDS(64, 3) SPD_ATTN_LDS(64, 4)
+#undef SPD_ATTN_LDS
+  return e;
+}
+
 // Attention over row-batched queries (prefill chunk, AR token or the draft
-// module's trailing rows) with the split merge fused; output fp32 rows r_o.
+// module's trailing rows); output fp32 rows r_o.
 template <typename WT>
 void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, int from_ctrl, int max_rows,
                     hipStream_t s) {
   const Geo& g = h->g;
+  const int G = g.Hq / g.Hkv;
   Attn t;
   memset(&t, 0, sizeof(t));
   t.pmode = PM_ROWS;
@@ -301,19 +337,20 @@ void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, in
   t.pacc = h->r_pacc;
   t.pml = h->r_pml;
   t.o = h->r_o;
-  t.counters = h->cnt_r;
   t.from_ctrl = from_ctrl;
   t.pos0_arg = pos0;
   t.nrows_arg = M;
-  t.QB = std::max(1, kAttnQ / (g.Hq / g.Hkv));
+  int QT = 1;
+  if (sizeof(WT) == 2) {
+    t.QB = std::min(kAttnMQ / G, max_rows);
+    QT = (t.QB * G + 15) / 16;
+  } else {
+    t.QB = std::max(1, kAttnQ / G);
+  }
   t.qblocks = (max_rows + t.QB - 1) / t.QB;
   t.ctrl = h->ctrl;
   t.g = g;
-  const dim3 grid(g.nsplit, g.Hkv * t.qblocks, 1);
-  if (g.hd == 128)
-    hipLaunchKernelGGL((k_attn<WT, 128>), grid, dim3(kWG), 0, s, t);
-  else
-    hipLaunchKernelGGL((k_attn<WT, 64>), grid, dim3(kWG), 0, s, t);
+  attention_any<WT>(t, dim3(g.nsplit, g.Hkv * t.qblocks, 1), QT, max_rows, s);
 }
 
 // One decoder layer over row-batched activations X on the VALU row GEMV
@@ -646,13 +683,9 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     t.pacc = h->s_pacc;
     t.pml = h->s_pml;
     t.o = h->s_o;
-    t.counters = h->cnt_s;
     t.ctrl = h->ctrl;
     t.g = g;
-    if (g.hd == 128)
-      hipLaunchKernelGGL((k_attn<WT, 128>), dim3(g.nsplit, g.Hkv, g.n), dim3(kWG), 0, ss, t);
-    else
-      hipLaunchKernelGGL((k_attn<WT, 64>), dim3(g.nsplit, g.Hkv, g.n), dim3(kWG), 0, ss, t);
+    attention_any<WT>(t, dim3(g.nsplit, g.Hkv, g.n), 1, g.n, ss);
     // output projection + residual
     StageGemv o = stage_base(h);
     o.n_groups = g.n;
@@ -1021,8 +1054,6 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   h->parts = (ArgPair*)(ws + L.parts);
   h->pparts = (ArgPair*)(ws + L.pparts);
   h->ring = (spd_cycle_rec*)(ws + L.ring);
-  h->cnt_s = (int32_t*)(ws + L.cnt_s);
-  h->cnt_r = (int32_t*)(ws + L.cnt_r);
   h->ssq_t = (float*)(ws + L.ssq_t);
   h->ssq_p = (float*)(ws + L.ssq_p);
   h->mpart = (float*)(ws + L.mpart);
@@ -1044,9 +1075,9 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   std::vector<int32_t> zl(SPD_MAX_LAYERS, 0);
   if ((e = hipMemcpy(h->kv_len, zl.data(), sizeof(int32_t) * SPD_MAX_LAYERS, hipMemcpyHostToDevice)) != hipSuccess)
     return fail(e);
-  // arrival counters start at zero (each merging workgroup resets its own);
-  // scratch is cleared once so that nothing reads uninitialised memory
-  if ((e = hipMemset(ws + L.cnt_s, 0, L.total - L.cnt_s)) != hipSuccess) return fail(e);
+  // matrix-core scratch is cleared once so that nothing reads uninitialised memory
+  if ((e = hipMemset(ws + L.ssq_t, 0, L.total - L.ssq_t)) != hipSuccess) return fail(e);
+  if ((e = attn_lds_limits()) != hipSuccess) return fail(e);
   hipLaunchKernelGGL(k_rope_table, dim3(512), dim3(256), 0, h->ss, h->rcos, h->rsin, L.ctx_cap, g.hd,
                      (double)cfg->rope_base);
   if ((e = hipGetLastError()) != hipSuccess) return fail(e);
@@ -1287,7 +1318,7 @@ int spd_debug_read(spd_t* h, int32_t what, int32_t index, void* out_host, size_t
           if (what == SPD_DBG_KV_K)
             src = (((size_t)kvh * (g.hd / 8) + dim / 8) * g.ctx_cap + p) * 8 + dim % 8;
           else
-            src = ((size_t)kvh * g.ctx_cap + p) * g.hd + dim;
+            src = (((size_t)kvh * (g.ctx_cap / 8) + p / 8) * g.hd + dim) * 8 + p % 8;
           memcpy(out + (((size_t)p * g.Hkv + kvh) * g.hd + dim) * es, tmp.data() + src * es, es);
         }
     return SPD_OK;
