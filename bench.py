@@ -181,6 +181,14 @@ def main():
     hbm_frac = float(per_cycle_bytes.sum() / (cyc_end.sum() * 1e-3) / PEAK_HBM)
     occ = recs["occupancy"]
     full = occ == w.n
+    # where the time and the bubble go, by occupancy (stderr diagnostics)
+    st = cyc_arr[:, 0].reshape(reps, K_c).mean(axis=0)
+    pd = cyc_arr[:, 1].reshape(reps, K_c).mean(axis=0)
+    for a in sorted(set(int(x) for x in occ)):
+        sel = occ == a
+        log(f"occupancy {a}: {int(sel.sum())} cycles, stage {st[sel].mean() * 1e3:.0f} us, "
+            f"draft {pd[sel].mean() * 1e3:.0f} us, cycle {cyc_end[sel].mean() * 1e3:.0f} us, "
+            f"bubble {np.maximum(0, pd[sel] - st[sel]).sum() / cyc_end.sum():.4f}")
     hbm_full = float(per_cycle_bytes[full].sum() / (cyc_end[full].sum() * 1e-3) / PEAK_HBM) if full.any() else None
     # dominant kernel: stage gate/up GEMV; algorithmic bytes = a * 2F * d * es per launch
     gu_bytes_step = float(sum(int(r["occupancy"]) for r in recs) * (w.L // w.n) * 2 * w.F * w.d * es)

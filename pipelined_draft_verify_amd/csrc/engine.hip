@@ -71,10 +71,12 @@ bool valid_config(const spd_config* c) {
   return true;
 }
 
-// K ranges of one matrix-core product (N weight rows, K inputs): the divisor
-// of K / kMKC that gives closest to ~640 workgroups in total.
+// K ranges of one matrix-core product (N weight rows, K inputs): one when
+// the 64-row groups alone cover the CUs (the epilogue then stays in the
+// GEMV), else the divisor of K / kMKC closest to ~640 workgroups in total.
 int mfma_splits(int N, int K) {
   const int groups = N / kMGroup;
+  if (groups >= kCUs) return 1;  // the epilogue stays fused: no reduce launch
   const int chunks = K / kMKC;
   const int target = (640 + groups - 1) / groups;
   int best = 1;
@@ -345,7 +347,9 @@ void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, in
   t.nrows_arg = M;
   int QT = 1;
   if (sizeof(WT) == 2) {
-    t.QB = std::min(kAttnMQ / G, max_rows);
+    // one query tile per workgroup: more workgroups, each streaming its KV
+    // split once more from the cache
+    t.QB = std::max(1, std::min(16 / G, max_rows));
     QT = (t.QB * G + 15) / 16;
   } else {
     t.QB = std::max(1, kAttnQ / G);
