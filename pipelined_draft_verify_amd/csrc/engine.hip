@@ -249,9 +249,15 @@ int stage_grid(int units, int upt, int n_groups, int K) {
 template <typename WT, int EPI>
 void launch_stage(spd_t* h, const StageGemv& a, int n_groups_max, hipStream_t s, int* grid_out = nullptr) {
   constexpr int upt = (epi_pairs(EPI) ? 2 : 4) * (kWG / kWave);
-  const int grid = stage_grid(a.units, upt, n_groups_max, a.K);
+  // un-normalised long inputs (the down projection) are read from the cache
+  // rather than staged: no LDS, so the draft stream's kernels fit beside it
+  const bool xg = EPI == EPI_RESID && a.K > h->g.d;
+  const int grid = stage_grid(a.units, upt, n_groups_max, xg ? 0 : a.K);
   if (grid_out) *grid_out = grid;
-  hipLaunchKernelGGL((k_gemv_stage<WT, EPI>), dim3(grid), dim3(kWG), a.K * sizeof(float), s, a);
+  if (xg)
+    hipLaunchKernelGGL((k_gemv_stage<WT, EPI, true>), dim3(grid), dim3(kWG), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemv_stage<WT, EPI>), dim3(grid), dim3(kWG), a.K * sizeof(float), s, a);
 }
 
 template <typename WT, int EPI>

@@ -86,9 +86,13 @@ struct StageGemv {
   Geo g;
 };
 
-template <typename WT, int EPI>
+// XG: the input row is read straight from global memory (cache-resident)
+// instead of being staged in LDS -- for un-normalised long inputs (the down
+// projection), so that the kernel holds no LDS and the draft stream's kernels
+// can share its CUs.  The arithmetic is the same either way.
+template <typename WT, int EPI, bool XG = false>
 __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
-  extern __shared__ float xs[];  // [K]
+  extern __shared__ float xs_lds[];  // [K] (unless XG)
   __shared__ float red[kWG / kWave];
   __shared__ ArgPair wbest[kWG / kWave];
   constexpr int VEC = WVec<WT>::N;
@@ -127,6 +131,7 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
 
   int cur = -1, pos = 0, slot = 0;
   const WT* W = nullptr;
+  const float* xs = xs_lds;
   for (long long tile = t0; tile < t1; ++tile) {
     const int grp = (int)(tile / tpg);
     const int ut = (int)(tile - (long long)grp * tpg);
@@ -137,14 +142,18 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
       slot = fixed ? 0 : pos % g.nslots;
       const float* x = fixed ? xfix : A.x + (A.x_by_slot ? slot : grp) * A.x_stride;
       const float* gm = A.gamma[grp];
-      __syncthreads();
-      if (gm) {
-        const float rstd = row_rstd(x, A.K, g.eps, red);
-        for (int i = threadIdx.x; i < A.K; i += kWG) xs[i] = x[i] * rstd * gm[i];
+      if (XG) {
+        xs = x;
       } else {
-        for (int i = threadIdx.x; i < A.K; i += kWG) xs[i] = x[i];
+        __syncthreads();
+        if (gm) {
+          const float rstd = row_rstd(x, A.K, g.eps, red);
+          for (int i = threadIdx.x; i < A.K; i += kWG) xs_lds[i] = x[i] * rstd * gm[i];
+        } else {
+          for (int i = threadIdx.x; i < A.K; i += kWG) xs_lds[i] = x[i];
+        }
+        __syncthreads();
       }
-      __syncthreads();
       W = reinterpret_cast<const WT*>(A.W[grp]);
       if (EPI == EPI_QKV && ut == 0 && threadIdx.x == 0 && A.kv_len) {
         int* len = A.kv_len + A.layer[grp];
