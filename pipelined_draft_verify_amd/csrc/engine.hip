@@ -297,6 +297,7 @@ RowsGemv rows_base(spd_t* h) {
 // of 16: QT = 1 for one token, up to 4 for blocks of rows), VALU for fp32.
 template <typename WT, int HD>
 void attention_launch(const Attn& t, dim3 grid, int QT, int merge_rows, hipStream_t s) {
+  // merge_rows == 0: the consumer merges the splits itself
   if (sizeof(WT) == 2) {
     switch (QT) {
       case 1: hipLaunchKernelGGL((k_attn_mfma<HD, 1>), grid, dim3(kWG), attn_mfma_lds(HD, 1), s, t); break;
@@ -307,7 +308,7 @@ void attention_launch(const Attn& t, dim3 grid, int QT, int merge_rows, hipStrea
   } else {
     hipLaunchKernelGGL((k_attn_valu<WT, HD>), grid, dim3(kWG), 0, s, t);
   }
-  hipLaunchKernelGGL((k_attn_merge<HD>), dim3(merge_rows, t.g.Hq), dim3(HD), 0, s, t);
+  if (merge_rows > 0) hipLaunchKernelGGL((k_attn_merge<HD>), dim3(merge_rows, t.g.Hq), dim3(HD), 0, s, t);
 }
 
 template <typename WT>
@@ -335,7 +336,7 @@ hipError_t attn_lds_limits() {
 // module's trailing rows); output fp32 rows r_o.
 template <typename WT>
 void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, int from_ctrl, int max_rows,
-                    hipStream_t s) {
+                    bool merge, hipStream_t s) {
   const Geo& g = h->g;
   const int G = g.Hq / g.Hkv;
   Attn t;
@@ -363,7 +364,7 @@ void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, in
   t.qblocks = (max_rows + t.QB - 1) / t.QB;
   t.ctrl = h->ctrl;
   t.g = g;
-  attention_any<WT>(t, dim3(g.nsplit, g.Hkv * t.qblocks, 1), QT, max_rows, s);
+  attention_any<WT>(t, dim3(g.nsplit, g.Hkv * t.qblocks, 1), QT, merge ? max_rows : 0, s);
 }
 
 // One decoder layer over row-batched activations X on the VALU row GEMV
@@ -394,7 +395,7 @@ void rows_layer(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int l
   a.vc = vc;
   a.kv_len = kv_len;
   launch_rows<WT, EPI_QKV>(h, a, max_rows, s);
-  rows_attention<WT>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, s);
+  rows_attention<WT>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, true, s);
   // output projection + residual
   a = rows_base(h);
   a.from_ctrl = from_ctrl;
@@ -503,14 +504,16 @@ void rows_layer_mfma(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, 
   a.vc = vc;
   a.kv_len = kv_len;
   launch_mfma<EPI_QKV>(h, a, 1, max_rows, s);
-  rows_attention<uint16_t>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, s);
+  // attention splits; the output projection merges them as it stages its input
+  rows_attention<uint16_t>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, false, s);
   // output projection + residual
   a.kv_len = nullptr;
   a.W[0] = (const uint16_t*)lw.w_o;
   a.K[0] = qd;
   a.N = g.d;
-  a.x = h->r_o;
-  a.ldx = qd;
+  a.rmode = RM_ATTN;
+  a.apacc = h->r_pacc;
+  a.apml = h->r_pml;
   a.gamma = nullptr;
   a.ssq = nullptr;
   a.out = X;
@@ -518,6 +521,7 @@ void rows_layer_mfma(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, 
   a.ssq_out = ssqX;
   launch_mfma<EPI_RESID>(h, a, 1, max_rows, s);
   // norm + gate/up + SwiGLU
+  a.rmode = RM_CONTIG;
   a.W[0] = (const uint16_t*)lw.w_gu;
   a.K[0] = g.d;
   a.N = 2 * g.F;

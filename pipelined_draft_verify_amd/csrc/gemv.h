@@ -23,7 +23,7 @@ namespace spd {
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3, EPI_STORE = 4 };
 enum GMode { GM_STAGE = 0, GM_EXIT = 1, GM_FIXED = 2, GM_PDMLAST = 3 };
-enum RMode { RM_CONTIG = 0, RM_FC = 1 };
+enum RMode { RM_CONTIG = 0, RM_FC = 1, RM_ATTN = 2 };
 
 __host__ __device__ constexpr bool epi_pairs(int epi) { return epi == EPI_QKV || epi == EPI_SWIGLU; }
 

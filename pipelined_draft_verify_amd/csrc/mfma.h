@@ -54,10 +54,12 @@ struct MfmaArgs {
   int poff[SPD_MAX_ANCHORS];    // first partial slab of the product
   int N;                        // weight rows (multiple of kMGroup)
   // activation rows (fp32)
-  int rmode;                    // RM_CONTIG or RM_FC
+  int rmode;                    // RM_CONTIG, RM_FC or RM_ATTN
   const float* x;               // RM_CONTIG: row m at x + (row_base + m) * ldx
   int ldx;
   const float* slot_anchors;    // RM_FC: row i reads anchors 0..f of the slot of position pos0 + i
+  const float* apacc;           // RM_ATTN: row i is the attention output of row i, merged from its
+  const float* apml;            //   split partials [row][Hq][nsplit][hd] and (max, sum) [row][Hq][nsplit][2]
   const float* gamma;           // fused RMSNorm gain [K], or nullptr (no norm)
   const float* ssq;             // per-row partial sums of squares of the input [row][ssq_parts], or nullptr
   int ssq_parts;
@@ -269,7 +271,34 @@ __global__ __launch_bounds__(kWG) void k_mfma_gemv(const MfmaArgs A) {
     for (int mt = 0; mt < MT; ++mt) {
       const int m = br + 16 * mt;
       const int k = kb + c * kMKC + bk;
-      if (m < M) {
+      if (m < M && A.rmode == RM_ATTN) {
+        // merge the row's attention splits for the 16 dims k..k+15 (one head):
+        // the same arithmetic, in split order, as the split-merge kernel
+        const Geo& g = A.g;
+        const int orow = rsrc[m];
+        const int ns = (pos0 + orow) / kSplit + 1;
+        const int head = k / g.hd, d0 = k - head * g.hd;
+        const size_t base = ((size_t)orow * g.Hq + head) * g.nsplit;
+        float M = -INFINITY;
+        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, A.apml[(base + sp) * 2]);
+        float num[16], den = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) num[e] = 0.f;
+        for (int sp = 0; sp < ns; ++sp) {
+          const float w = expf(A.apml[(base + sp) * 2] - M);
+          den = fmaf(w, A.apml[(base + sp) * 2 + 1], den);
+          const float* pa = A.apacc + (base + sp) * g.hd + d0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(pa + 4 * j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) num[4 * j + e] = fmaf(w, a[e], num[4 * j + e]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xr[mt][j] = f32x4{num[4 * j] / den, num[4 * j + 1] / den, num[4 * j + 2] / den, num[4 * j + 3] / den};
+      } else if (m < M) {
         const float* x = mfma_in_row(A, rsrc[m], pos0) + k;
 #pragma unroll
         for (int j = 0; j < 4; ++j) xr[mt][j] = *reinterpret_cast<const f32x4*>(x + 4 * j);
