@@ -21,6 +21,8 @@
 
 namespace spd {
 
+constexpr int kStageMinWG = 256;  // workgroups of a stage step at the lowest occupancy
+
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3, EPI_STORE = 4 };
 enum GMode { GM_STAGE = 0, GM_EXIT = 1, GM_FIXED = 2, GM_PDMLAST = 3 };
 enum RMode { RM_CONTIG = 0, RM_FC = 1, RM_ATTN = 2 };
@@ -122,8 +124,14 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
   const float* xfix = (A.gmode == GM_PDMLAST) ? A.x + (size_t)(C->a + C->pending - 1) * A.x_stride : A.x;
   const int tpg = (A.units + UPT - 1) / UPT;
   const long long T = (long long)n_act * tpg;
-  const long long t0 = T * blockIdx.x / gridDim.x;
-  const long long t1 = T * (blockIdx.x + 1) / gridDim.x;
+  // stage steps with few tokens in flight use a proportional share of the
+  // grid (at least one workgroup per CU): the step takes about as long, and
+  // the draft stream's latency-bound kernels find free CUs
+  int nwg = gridDim.x;
+  if (A.gmode == GM_STAGE) nwg = max(min((int)gridDim.x, kStageMinWG), (int)((long long)gridDim.x * n_act / g.n));
+  if ((int)blockIdx.x >= nwg) return;
+  const long long t0 = T * blockIdx.x / nwg;
+  const long long t1 = T * (blockIdx.x + 1) / nwg;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   float bv = -INFINITY;
