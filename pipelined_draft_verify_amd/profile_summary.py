@@ -1,7 +1,13 @@
 """Summaries of rocprofv3 output for the committed profiles/ files.
 
   python -m pipelined_draft_verify_amd.profile_summary stats <kernel_stats.csv> [--cmd "..."]
+  python -m pipelined_draft_verify_amd.profile_summary timeline <kernel_trace.csv> --cycles K [--skip S] [--cmd "..."]
   python -m pipelined_draft_verify_amd.profile_summary traffic <fetch_dir> <write_dir> --cmd "..."
+
+`timeline` takes K cycles of a kernel trace, ending --skip cycles before its
+end (a cycle starts at each k_entry dispatch), and prints, per stream and per kernel/grid, the launches,
+average duration and time per cycle, plus each stream's busy time and the
+device-idle time (no kernel on any stream).
 
 `traffic` reads two counter-collection runs (FETCH_SIZE, then WRITE_SIZE, KiB
 per dispatch), scales each by what the same counter read for a plain copy of
@@ -23,7 +29,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_gate_up_4b_n8.json")
-GU_REGEX = r"k_gemv_stage<unsigned short, 2>"
+GU_REGEX = r"k_gemv_stage<unsigned short, 2[,>]"
 COPY_REGEX = r"copy"
 COPY_BYTES = 1 << 30
 
@@ -48,6 +54,46 @@ def stats(path: str, top: int = 16) -> str:
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:top]:
         out.append(f"{_short(r['Name'])[:44]:44s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} "
                    f"{float(r['TotalDurationNs']) / 1e6:9.1f} {100 * float(r['TotalDurationNs']) / tot:6.1f}")
+    return "\n".join(out)
+
+
+def timeline(path: str, cycles: int, skip: int = 0, top: int = 30) -> str:
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    ent = [i for i, r in enumerate(rows) if "k_entry" in r["Kernel_Name"]]
+    if len(ent) < cycles + skip:
+        raise ValueError(f"trace has {len(ent)} cycles, fewer than {cycles + skip}")
+    # cycles [-(cycles + skip), -skip) of the trace; host-side copies between
+    # steps (rollback) are not part of the region
+    lo = ent[-(cycles + skip)]
+    hi = ent[-skip] if skip else len(rows)
+    sel = [r for r in rows[lo:hi] if "copyBuffer" not in r["Kernel_Name"]]
+    t0 = int(sel[0]["Start_Timestamp"])
+    t1 = max(int(r["End_Timestamp"]) for r in sel)
+    span = (t1 - t0) / 1e3
+    out = [f"region: {len(sel)} dispatches over {span / 1e3:.1f} ms for {cycles} cycles "
+           f"-> {span / cycles:.1f} us/cycle"]
+    busy, agg = {}, {}
+    for r in sel:
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        st = r["Stream_Id"]
+        busy[st] = busy.get(st, 0.0) + d
+        key = (st, _short(r["Kernel_Name"]), r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"])
+        a = agg.setdefault(key, [0, 0.0])
+        a[0] += 1
+        a[1] += d
+    for st in sorted(busy):
+        out.append(f"stream {st}: busy {busy[st] / 1e3:.1f} ms ({busy[st] / cycles:.1f} us/cycle)")
+    # device-idle: time covered by no kernel of any stream
+    iv = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in sel)
+    idle, end = 0, iv[0][0]
+    for s0, e0 in iv:
+        if s0 > end:
+            idle += s0 - end
+        end = max(end, e0)
+    out.append(f"device idle: {idle / 1e3 / cycles:.1f} us/cycle ({100 * idle / 1e3 / span:.1f}% of the region)")
+    out.append(f"{'stream':>6s} {'kernel':34s} {'grid (threads x, y, z)':>24s} {'calls':>6s} {'avg us':>8s} {'us/cycle':>9s}")
+    for (st, name, gx, gy, gz), (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:top]:
+        out.append(f"{st:>6s} {name[:34]:34s} {gx + ',' + gy + ',' + gz:>24s} {n:6d} {t / n:8.2f} {t / cycles:9.2f}")
     return "\n".join(out)
 
 
@@ -100,6 +146,11 @@ def main(argv=None):
     a = sub.add_parser("stats")
     a.add_argument("csv")
     a.add_argument("--cmd", default="")
+    t = sub.add_parser("timeline")
+    t.add_argument("csv")
+    t.add_argument("--cycles", type=int, required=True)
+    t.add_argument("--skip", type=int, default=0)
+    t.add_argument("--cmd", default="")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_dir")
     b.add_argument("write_dir")
@@ -110,6 +161,10 @@ def main(argv=None):
         if args.cmd:
             print(f"command: {args.cmd}")
         print(stats(args.csv))
+    elif args.what == "timeline":
+        if args.cmd:
+            print(f"command: {args.cmd}")
+        print(timeline(args.csv, args.cycles, args.skip))
     else:
         rec = traffic(args.fetch_dir, args.write_dir)
         rec["command"] = args.cmd
