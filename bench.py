@@ -62,15 +62,16 @@ def cycle_bytes(w, rec, es):
     return b
 
 
-def traffic_bytes(algo_bytes):
+def traffic_bytes(workload):
     """HBM bytes per gate/up launch from the committed counter summary, or
-    None if the kernel sources changed since the counters were taken."""
+    None if it was taken on another workload or the kernel sources changed
+    since the counters were taken."""
     from pipelined_draft_verify_amd import profile_summary as ps
     try:
         rec = json.load(open(ps.TRAFFIC_JSON))
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != ps.kernel_source_hash():
+    if rec.get("workload") != workload or rec.get("source_hash") != ps.kernel_source_hash():
         return None
     return int(rec["traffic_bytes_per_launch"])
 
@@ -233,7 +234,7 @@ def main():
             "peak": PEAK_HBM / 1e9,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM, 4),
-            "traffic": traffic_bytes(gu_bytes_launch),
+            "traffic": traffic_bytes(w.name),
             "avg_launch_us": round(gu_avg_s * 1e6, 2),
             "bytes_per_launch": int(gu_bytes_launch),
             "timed_over": "every gate/up launch of one eager-launched step of the workload",
