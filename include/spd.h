@@ -59,6 +59,7 @@ extern "C" {
 #define SPD_MAX_PDM_LAYERS 8
 #define SPD_MAX_ANCHORS 8
 #define SPD_MAX_STAGES 16
+#define SPD_MAX_VOCAB (1 << 20)
 
 /* return codes */
 #define SPD_OK 0
@@ -107,7 +108,8 @@ extern "C" {
  * up to n_stages + 1 rows); pdm_layers <= n_layers / n_stages; anchors strictly
  * increasing with anchors[0] == 0 and anchors[n_anchors-1] <= n_layers;
  * n_heads % n_kv_heads == 0; head_dim in {64, 128}; d_model, d_ffn and
- * n_heads*head_dim multiples of 256; max_ctx <= 32768.
+ * n_heads*head_dim multiples of 256; max_ctx <= 32768; 2 <= vocab <=
+ * SPD_MAX_VOCAB.
  */
 typedef struct spd_config {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab;

@@ -17,6 +17,7 @@ SPD_MAX_LAYERS = 64
 SPD_MAX_PDM_LAYERS = 8
 SPD_MAX_ANCHORS = 8
 SPD_MAX_STAGES = 16
+SPD_MAX_VOCAB = 1 << 20
 
 SPD_OK, SPD_EINVAL, SPD_ESTATE, SPD_ECTX, SPD_EHIP, SPD_EDEVICE = 0, -1, -2, -3, -4, -5
 SPD_DTYPE_F32, SPD_DTYPE_BF16 = 0, 1

@@ -30,108 +30,251 @@ __device__ __forceinline__ ArgPair block_argmax_parts(const ArgPair* parts, int 
   return b;
 }
 
-// Each thread owns the contiguous index range [lo, hi) of V.
-__device__ __forceinline__ void chunk_of(int V, int& lo, int& hi) {
-  const int ch = (V + kCtlThreads - 1) / kCtlThreads;
-  lo = min(V, threadIdx.x * ch);
-  hi = min(V, lo + ch);
+// ---- sampling: softmax weights and inverse-CDF draws ------------------------
+// The vocabulary is cut into blocks of kCdfBlock consecutive ids, lane l of a
+// wave owning ids 4l..4l+3 of a block (one 16-byte load per lane).  A lane's
+// four weights are summed in id order in fp64, and an inclusive scan over the
+// 64 lanes gives the running sums inside the block; its last lane is the block
+// sum.  Blocks group into superblocks of 64 blocks, scanned the same way, and
+// one wave scans the superblock sums.  The cumulative weight of an id is the
+// sum of its superblock, block, lane and in-lane prefixes (all fp64), and a
+// draw takes the smallest id whose cumulative weight exceeds u * total.  Every
+// pass is coalesced, and the only serial steps are the three 64-wide scans of
+// the search, done by one wave.
+constexpr int kCdfPer = 4;
+constexpr int kCdfBlock = kWave * kCdfPer;                  // 256 ids
+constexpr int kCdfMaxBlocks = SPD_MAX_VOCAB / kCdfBlock;    // 4096
+constexpr int kCdfMaxSuper = kCdfMaxBlocks / kWave;         // 64
+constexpr int kCdfUnroll = 4;                               // blocks in flight per wave
+constexpr int kCtlWaves = kCtlThreads / kWave;
+static_assert(kCdfMaxSuper <= kWave, "one wave scans the superblock sums");
+
+struct CdfShared {
+  double bs[kCdfMaxBlocks];  // block sums
+  double ss[kCdfMaxSuper];   // superblock sums
+  double sinc[kCdfMaxSuper]; // inclusive scan of ss
+  double total;
+  int pick;
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave (fp64, log-step).
+__device__ __forceinline__ double wave_scan_d(double v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
 }
 
-// fp64 sum of per-thread values in thread order.
-__device__ __forceinline__ double block_sum_ordered(double v, double* sh) {
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  __shared__ double tot;
-  if (threadIdx.x == 0) {
-    double s = 0.0;
-    for (int k = 0; k < kCtlThreads; ++k) s += sh[k];
-    tot = s;
+__device__ __forceinline__ double lane_sum4(const double x[4]) { return ((x[0] + x[1]) + x[2]) + x[3]; }
+
+// Four consecutive floats p[v0..v0+3], zero at ids >= V.
+__device__ __forceinline__ void load4(const float* p, int v0, int V, bool vec, float out[4]) {
+  if (vec && v0 + 4 <= V) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(p + v0);
+    out[0] = t.x;
+    out[1] = t.y;
+    out[2] = t.z;
+    out[3] = t.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = (v0 + k < V) ? p[v0 + k] : 0.f;
+  }
+}
+__device__ __forceinline__ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Block sums of the weights given by w4(v0, x[4]) (the fp64 weights of ids
+// v0..v0+3, zero beyond V) into S.bs, then the superblock sums and the total.
+// Ends with a barrier; S.total is then valid in every thread.
+template <typename W4>
+__device__ __forceinline__ void cdf_sums(W4 w4, int V, CdfShared& S) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nb = (V + kCdfBlock - 1) / kCdfBlock;
+  const int nsb = (nb + kWave - 1) / kWave;
+  for (int b0 = wave; b0 < nb; b0 += kCtlWaves * kCdfUnroll) {
+    double x[kCdfUnroll][4];
+#pragma unroll
+    for (int u = 0; u < kCdfUnroll; ++u) {
+      const int b = b0 + u * kCtlWaves;
+      if (b < nb) {
+        w4(b * kCdfBlock + lane * kCdfPer, x[u]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[u][k] = 0.0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCdfUnroll; ++u) {
+      const int b = b0 + u * kCtlWaves;
+      const double s = wave_scan_d(lane_sum4(x[u]));
+      if (lane == kWave - 1 && b < nb) S.bs[b] = s;
+    }
   }
   __syncthreads();
-  const double r = tot;
+  for (int sb = wave; sb < nsb; sb += kCtlWaves) {
+    const int b = sb * kWave + lane;
+    const double s = wave_scan_d(b < nb ? S.bs[b] : 0.0);
+    if (lane == kWave - 1) S.ss[sb] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const double s = wave_scan_d(lane < nsb ? S.ss[lane] : 0.0);
+    if (lane < nsb) S.sinc[lane] = s;
+    if (lane == nsb - 1) S.total = s;
+  }
+  __syncthreads();
+}
+
+// Highest set lane of a nonzero ballot.
+__device__ __forceinline__ int last_lane(unsigned long long m) { return 63 - __clzll(m); }
+__device__ __forceinline__ int first_lane(unsigned long long m) { return __ffsll(m) - 1; }
+
+// Last id of block b with a positive weight (wave-uniform), or -1.
+template <typename W4>
+__device__ __forceinline__ int cdf_last_in_block(W4 w4, int b) {
+  const int lane = threadIdx.x & (kWave - 1);
+  double x[4];
+  w4(b * kCdfBlock + lane * kCdfPer, x);
+  int k_last = -1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (x[k] > 0.0) k_last = k;
+  const unsigned long long m = __ballot(k_last >= 0);
+  if (m == 0) return -1;
+  const int l = last_lane(m);
+  return b * kCdfBlock + l * kCdfPer + __shfl(k_last, l, kWave);
+}
+
+// Last id with a positive weight (wave-uniform), or -1.
+template <typename W4>
+__device__ __forceinline__ int cdf_last_positive(W4 w4, int nb, const CdfShared& S) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nsb = (nb + kWave - 1) / kWave;
+  unsigned long long m = __ballot(lane < nsb && S.ss[lane] > 0.0);
+  if (m == 0) return -1;
+  const int sb = last_lane(m);
+  const int b = sb * kWave + lane;
+  m = __ballot(b < nb && S.bs[b] > 0.0);
+  if (m == 0) return -1;
+  return cdf_last_in_block(w4, sb * kWave + last_lane(m));
+}
+
+// Smallest id whose cumulative weight exceeds thr, else the last id with a
+// positive weight (thr at or beyond the total), else -1.  Called after
+// cdf_sums with the same weights; run by wave 0, whose lanes all return it.
+template <typename W4>
+__device__ __forceinline__ int cdf_search_wave(W4 w4, int V, double thr, const CdfShared& S) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nb = (V + kCdfBlock - 1) / kCdfBlock;
+  const int nsb = (nb + kWave - 1) / kWave;
+  // superblock
+  double inc = lane < nsb ? S.sinc[lane] : 0.0;
+  unsigned long long m = __ballot(lane < nsb && inc > thr);
+  if (m == 0) return cdf_last_positive(w4, nb, S);
+  const int sb = first_lane(m);
+  double base = sb > 0 ? S.sinc[sb - 1] : 0.0;
+  // block within the superblock
+  const int b = sb * kWave + lane;
+  inc = wave_scan_d(b < nb ? S.bs[b] : 0.0);
+  double exc = __shfl_up(inc, 1, kWave);
+  if (lane == 0) exc = 0.0;
+  m = __ballot(b < nb && base + inc > thr);
+  int blk;
+  if (m == 0) {  // rounding between the two levels: the last block with weight
+    m = __ballot(b < nb && S.bs[b] > 0.0);
+    if (m == 0) return cdf_last_positive(w4, nb, S);
+    return cdf_last_in_block(w4, sb * kWave + last_lane(m));
+  }
+  const int bi = first_lane(m);
+  blk = sb * kWave + bi;
+  base = base + __shfl(exc, bi, kWave);
+  // lane within the block
+  double x[4];
+  w4(blk * kCdfBlock + lane * kCdfPer, x);
+  inc = wave_scan_d(lane_sum4(x));
+  exc = __shfl_up(inc, 1, kWave);
+  if (lane == 0) exc = 0.0;
+  m = __ballot(base + inc > thr);
+  if (m == 0) {
+    const int r = cdf_last_in_block(w4, blk);
+    return r >= 0 ? r : cdf_last_positive(w4, nb, S);
+  }
+  const int l = first_lane(m);
+  // id within the lane
+  double c = base + exc;
+  int found = -1, k_last = -1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    c += x[k];
+    if (found < 0 && c > thr) found = k;
+    if (x[k] > 0.0) k_last = k;
+  }
+  if (found < 0) found = k_last;  // rounding inside the lane
+  found = __shfl(found, l, kWave);
+  if (found < 0) {
+    const int r = cdf_last_in_block(w4, blk);
+    return r >= 0 ? r : cdf_last_positive(w4, nb, S);
+  }
+  return blk * kCdfBlock + l * kCdfPer + found;
+}
+
+// The draw by the whole workgroup: wave 0 searches, all threads get the id.
+template <typename W4>
+__device__ __forceinline__ int cdf_draw(W4 w4, int V, double u, CdfShared& S) {
+  if (threadIdx.x < kWave) {
+    const int r = cdf_search_wave(w4, V, u * S.total, S);
+    if (threadIdx.x == 0) S.pick = r;
+  }
+  __syncthreads();
+  const int r = S.pick;
   __syncthreads();
   return r;
 }
 
-// Softmax weights w_v = exp(l_v / T - max) written to `w` (fp32), returns
-// Z = sum_v w_v accumulated in fp64 (per-thread chunks in id order, then
-// thread order).  `lmax` is max_v l_v.
+// Softmax weights w_v = exp(l_v / T - max_v l_v / T) stored to `w` (fp32);
+// their block sums go to S and the fp64 total Z = sum_v w_v is returned.
+// `lmax` is max_v l_v.
 __device__ __forceinline__ double softmax_weights(const float* logits, float* w, int V, float T, float lmax,
-                                                  double* sh) {
-  int lo, hi;
-  chunk_of(V, lo, hi);
+                                                  CdfShared& S) {
   const float mt = (T == 1.0f) ? lmax : lmax / T;
-  double s = 0.0;
-  for (int v = lo; v < hi; ++v) {
-    const float l = (T == 1.0f) ? logits[v] : logits[v] / T;
-    const float e = expf(l - mt);
-    w[v] = e;
-    s += (double)e;
-  }
-  return block_sum_ordered(s, sh);
+  const bool vec = aligned16(logits) && aligned16(w);
+  cdf_sums(
+      [&](int v0, double x[4]) {
+        float l[4];
+        load4(logits, v0, V, vec, l);
+        float e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lt = (T == 1.0f) ? l[k] : l[k] / T;
+          e[k] = (v0 + k < V) ? expf(lt - mt) : 0.f;
+          x[k] = (double)e[k];
+        }
+        if (vec && v0 + 4 <= V) {
+          *reinterpret_cast<f32x4*>(w + v0) = f32x4{e[0], e[1], e[2], e[3]};
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (v0 + k < V) w[v0 + k] = e[k];
+        }
+      },
+      V, S);
+  return S.total;
 }
 
-// Inverse CDF: smallest id i with (ascending cumulative weight) > u * total,
-// where weight(v) is given by `wf(v)` (fp64).  Falls back to the last id with
-// positive weight.  All threads return the same id.
-template <typename WF>
-__device__ __forceinline__ int inverse_cdf(WF wf, int V, double u, double* sh) {
-  __shared__ int pick;
-  __shared__ int last_pos;
-  int lo, hi;
-  chunk_of(V, lo, hi);
-  double s = 0.0;
-  int lastnz = -1;
-  for (int v = lo; v < hi; ++v) {
-    const double x = wf(v);
-    s += x;
-    if (x > 0.0) lastnz = v;
+// Reads the stored fp32 weights back as the fp64 weights of a draw.
+struct StoredWeights {
+  const float* w;
+  int V;
+  bool vec;
+  __device__ void operator()(int v0, double x[4]) const {
+    float f[4];
+    load4(w, v0, V, vec, f);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = (double)f[k];
   }
-  sh[threadIdx.x] = s;
-  if (threadIdx.x == 0) {
-    pick = -1;
-    last_pos = -1;
-  }
-  __syncthreads();
-  if (lastnz >= 0) atomicMax(&last_pos, lastnz);
-  __shared__ double thr_s;
-  __shared__ int owner;
-  __shared__ double pre_s;
-  if (threadIdx.x == 0) {
-    double tot = 0.0;
-    for (int k = 0; k < kCtlThreads; ++k) tot += sh[k];
-    const double thr = u * tot;
-    double pre = 0.0;
-    int own = -1;
-    for (int k = 0; k < kCtlThreads; ++k) {
-      if (pre + sh[k] > thr) {
-        own = k;
-        break;
-      }
-      pre += sh[k];
-    }
-    thr_s = thr;
-    owner = own;
-    pre_s = pre;
-  }
-  __syncthreads();
-  if ((int)threadIdx.x == owner) {
-    double c = pre_s;
-    int found = -1;
-    for (int v = lo; v < hi; ++v) {
-      c += wf(v);
-      if (c > thr_s) {
-        found = v;
-        break;
-      }
-    }
-    pick = found;
-  }
-  __syncthreads();
-  const int r = (pick >= 0) ? pick : last_pos;
-  __syncthreads();
-  return r;
-}
+};
 
 // ---- tables -----------------------------------------------------------------
 // cos/sin of pos * base^(-2i/hd), computed in fp64 and rounded to fp32.
@@ -246,7 +389,7 @@ struct VerifyArgs {
 // ---- verification (A5) + accept / three-step rollback (A6) -----------------
 __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
   __shared__ ArgPair sh_ap[kCtlThreads / kWave];
-  __shared__ double sh_d[kCtlThreads];
+  __shared__ CdfShared S;
   __shared__ int s_y, s_acc;
   Ctrl* C = A.ctrl;
   const Geo& g = A.g;
@@ -276,8 +419,7 @@ __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
     }
   } else {
     // P = softmax(logits / T); accept iff u * Q(x) < P(x); else redraw from max(0, P - Q)
-    const double pZ = softmax_weights(A.logits, A.pw, g.V, A.temp, best.v, sh_d);
-    __syncthreads();
+    const double pZ = softmax_weights(A.logits, A.pw, g.V, A.temp, best.v, S);
     const float* qw = A.qring + (size_t)nslot * g.V;
     const double qZ = A.qz[nslot];
     const double u_acc = A.uni[(size_t)(j + 1) * SPD_U_COUNT + SPD_U_ACCEPT];
@@ -286,14 +428,23 @@ __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
     const bool acc = u_acc * Qx < Px;
     int y = xd;
     if (!acc) {
+      // max(0, P - Q) scaled by pZ * qZ > 0, which leaves the draw unchanged
       const double u_res = A.uni[(size_t)(j + 1) * SPD_U_COUNT + SPD_U_RESAMPLE];
       const float* pw = A.pw;
-      y = inverse_cdf(
-          [&](int v) {
-            const double r = (double)pw[v] / pZ - (double)qw[v] / qZ;
-            return r > 0.0 ? r : 0.0;
-          },
-          g.V, u_res, sh_d);
+      const int V = g.V;
+      const bool vec = aligned16(pw) && aligned16(qw);
+      auto r4 = [&](int v0, double x[4]) {
+        float p[4], q[4];
+        load4(pw, v0, V, vec, p);
+        load4(qw, v0, V, vec, q);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const double r = fma((double)p[k], qZ, -((double)q[k] * pZ));
+          x[k] = r > 0.0 ? r : 0.0;
+        }
+      };
+      cdf_sums(r4, V, S);
+      y = cdf_draw(r4, V, u_res, S);
     }
     if (threadIdx.x == 0) {
       s_y = y;
@@ -350,7 +501,7 @@ struct FinalizeArgs {
 // ---- draft finalisation (A9): prediction, draft policy, commit -------------
 __global__ __launch_bounds__(kCtlThreads) void k_pdm_finalize(const FinalizeArgs A) {
   __shared__ ArgPair sh_ap[kCtlThreads / kWave];
-  __shared__ double sh_d[kCtlThreads];
+  __shared__ CdfShared S;
   Ctrl* C = A.ctrl;
   const Geo& g = A.g;
   if (!C->active) return;
@@ -362,10 +513,9 @@ __global__ __launch_bounds__(kCtlThreads) void k_pdm_finalize(const FinalizeArgs
     raw = best.i;
   } else {
     float* qw = A.qring + (size_t)slot * g.V;
-    const double Z = softmax_weights(A.logits, qw, g.V, A.temp, best.v, sh_d);
-    __syncthreads();
+    const double Z = softmax_weights(A.logits, qw, g.V, A.temp, best.v, S);
     const double u = A.uni[(size_t)q * SPD_U_COUNT + SPD_U_DRAFT];
-    raw = inverse_cdf([&](int v) { return (double)qw[v]; }, g.V, u, sh_d);
+    raw = cdf_draw(StoredWeights{qw, g.V, aligned16(qw)}, g.V, u, S);
     if (threadIdx.x == 0) A.qz[slot] = Z;
   }
   if (threadIdx.x == 0) {
@@ -419,14 +569,13 @@ __global__ __launch_bounds__(kCtlThreads) void k_pick_token(const ArgPair* parts
                                                             float* pw, int V, int mode, float temp, const float* uni,
                                                             int32_t* tokens, int pos, Ctrl* C, uint32_t* flags) {
   __shared__ ArgPair sh_ap[kCtlThreads / kWave];
-  __shared__ double sh_d[kCtlThreads];
+  __shared__ CdfShared S;
   const ArgPair best = block_argmax_parts(parts, nparts, sh_ap);
   int y = best.i;
   if (mode == SPD_MODE_SAMPLE) {
-    softmax_weights(logits, pw, V, temp, best.v, sh_d);
-    __syncthreads();
+    softmax_weights(logits, pw, V, temp, best.v, S);
     const double u = uni[(size_t)pos * SPD_U_COUNT + SPD_U_TARGET];
-    y = inverse_cdf([&](int v) { return (double)pw[v]; }, V, u, sh_d);
+    y = cdf_draw(StoredWeights{pw, V, aligned16(pw)}, V, u, S);
   }
   if (threadIdx.x == 0) {
     y = valid_token(y, V, flags);

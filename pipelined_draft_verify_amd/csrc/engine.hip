@@ -61,7 +61,7 @@ bool valid_config(const spd_config* c) {
   if (c->d_model % 256 || c->d_ffn % 256 || (c->n_heads * c->head_dim) % 256) return false;
   if (c->d_model * c->n_anchors > 64 * 1024) return false;
   if (c->d_ffn > 12288 || c->d_model > 12288 || c->n_heads * c->head_dim > 12288) return false;
-  if (c->vocab < 2) return false;
+  if (c->vocab < 2 || c->vocab > SPD_MAX_VOCAB) return false;
   if (c->dtype != SPD_DTYPE_F32 && c->dtype != SPD_DTYPE_BF16) return false;
   if (c->mode != SPD_MODE_GREEDY && c->mode != SPD_MODE_SAMPLE) return false;
   if (c->mode == SPD_MODE_SAMPLE && !(c->temperature > 0.f)) return false;

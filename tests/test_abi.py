@@ -91,3 +91,14 @@ def test_stage_count_limit():
     with pytest.raises(A.SPDError) as e:
         A.spd_workspace_bytes(c)
     assert e.value.code == A.SPD_EINVAL
+
+
+def test_vocab_limit():
+    """A vocabulary beyond SPD_MAX_VOCAB (the sampler's block-sum capacity) is rejected."""
+    c = make_config(si.workload("4b_n8"))
+    c.vocab = A.SPD_MAX_VOCAB
+    assert A.spd_workspace_bytes(c) > 0
+    c.vocab = A.SPD_MAX_VOCAB + 1
+    with pytest.raises(A.SPDError) as e:
+        A.spd_workspace_bytes(c)
+    assert e.value.code == A.SPD_EINVAL

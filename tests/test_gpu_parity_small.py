@@ -90,6 +90,9 @@ SAMPLE_VARIANTS = {
     "bf16_n4_T0.3": dict(dtype="bf16", temperature=0.3, L=4, n=4, anchors=[0, 1, 2, 3, 4], G=30, seed=41),
     "bf16_gqa_T0.5": dict(dtype="bf16", temperature=0.5, L=6, n=3, Hq=8, Hkv=2, F=768, V=500,
                           anchors=[0, 2, 5], Ls=2, seed=42),
+    # odd vocabulary over several superblocks of the sampler's block sums:
+    # tail blocks, unaligned draft-weight slots, multi-level search
+    "f32_V20001_T1": dict(dtype="f32", temperature=1.0, V=20001, seed=43),
 }
 # a differing draw is a near-tie only if the threshold lies this close (as a
 # fraction of the total mass, or of Q(x) for the accept test) to its boundary
