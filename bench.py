@@ -88,6 +88,8 @@ def main():
                     help="launch every kernel from the host in the timed region (no HIP graphs)")
     ap.add_argument("--serialized", action="store_true",
                     help="run the draft module on the stage stream ahead of the stage step (no overlap)")
+    ap.add_argument("--schedule", choices=["pre", "post"], default="pre",
+                    help="draft-module features before (pre) or after (post) the stage step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -98,6 +100,8 @@ def main():
     from pipelined_draft_verify_amd import SPDEngine
 
     w = si.workload(args.workload)
+    if args.schedule != "pre":
+        w = w.replace(schedule=args.schedule)
     es = 2 if w.dtype == "bf16" else 4
     t0 = time.time()
     T = si.make_weights(w, "cuda:0")
@@ -189,7 +193,7 @@ def main():
         sel = occ == a
         log(f"occupancy {a}: {int(sel.sum())} cycles, stage {st[sel].mean() * 1e3:.0f} us, "
             f"draft {pd[sel].mean() * 1e3:.0f} us, cycle {cyc_end[sel].mean() * 1e3:.0f} us, "
-            f"bubble {np.maximum(0, pd[sel] - st[sel]).sum() / cyc_end.sum():.4f}")
+            f"share of the bubble {np.maximum(0, pd[sel] - st[sel]).sum() / cyc_end.sum():.4f}")
     hbm_full = float(per_cycle_bytes[full].sum() / (cyc_end[full].sum() * 1e-3) / PEAK_HBM) if full.any() else None
     # dominant kernel: stage gate/up GEMV; algorithmic bytes = a * 2F * d * es per launch
     gu_bytes_step = float(sum(int(r["occupancy"]) for r in recs) * (w.L // w.n) * 2 * w.F * w.d * es)
@@ -215,7 +219,8 @@ def main():
         "config": {
             "workload": f"{w.name}: L={w.L} d={w.d} heads {w.Hq}/{w.Hkv}x{w.hd} FFN {w.F} V={w.V} n={w.n} "
                         f"Ls={w.Ls} anchors={w.anchors} prompt {w.P} gen {w.G} "
-                        f"{w.mode} {w.policy}{' p=' + str(w.p_accept) if w.policy == 'forced' else ''}",
+                        f"{w.mode} {w.policy}{' p=' + str(w.p_accept) if w.policy == 'forced' else ''}"
+                        f" {w.schedule}-step drafting",
             "cycles_per_step": K_c,
             "parallelism": "single GPU, " + ("one stream (draft module serialized)" if args.serialized
                                              else "two HIP streams"),

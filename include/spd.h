@@ -77,6 +77,18 @@ extern "C" {
 #define SPD_MODE_GREEDY 0 /* accept iff draft == argmax ([TW] 6) */
 #define SPD_MODE_SAMPLE 1 /* accept w.p. min(1, P/Q), else redraw from max(0,P-Q) ([YB] 2.1) */
 
+/* Draft-module schedule ([PL] §3.3; the scheduling ablation of [PL] §4).
+ * PRE: the draft module reads the features of the trailing positions as they
+ *   stand before this cycle's stage step (the just-verified position at depth
+ *   n, in-flight tokens at depths a-1..0) and runs concurrently with it.
+ * POST: it reads them after the stage step (in-flight tokens at depths a..1;
+ *   an exiting token at depth n, whose draft-module key/values are committed
+ *   in the same cycle) and therefore runs after the stage step and the
+ *   verification, on the stage stream: drafting is serial again.  The tokens
+ *   entering the pipeline follow the same rules in both schedules. */
+#define SPD_SCHED_PRE 0
+#define SPD_SCHED_POST 1
+
 /* draft policy */
 #define SPD_DRAFT_NATURAL 0 /* the PDM's own prediction */
 #define SPD_DRAFT_FORCED 1  /* seeded forced acceptance (test harness device, greedy only) */
@@ -124,6 +136,7 @@ typedef struct spd_config {
   float rms_eps;      /* RMSNorm epsilon */
   float rope_base;    /* RoPE base */
   float temperature;  /* sample mode only */
+  int32_t schedule;   /* SPD_SCHED_* */
 } spd_config;
 
 /* Device pointers of one decoder layer.  Row-major, output features first:

@@ -18,7 +18,8 @@ finally-verified tokens only.
 
 Readings are those of the full state machine: the exiting token j verifies
 j+1, a rejection truncates to j+1 and re-seeds (y, j+1), the just-verified row
-is committed in the cycle after its exit.
+is committed in the cycle after its exit -- or, under the post-step schedule
+(the scheduling ablation of [PL] §4), in the cycle of its exit.
 """
 from __future__ import annotations
 
@@ -30,12 +31,14 @@ class ReplayError(AssertionError):
 
 
 class Replay:
-    def __init__(self, n: int, L: int, P: int, first: int, policy=None, sample: bool = False):
+    def __init__(self, n: int, L: int, P: int, first: int, policy=None, sample: bool = False,
+                 post: bool = False):
         if L % n:
             raise ValueError("n must divide L")
         self.n, self.L, self.per = n, L, L // n
         self.policy = policy
         self.sample = sample
+        self.post = post
         self.kv: List[int] = [P] * L
         self.C = P
         self.pending = False
@@ -95,7 +98,10 @@ class Replay:
                 acc = int(xd == yy)
             self.tokens[j + 1] = yy
             self.emitted += 1
-            self.pending = True
+            if self.post:
+                self.C += 1  # committed by this cycle's (post-step) draft step
+            else:
+                self.pending = True
             exit_pos = j
             if not acc:
                 self.kv = [j + 1] * self.L

@@ -60,6 +60,20 @@ def depth_layout(a: int, pending: bool, n: int) -> List[int]:
     return ([n] if pending else []) + list(range(a - 1, -1, -1))
 
 
+def post_depth_layout(a: int, n: int) -> List[int]:
+    """Depths of the draft module's rows under the post-step schedule.
+
+    After the stage step every token of the pre-step layout is one stage
+    deeper: the a tokens in flight at entry sit at depths a .. 1, and when
+    a = n the oldest of them has just exited at depth n (its row is the
+    full-depth row, committed in the same cycle; no row waits for the next
+    cycle).  [PL] §3.3 and the scheduling ablation of [PL] §4 describe the
+    post-step features only as "after the pipeline step"; this is that
+    reading.
+    """
+    return list(range(a, 0, -1))
+
+
 def key_depth(t: int, T: int, fill: int, n: int) -> int:
     """Depth at which position T appears in the feature sequence of step t.
 

@@ -16,6 +16,12 @@ One cycle ([RB] method steps 1-5, [PL] §3.1-3.4, [TW] §3-6):
      truncated to the verified length, the in-flight states are dropped, and
      stage 0 is re-seeded with the corrected token.
 
+Post-step schedule (the scheduling ablation of [PL] §4): step 2 moves after
+step 4 and reads the features as the stage step left them -- the exited
+token at depth n (its draft-module key/values committed in the same cycle),
+the in-flight tokens at depths a-1..1 -- so drafting waits for the stage step.
+Which token enters the pipeline in each cycle follows the same rules.
+
 Readings taken where the pages leave a step open:
   * positions are 0-indexed: the exiting token j keeps its KV, so the
     truncation length is j+1 (the pages' 1-indexed "t-n+1");
@@ -35,7 +41,7 @@ from seeded_inputs import U_ACCEPT, U_DRAFT, U_FORCE, U_RESAMPLE, U_TARGET
 
 from . import sampling
 from .model import PDM, Target
-from .schedule import depth_layout, key_depth
+from .schedule import depth_layout, key_depth, post_depth_layout
 
 
 class NaturalPolicy:
@@ -145,6 +151,7 @@ class SPDOracle:
         self.target = Target(w, W)
         self.pdm = PDM(w, W)
         self.sample = w.mode == "sample"
+        self.post = getattr(w, "schedule", "pre") == "post"
         self.T = w.temperature
         self.policy = policy or NaturalPolicy()
         self.u = uniforms
@@ -206,33 +213,19 @@ class SPDOracle:
         a = len(self.inflight)
         assert 1 <= a <= n, f"occupancy {a} outside 1..{n}"
         pending_row = self.pending is not None
+        post = self.post
 
-        # 2. draft module, on the pre-step features
-        rows = ([(self.pending, n)] if pending_row else []) + [(p, k) for p, k, _ in self.inflight]
-        depths = [k for _, k in rows]
-        assert depths == depth_layout(a, pending_row, n), (depths, a)
-        positions = [p for p, _ in rows]
-        assert positions == list(range(self.pdm.C, t + 1)), (positions, self.pdm.C)
-        for p, k in rows:
-            assert key_depth(t, p, a, n) == k
-        Gm = np.stack([self.pdm.feature(self.anchors[p], k) for p, k in rows])
-        X = self.pdm.run_rows(Gm, self.pdm.C)
-        if pending_row:
-            self.pdm.commit(1)
-            self.anchors.pop(self.pending, None)
-            self.pending = None
-        pl = self.pdm.logits(X[-1])
-        if self.hook is not None:
-            self.hook("pdm", dict(cycle=c, rows=rows, G=Gm, logits=pl))
-        if self.sample:
-            qw, qZ = sampling.softmax_weights(pl, self.T)
-            d_raw = self.dec.sample(("draft", c), qw, float(self.u[t + 1, U_DRAFT]))
-            d = d_raw
-            self.drafts[t + 1] = (d, (qw, qZ))
-        else:
-            d_raw = self.dec.argmax(("pdm", c), pl)
-            d = int(self.policy.draft(t + 1, d_raw))
-            self.drafts[t + 1] = (d, None)
+        # 2. draft module, on the pre-step features (post-step: after step 4)
+        if not post:
+            rows = ([(self.pending, n)] if pending_row else []) + [(p, k) for p, k, _ in self.inflight]
+            depths = [k for _, k in rows]
+            assert depths == depth_layout(a, pending_row, n), (depths, a)
+            for p, k in rows:
+                assert key_depth(t, p, a, n) == k
+            d_raw, d = self._draft(c, t, rows, commit=pending_row)
+            if pending_row:
+                self.anchors.pop(self.pending, None)
+                self.pending = None
 
         # 3. stage step: each token through its own stage
         for item in self.inflight:
@@ -264,8 +257,24 @@ class SPDOracle:
                 accept = int(xd == y)
             self.tokens[j + 1] = int(y)
             self.emitted += 1
-            self.pending = j
+            if not post:
+                self.pending = j
             exit_pos = j
+
+        # 2'. post-step schedule: the draft module reads the features after
+        # the stage step -- the exited token at depth n (committed now), the
+        # in-flight tokens at depths a-1..1 -- and runs before the rollback
+        # (a flushed cycle's draft is discarded like any other)
+        if post:
+            rows = ([(exit_pos, n)] if exit_pos >= 0 else []) + [(p, k) for p, k, _ in self.inflight]
+            depths = [k for _, k in rows]
+            assert depths == post_depth_layout(a, n), (depths, a)
+            for p, k in rows:
+                assert min(n, key_depth(t, p, a, n) + 1) == k
+            d_raw, d = self._draft(c, t, rows, commit=exit_pos >= 0)
+            if exit_pos >= 0:
+                self.anchors.pop(exit_pos, None)
+                self.pending = None
 
         # 5. transition / three-step rollback
         if exit_pos >= 0 and not accept:
@@ -287,6 +296,31 @@ class SPDOracle:
         self.logs.append(rec)
         self.ncycles += 1
         return rec
+
+    def _draft(self, c: int, t: int, rows, commit: bool):
+        """Draft-module step over the trailing rows [(position, depth)]: the
+        features g(p, k), the Ls layers over committed + trailing rows, the
+        first row's key/values committed if `commit`, and the prediction for
+        position t+1 from the newest row ([RB] method steps 2-4)."""
+        positions = [p for p, _ in rows]
+        assert positions == list(range(self.pdm.C, t + 1)), (positions, self.pdm.C)
+        Gm = np.stack([self.pdm.feature(self.anchors[p], k) for p, k in rows])
+        X = self.pdm.run_rows(Gm, self.pdm.C)
+        if commit:
+            self.pdm.commit(1)
+        pl = self.pdm.logits(X[-1])
+        if self.hook is not None:
+            self.hook("pdm", dict(cycle=c, rows=rows, G=Gm, X=X, logits=pl))
+        if self.sample:
+            qw, qZ = sampling.softmax_weights(pl, self.T)
+            d_raw = self.dec.sample(("draft", c), qw, float(self.u[t + 1, U_DRAFT]))
+            d = d_raw
+            self.drafts[t + 1] = (d, (qw, qZ))
+        else:
+            d_raw = self.dec.argmax(("pdm", c), pl)
+            d = int(self.policy.draft(t + 1, d_raw))
+            self.drafts[t + 1] = (d, None)
+        return d_raw, d
 
     def run(self, prompt: Sequence[int], G: int, max_cycles: Optional[int] = None):
         """Prefill, then cycle until G tokens are emitted (the first from prefill)."""

@@ -22,6 +22,7 @@ SPD_MAX_VOCAB = 1 << 20
 SPD_OK, SPD_EINVAL, SPD_ESTATE, SPD_ECTX, SPD_EHIP, SPD_EDEVICE = 0, -1, -2, -3, -4, -5
 SPD_DTYPE_F32, SPD_DTYPE_BF16 = 0, 1
 SPD_MODE_GREEDY, SPD_MODE_SAMPLE = 0, 1
+SPD_SCHED_PRE, SPD_SCHED_POST = 0, 1
 SPD_DRAFT_NATURAL, SPD_DRAFT_FORCED = 0, 1
 SPD_U_COUNT = 5
 SPD_FLAG_KVLEN, SPD_FLAG_OCCUPANCY, SPD_FLAG_CTX, SPD_FLAG_IDLE, SPD_FLAG_NODRAFT, SPD_FLAG_BADTOKEN = 1, 2, 4, 8, 16, 32
@@ -36,6 +37,7 @@ class spd_config(Structure):
         ("anchors", c_int32 * SPD_MAX_ANCHORS),
         ("dtype", c_int32), ("max_ctx", c_int32), ("max_new", c_int32), ("mode", c_int32),
         ("rms_eps", c_float), ("rope_base", c_float), ("temperature", c_float),
+        ("schedule", c_int32),
     ]
 
 

@@ -188,10 +188,20 @@ struct Geo {
   int qkv_rows;  // (Hq + 2 Hkv) hd
   int max_new;
   int max_ctx;   // positions must stay below this (uniform-table rows, KV capacity)
+  int post;      // draft module on post-step features (SPD_SCHED_POST)
   float eps;
   int anchor_of_layer[SPD_MAX_LAYERS + 1];  // anchor index of boundary b, or -1
   int fpat[SPD_MAX_STAGES + 1];             // f(k) for k = 0..n
 };
+
+// Depth (stages completed) of the feature of draft-module row i, position p.
+// Pre-step ([PL] §3.3): the just-verified row (pending) at depth n, in-flight
+// tokens at t - p (the newest at 0).  Post-step: every row one stage deeper,
+// t - p + 1, the exiting token then being at depth n.
+__device__ __forceinline__ int pdm_row_depth(const Geo& g, const Ctrl* C, int i, int p) {
+  if (g.post) return C->t - p + 1;
+  return (C->pending && i == 0) ? g.n : (C->t - p);
+}
 
 // KV-cache addressing.  K is stored [layer][kvh][hd/8][ctx][8]: eight
 // consecutive head dims of one position are a 16-byte chunk and consecutive

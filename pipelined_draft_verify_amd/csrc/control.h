@@ -463,7 +463,9 @@ __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
     C->r_exit = j;
     C->r_y = y;
     C->r_accept = acc;
-    C->pend_next = 1;
+    // pre-step: the exiting row's draft-module key/values are committed by
+    // the next cycle's draft step; post-step: by this cycle's
+    C->pend_next = g.post ? 0 : 1;
     if (!acc) {  // (ii) flush in-flight state and (iii) reseed stage 0
       C->reseed = 1;
       C->seed_tok = y;
@@ -530,7 +532,8 @@ __global__ __launch_bounds__(kCtlThreads) void k_pdm_finalize(const FinalizeArgs
     A.dring[slot] = d;
     C->r_draft = d;
     C->r_raw = raw;
-    C->C += C->pending;  // the just-verified row's key/values stay cached
+    // the just-verified row's key/values stay cached
+    C->C += g.post ? (C->a == g.n ? 1 : 0) : C->pending;
     spd_cycle_rec* rec = A.ring + C->rec_slot;
     rec->pdm_argmax = raw;
     rec->draft = d;

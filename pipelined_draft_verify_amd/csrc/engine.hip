@@ -68,6 +68,7 @@ bool valid_config(const spd_config* c) {
   if (c->max_new < 1 || c->max_ctx < c->n_stages + 2) return false;
   if (align_up((size_t)c->max_ctx, kSplit) / kSplit > (size_t)kMaxSplit) return false;
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 1.f)) return false;
+  if (c->schedule != SPD_SCHED_PRE && c->schedule != SPD_SCHED_POST) return false;
   return true;
 }
 
@@ -837,8 +838,11 @@ int enqueue_cycle(spd_t* h) {
   hipStream_t ss = h->ss, ps = h->ps;
   const bool graph = h->launch_mode == 1;
   // serialized: the draft module is enqueued on the stage stream ahead of the
-  // stage step (it reads only pre-step state, so the result is unchanged)
-  if (h->serialized) ps = ss;
+  // stage step (it reads only pre-step state, so the result is unchanged).
+  // Post-step schedule: it reads the stage step's output and the verdict, so
+  // it follows them on the stage stream.
+  const bool post = g.post != 0;
+  if (h->serialized || post) ps = ss;
   hipEvent_t e_start = nullptr, e_stage = nullptr, e_pdm_t = nullptr;
   if (h->timing) {
     e_start = pool_event(h);
@@ -856,15 +860,28 @@ int enqueue_cycle(spd_t* h) {
     HIPCHK(h, hipEventRecord(h->ev_entry, ss));
     HIPCHK(h, hipStreamWaitEvent(ps, h->ev_entry, 0));
   }
-  int r = graph ? (hipGraphLaunch(h->gx_pdm, ps) == hipSuccess ? SPD_OK : SPD_EHIP) : pdm_chain<WT>(h, ps);
-  if (r) return r;
-  if (e_pdm_t) HIPCHK(h, hipEventRecord(e_pdm_t, ps));
-  HIPCHK(h, hipEventRecord(h->ev_pdm, ps));
-  r = graph ? (hipGraphLaunch(h->gx_stage, ss) == hipSuccess ? SPD_OK : SPD_EHIP)
-            : stage_chain<WT>(h, ss, h->timing != 0);
-  if (r) return r;
+  auto draft = [&]() -> int {
+    int r = graph ? (hipGraphLaunch(h->gx_pdm, ps) == hipSuccess ? SPD_OK : SPD_EHIP) : pdm_chain<WT>(h, ps);
+    if (r) return r;
+    if (e_pdm_t) HIPCHK(h, hipEventRecord(e_pdm_t, ps));
+    HIPCHK(h, hipEventRecord(h->ev_pdm, ps));
+    return SPD_OK;
+  };
+  auto stage = [&]() -> int {
+    return graph ? (hipGraphLaunch(h->gx_stage, ss) == hipSuccess ? SPD_OK : SPD_EHIP)
+                 : stage_chain<WT>(h, ss, h->timing != 0);
+  };
+  int r;
+  if (post) {
+    if ((r = stage())) return r;
+    if (e_stage) HIPCHK(h, hipEventRecord(e_stage, ss));
+    if ((r = draft())) return r;
+  } else {
+    if ((r = draft())) return r;
+    if ((r = stage())) return r;
+    if (e_stage) HIPCHK(h, hipEventRecord(e_stage, ss));
+  }
   if (e_stage) {
-    HIPCHK(h, hipEventRecord(e_stage, ss));
     h->cyc_ev.push_back(e_start);
     h->cyc_ev.push_back(e_stage);
     h->cyc_ev.push_back(e_pdm_t);
@@ -1024,6 +1041,7 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   g.qkv_rows = (g.Hq + 2 * g.Hkv) * g.hd;
   g.max_new = cfg->max_new;
   g.max_ctx = cfg->max_ctx;
+  g.post = cfg->schedule == SPD_SCHED_POST ? 1 : 0;
   g.eps = cfg->rms_eps;
   for (int b = 0; b <= SPD_MAX_LAYERS; ++b) g.anchor_of_layer[b] = -1;
   for (int i = 0; i < g.m; ++i) g.anchor_of_layer[cfg->anchors[i]] = i;

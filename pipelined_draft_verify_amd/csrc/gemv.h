@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kWG) void k_gemv_rows(const RowsGemv A) {
       int cnt = 0, seen = 0;
       for (int i = 0; i < Mtot; ++i) {
         const int p = pos0 + i;
-        const int dep = (C->pending && i == 0) ? g.n : (C->t - p);
+        const int dep = pdm_row_depth(g, C, i, p);
         if (g.fpat[dep] == grp) {
           if (seen >= A.row_base && cnt < kRowsMR) rsrc[cnt++] = i;
           ++seen;

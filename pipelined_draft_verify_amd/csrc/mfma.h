@@ -111,7 +111,7 @@ __device__ __forceinline__ void mfma_select_rows(const MfmaArgs& A, int prob, in
       M = 0;
       for (int i = 0; i < Mtot; ++i) {
         const int p = pos0 + i;
-        const int dep = (C->pending && i == 0) ? g.n : (C->t - p);
+        const int dep = pdm_row_depth(g, C, i, p);
         if (g.fpat[dep] == prob && M < cap) rsrc[M++] = i;
       }
     } else {

@@ -57,6 +57,7 @@ class Workload:
     eps: float = 1e-6
     rope_base: float = 10000.0
     norm_gain: str = "ones"  # "ones" or "random" (1 + 0.1 N(0,1), for tests)
+    schedule: str = "pre"   # draft-module features: "pre" (before the stage step) or "post"
 
     @property
     def max_ctx(self) -> int:
@@ -85,6 +86,10 @@ WORKLOADS: Dict[str, Workload] = {
     "9b_sample": Workload("9b_sample", "bf16", 32, 4096, 32, 8, 128, 12288, 151936, 8, 4,
                           [0, 8, 16, 24, 31], P=2048, G=512, mode="sample",
                           temperature=1.0, seed=5),
+    # 4b_n8 with the draft module on post-step features (scheduling ablation)
+    "4b_n8_post": Workload("4b_n8_post", "bf16", 32, 2560, 20, 4, 128, 9728, 151936, 8, 4,
+                           [0, 8, 16, 24, 31], P=512, G=256, policy="forced",
+                           p_accept=0.8, seed=2, schedule="post"),
 }
 
 

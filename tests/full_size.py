@@ -109,7 +109,8 @@ def replay(run: dict):
     pol = None
     if w.mode == "greedy" and w.policy == "forced":
         pol = ForcedPolicy(run["ref"], w.p_accept, run["uni"], w.V)
-    rp = Replay(w.n, w.L, w.P, run["first"], policy=pol, sample=(w.mode == "sample"))
+    rp = Replay(w.n, w.L, w.P, run["first"], policy=pol, sample=(w.mode == "sample"),
+                post=(w.schedule == "post"))
     out = []
     for i, r in enumerate(recs):
         ex = int(r["exit_pos"]) >= 0
@@ -151,7 +152,10 @@ class OracleView:
         """Draft-module logits of the cycle of replay record q (rows row0..t)."""
         w, pdm = self.w, self.pdm
         row0, t = q["row0"], q["t"]
-        depths = schedule.depth_layout(q["a"], bool(q["pending_row"]), w.n)
+        if w.schedule == "post":
+            depths = schedule.post_depth_layout(q["a"], w.n)
+        else:
+            depths = schedule.depth_layout(q["a"], bool(q["pending_row"]), w.n)
         G = np.stack([pdm.feature(self.taps[p], k) for p, k in zip(range(row0, t + 1), depths)])
         saved = [(kv.K[row0:t + 1].copy(), kv.V[row0:t + 1].copy()) for kv in pdm.kv]
         C0 = pdm.C

@@ -19,7 +19,7 @@ from tests import full_size as fs
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = ["4b_n8", "9b_n8", "4b_n16", "9b_sample"]
+WORKLOADS = ["4b_n8", "9b_n8", "4b_n16", "9b_sample", "4b_n8_post"]
 PARTS = ["replay", "verifications", "draft_module_and_floats"]
 _C = {}
 

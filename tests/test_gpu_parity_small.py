@@ -61,6 +61,11 @@ VARIANTS = {
     # n = 16: up to 17 draft-module rows (two row tiles), all in one fusion pattern
     "n16_one_anchor_bf16": dict(dtype="bf16", L=16, n=16, Ls=1, anchors=[0], G=40, p=0.7, seed=43),
     "n16_one_anchor_f32": dict(dtype="f32", L=16, n=16, Ls=1, anchors=[0], G=40, p=0.7, seed=44),
+    # post-step schedule: the draft module reads the features after the stage step
+    "post_f32_forced": dict(dtype="f32", p=0.6, seed=37, schedule="post"),
+    "post_bf16_gqa_forced": dict(dtype="bf16", L=6, n=3, Hq=8, Hkv=2, F=768, V=500, anchors=[0, 2, 5], Ls=2,
+                                 p=0.5, seed=38, schedule="post"),
+    "post_deep_n8": dict(L=8, n=8, Ls=1, anchors=[0, 3, 8], G=20, p=0.7, seed=39, schedule="post"),
 }
 
 
@@ -93,6 +98,7 @@ SAMPLE_VARIANTS = {
     # odd vocabulary over several superblocks of the sampler's block sums:
     # tail blocks, unaligned draft-weight slots, multi-level search
     "f32_V20001_T1": dict(dtype="f32", temperature=1.0, V=20001, seed=43),
+    "f32_post_T1": dict(dtype="f32", temperature=1.0, seed=46, schedule="post"),
 }
 # a differing draw is a near-tie only if the threshold lies this close (as a
 # fraction of the total mass, or of Q(x) for the accept test) to its boundary

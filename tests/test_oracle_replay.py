@@ -19,7 +19,7 @@ FIELDS = ["t", "a", "pending_row", "draft", "exit_pos", "y", "accept", "kv_len",
 
 
 def _replay(w, first, logs, policy, sample=False):
-    r = Replay(w.n, w.L, w.P, first, policy=policy, sample=sample)
+    r = Replay(w.n, w.L, w.P, first, policy=policy, sample=sample, post=w.schedule == "post")
     out = []
     for l in logs:
         ex = l["exit_pos"] >= 0
@@ -34,9 +34,10 @@ def _same(logs, rep):
             assert l[f] == q[f], (l["cycle"], f, l[f], q[f])
 
 
+@pytest.mark.parametrize("sched", ["pre", "post"])
 @pytest.mark.parametrize("mi", range(len(MODELS)))
-def test_replay_reproduces_greedy_runs(mi):
-    w, W, prompt, u = _setup(G=14, **MODELS[mi])
+def test_replay_reproduces_greedy_runs(mi, sched):
+    w, W, prompt, u = _setup(G=14, schedule=sched, **MODELS[mi])
     ref, _ = ar_greedy(w, W, prompt, w.G)
     for name, pol in _policies(w, ref, u).items():
         o = SPDOracle(w, W, policy=pol, uniforms=u)
@@ -44,9 +45,10 @@ def test_replay_reproduces_greedy_runs(mi):
         _same(logs, _replay(w, toks[w.P], logs, pol))
 
 
-@pytest.mark.parametrize("mi,temp", [(0, 1.0), (3, 0.1), (5, 0.1)])
-def test_replay_reproduces_sampling_runs(mi, temp):
-    w, W, prompt, u = _setup(G=14, mode="sample", temperature=temp, **MODELS[mi])
+@pytest.mark.parametrize("mi,temp,sched", [(0, 1.0, "pre"), (3, 0.1, "pre"), (5, 0.1, "pre"), (0, 1.0, "post"),
+                                           (5, 0.1, "post")])
+def test_replay_reproduces_sampling_runs(mi, temp, sched):
+    w, W, prompt, u = _setup(G=14, mode="sample", temperature=temp, schedule=sched, **MODELS[mi])
     o = SPDOracle(w, W, uniforms=u)
     toks, logs = o.run(prompt, w.G)
     assert any(l["accept"] == 1 for l in logs) and any(l["accept"] == 0 for l in logs)
