@@ -10,18 +10,38 @@ Precision (the decisions are taken the same way on both sides): weights
 w_v = exp(l_v/T - max) in float32; normalisers, CDFs and the acceptance
 comparison in float64; inverse CDF = smallest id i whose ascending-id
 cumulative weight exceeds u * (total weight).
+
+Top-k ([RB] reproducibility assessment: the evaluation decodes with top-k 50,
+top-p 1.0): only the k largest logits keep their weight, the others weigh 0;
+equal logits rank by the lower id; the selection is on the logits as given
+(before the temperature).  Applying the same truncation to P and Q keeps the
+rejection rule exact for the truncated target law.  Top-p 1.0 truncates
+nothing.
 """
 from __future__ import annotations
 
 import numpy as np
 
 
-def softmax_weights(logits: np.ndarray, temperature: float = 1.0):
-    """(w float32, Z float64): unnormalised softmax weights and their sum."""
+def top_k_ids(logits: np.ndarray, k: int) -> np.ndarray:
+    """Ids of the k largest logits in ascending id order; equal logits rank
+    by the lower id (a stable sort on the negated value)."""
+    l = np.asarray(logits, np.float32)
+    order = np.lexsort((np.arange(len(l)), -l))
+    return np.sort(order[:k])
+
+
+def softmax_weights(logits: np.ndarray, temperature: float = 1.0, top_k: int = 0):
+    """(w float32, Z float64): unnormalised softmax weights and their sum;
+    with top_k > 0 only the top-k ids keep their weight."""
     l = logits.astype(np.float32)
     if temperature != 1.0:
         l = l / np.float32(temperature)
     w = np.exp(l - l.max()).astype(np.float32)
+    if 0 < top_k < len(w):
+        keep = np.zeros(len(w), bool)
+        keep[top_k_ids(logits, top_k)] = True
+        w = np.where(keep, w, np.float32(0)).astype(np.float32)
     return w, float(np.sum(w.astype(np.float64)))
 
 

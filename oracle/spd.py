@@ -153,6 +153,7 @@ class SPDOracle:
         self.sample = w.mode == "sample"
         self.post = getattr(w, "schedule", "pre") == "post"
         self.T = w.temperature
+        self.top_k = getattr(w, "top_k", 0)
         self.policy = policy or NaturalPolicy()
         self.u = uniforms
         if self.sample:
@@ -185,7 +186,7 @@ class SPDOracle:
                 full.append(taps)
         lg = self.target.logits(h)
         if self.sample:
-            pw, _ = sampling.softmax_weights(lg, self.T)
+            pw, _ = sampling.softmax_weights(lg, self.T, self.top_k)
             first = self.dec.sample(("first", 0), pw, float(self.u[self.P, U_TARGET]))
         else:
             first = self.dec.argmax(("first", 0), lg)
@@ -243,7 +244,7 @@ class SPDOracle:
             assert (j + 1) in self.drafts, "successor of an exiting token must be a draft"
             xd, qinfo = self.drafts.pop(j + 1)
             if self.sample:
-                pw, pZ = sampling.softmax_weights(lg, self.T)
+                pw, pZ = sampling.softmax_weights(lg, self.T, self.top_k)
                 ok = self.dec.accept(("accept", c), pw, pZ, qinfo[0], qinfo[1], xd,
                                      float(self.u[j + 1, U_ACCEPT]))
                 if ok:
@@ -312,7 +313,7 @@ class SPDOracle:
         if self.hook is not None:
             self.hook("pdm", dict(cycle=c, rows=rows, G=Gm, X=X, logits=pl))
         if self.sample:
-            qw, qZ = sampling.softmax_weights(pl, self.T)
+            qw, qZ = sampling.softmax_weights(pl, self.T, self.top_k)
             d_raw = self.dec.sample(("draft", c), qw, float(self.u[t + 1, U_DRAFT]))
             d = d_raw
             self.drafts[t + 1] = (d, (qw, qZ))

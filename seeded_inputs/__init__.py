@@ -58,6 +58,7 @@ class Workload:
     rope_base: float = 10000.0
     norm_gain: str = "ones"  # "ones" or "random" (1 + 0.1 N(0,1), for tests)
     schedule: str = "pre"   # draft-module features: "pre" (before the stage step) or "post"
+    top_k: int = 0          # sample mode: keep the k largest logits (0: the whole vocabulary)
 
     @property
     def max_ctx(self) -> int:

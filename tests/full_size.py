@@ -212,7 +212,7 @@ def check_sampling(run: dict, view: OracleView, reps, k: int = 32) -> Decisions:
     T = w.temperature
     teacher = {("first", 0): run["first"]}
     dec = Decisions(teacher, TOL[w.dtype], STOL[w.dtype])
-    pw0, _ = sampling.softmax_weights(view.logits_at(w.P - 1), T)
+    pw0, _ = sampling.softmax_weights(view.logits_at(w.P - 1), T, w.top_k)
     dec.sample(("first", 0), pw0, float(uni[w.P, U_TARGET]))
     exits = [i for i, q in enumerate(reps) if q["exit_pos"] >= 0]
     chosen = sample_indices(exits, k)
@@ -221,10 +221,10 @@ def check_sampling(run: dict, view: OracleView, reps, k: int = 32) -> Decisions:
         j, c2 = q["exit_pos"], q["drafted_at"]
         qd = reps[c2]
         assert qd["t"] == j and view.survived(qd)
-        qw, qZ = sampling.softmax_weights(view.pdm_logits(qd), T)
+        qw, qZ = sampling.softmax_weights(view.pdm_logits(qd), T, w.top_k)
         teacher[("draft", c2)] = int(recs[c2]["pdm_argmax"])
         dec.sample(("draft", c2), qw, float(uni[j + 1, U_DRAFT]))
-        pw, pZ = sampling.softmax_weights(view.logits_at(j), T)
+        pw, pZ = sampling.softmax_weights(view.logits_at(j), T, w.top_k)
         teacher[("accept", i)] = bool(recs[i]["accepted"])
         ok = dec.accept(("accept", i), pw, pZ, qw, qZ, qd["draft"], float(uni[j + 1, U_ACCEPT]))
         if not ok:

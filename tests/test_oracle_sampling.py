@@ -71,9 +71,9 @@ def test_softmax_weights_match_definition():
     assert Z == pytest.approx(ref.sum(), rel=1e-6)
 
 
-def _first_two_tokens_chi2():
+def _first_two_tokens_chi2(top_k: int = 0):
     w = si.tiny(L=2, n=2, Ls=1, anchors=[0, 2], d=32, Hq=2, Hkv=1, hd=16, F=48, V=11,
-                P=4, G=2, mode="sample", seed=21)
+                P=4, G=2, mode="sample", seed=21, top_k=top_k)
     W = si.nest_weights(si.weights_numpy_f32(si.make_weights(w)), w)
     W["lm_head"] = W["lm_head"] * np.float32(25.0)       # sharpen P
     W["pdm_lm_head"] = W["pdm_lm_head"] * np.float32(25.0)  # a different, sharp Q
@@ -83,14 +83,14 @@ def _first_two_tokens_chi2():
     for p, tok in enumerate(prompt):
         h, _ = tgt.forward_token(int(tok), p)
     lp1 = tgt.logits(h)
-    w1, Z1 = sampling.softmax_weights(lp1)
+    w1, Z1 = sampling.softmax_weights(lp1, 1.0, top_k)
     P1 = w1.astype(np.float64) / Z1
     joint = np.zeros((w.V, w.V))
     for x in range(w.V):
         t2 = Target(w, W)
         for p, tok in enumerate(list(prompt) + [x]):
             h2, _ = t2.forward_token(int(tok), p)
-        w2, Z2 = sampling.softmax_weights(t2.logits(h2))
+        w2, Z2 = sampling.softmax_weights(t2.logits(h2), 1.0, top_k)
         joint[x] = P1[x] * w2.astype(np.float64) / Z2
     runs = 4000
     counts = np.zeros((w.V, w.V))
@@ -113,10 +113,12 @@ def _first_two_tokens_chi2():
 
 
 @pytest.mark.slow
-def test_spd_sampling_first_tokens_follow_autoregressive_law():
+@pytest.mark.parametrize("top_k", [0, 3])
+def test_spd_sampling_first_tokens_follow_autoregressive_law(top_k):
     """Chi-square test: the joint law of the first two generated tokens under
-    SPD with rejection sampling equals the target's autoregressive law."""
-    chi2, crit, tail_n, tail_e = _first_two_tokens_chi2()
+    SPD with rejection sampling equals the target's autoregressive law (with
+    top-k: the autoregressive law of the truncated target)."""
+    chi2, crit, tail_n, tail_e = _first_two_tokens_chi2(top_k)
     assert chi2 < crit, (chi2, crit)
     assert tail_n <= tail_e * 3 + 10
 
