@@ -219,7 +219,8 @@ def main():
         "config": {
             "workload": f"{w.name}: L={w.L} d={w.d} heads {w.Hq}/{w.Hkv}x{w.hd} FFN {w.F} V={w.V} n={w.n} "
                         f"Ls={w.Ls} anchors={w.anchors} prompt {w.P} gen {w.G} "
-                        f"{w.mode} {w.policy}{' p=' + str(w.p_accept) if w.policy == 'forced' else ''}"
+                        f"{w.mode}{' top-k ' + str(w.top_k) if w.top_k else ''} "
+                        f"{w.policy}{' p=' + str(w.p_accept) if w.policy == 'forced' else ''}"
                         f" {w.schedule}-step drafting",
             "cycles_per_step": K_c,
             "parallelism": "single GPU, " + ("one stream (draft module serialized)" if args.serialized

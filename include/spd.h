@@ -60,6 +60,7 @@ extern "C" {
 #define SPD_MAX_ANCHORS 8
 #define SPD_MAX_STAGES 16
 #define SPD_MAX_VOCAB (1 << 20)
+#define SPD_MAX_TOPK 64
 
 /* return codes */
 #define SPD_OK 0
@@ -121,7 +122,7 @@ extern "C" {
  * increasing with anchors[0] == 0 and anchors[n_anchors-1] <= n_layers;
  * n_heads % n_kv_heads == 0; head_dim in {64, 128}; d_model, d_ffn and
  * n_heads*head_dim multiples of 256; max_ctx <= 32768; 2 <= vocab <=
- * SPD_MAX_VOCAB.
+ * SPD_MAX_VOCAB; schedule one of SPD_SCHED_*; 0 <= top_k <= min(SPD_MAX_TOPK, vocab).
  */
 typedef struct spd_config {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab;
@@ -137,6 +138,11 @@ typedef struct spd_config {
   float rope_base;    /* RoPE base */
   float temperature;  /* sample mode only */
   int32_t schedule;   /* SPD_SCHED_* */
+  int32_t top_k;      /* sample mode: only the top_k largest logits keep their weight, in the
+                         target's P and the draft module's Q alike (equal logits rank by the lower
+                         id; selection before the temperature); 0 = the whole vocabulary.
+                         0 <= top_k <= min(SPD_MAX_TOPK, vocab).  [RB] reproducibility assessment:
+                         the evaluation decodes with top-k 50, top-p 1.0 (no nucleus cut). */
 } spd_config;
 
 /* Device pointers of one decoder layer.  Row-major, output features first:

@@ -31,6 +31,19 @@ def top_k_ids(logits: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[:k])
 
 
+def top_k_margin(logits: np.ndarray, k: int) -> float:
+    """Logit gap between the k-th and the (k+1)-th largest logit: how firmly
+    the top-k set is decided (inf without truncation).  The set is decided by
+    logit comparisons exactly like an argmax, so a second implementation may
+    legitimately keep a different set when this gap is within its argmax
+    tolerance."""
+    l = np.asarray(logits, np.float32)
+    if k <= 0 or k >= len(l):
+        return float("inf")
+    s = np.sort(l)[::-1]
+    return float(s[k - 1] - s[k])
+
+
 def softmax_weights(logits: np.ndarray, temperature: float = 1.0, top_k: int = 0):
     """(w float32, Z float64): unnormalised softmax weights and their sum;
     with top_k > 0 only the top-k ids keep their weight."""

@@ -126,18 +126,26 @@ class Decisions:
         y = int(np.argmax(logits))
         return self._teach(key, y, lambda t: float(logits[y] - logits[t]), self.tol)
 
-    def sample(self, key, weights: np.ndarray, u: float) -> int:
+    def sample(self, key, weights: np.ndarray, u: float, set_margin: float = float("inf")) -> int:
+        """A draw; `set_margin` (top-k: the gap of the k-th and (k+1)-th
+        logits the weights were truncated with) within `tol` also makes a
+        differing draw a near-tie: the kept set itself was a near-tie."""
         i, _ = sampling.inverse_cdf(weights, u)
         c = np.cumsum(weights.astype(np.float64))
         thr = np.float64(u) * c[-1]
 
         def gap(t):
-            lo = c[t - 1] if t > 0 else 0.0
-            return float(max(lo - thr, thr - c[t], 0.0) / c[-1])
+            if set_margin <= self.tol:
+                return 0.0
+            lo = c[t - 1] if (t > 0 and t < len(c)) else 0.0
+            hi = c[t] if t < len(c) else c[-1]
+            return float(max(lo - thr, thr - hi, 0.0) / c[-1])
         return self._teach(key, i, gap, self.sample_tol)
 
-    def accept(self, key, p_w, p_Z, q_w, q_Z, x, u) -> bool:
+    def accept(self, key, p_w, p_Z, q_w, q_Z, x, u, set_margin: float = float("inf")) -> bool:
         acc, g = sampling.accept_test(p_w, p_Z, q_w, q_Z, x, u)
+        if set_margin <= self.tol:
+            g = 0.0
         return bool(self._teach(key, acc, lambda t: g, self.sample_tol))
 
 
@@ -187,7 +195,8 @@ class SPDOracle:
         lg = self.target.logits(h)
         if self.sample:
             pw, _ = sampling.softmax_weights(lg, self.T, self.top_k)
-            first = self.dec.sample(("first", 0), pw, float(self.u[self.P, U_TARGET]))
+            first = self.dec.sample(("first", 0), pw, float(self.u[self.P, U_TARGET]),
+                                    sampling.top_k_margin(lg, self.top_k))
         else:
             first = self.dec.argmax(("first", 0), lg)
         G = np.stack([self.pdm.feature(full[p], n) for p in range(self.P)])
@@ -245,13 +254,14 @@ class SPDOracle:
             xd, qinfo = self.drafts.pop(j + 1)
             if self.sample:
                 pw, pZ = sampling.softmax_weights(lg, self.T, self.top_k)
+                sm = min(sampling.top_k_margin(lg, self.top_k), qinfo[2])
                 ok = self.dec.accept(("accept", c), pw, pZ, qinfo[0], qinfo[1], xd,
-                                     float(self.u[j + 1, U_ACCEPT]))
+                                     float(self.u[j + 1, U_ACCEPT]), sm)
                 if ok:
                     y = xd
                 else:
                     r = sampling.residual(pw, pZ, qinfo[0], qinfo[1])
-                    y = self.dec.sample(("resample", c), r, float(self.u[j + 1, U_RESAMPLE]))
+                    y = self.dec.sample(("resample", c), r, float(self.u[j + 1, U_RESAMPLE]), sm)
                 accept = int(ok)
             else:
                 y = self.dec.argmax(("y", c), lg)
@@ -314,9 +324,10 @@ class SPDOracle:
             self.hook("pdm", dict(cycle=c, rows=rows, G=Gm, X=X, logits=pl))
         if self.sample:
             qw, qZ = sampling.softmax_weights(pl, self.T, self.top_k)
-            d_raw = self.dec.sample(("draft", c), qw, float(self.u[t + 1, U_DRAFT]))
+            qm = sampling.top_k_margin(pl, self.top_k)
+            d_raw = self.dec.sample(("draft", c), qw, float(self.u[t + 1, U_DRAFT]), qm)
             d = d_raw
-            self.drafts[t + 1] = (d, (qw, qZ))
+            self.drafts[t + 1] = (d, (qw, qZ, qm))
         else:
             d_raw = self.dec.argmax(("pdm", c), pl)
             d = int(self.policy.draft(t + 1, d_raw))

@@ -18,6 +18,7 @@ SPD_MAX_PDM_LAYERS = 8
 SPD_MAX_ANCHORS = 8
 SPD_MAX_STAGES = 16
 SPD_MAX_VOCAB = 1 << 20
+SPD_MAX_TOPK = 64
 
 SPD_OK, SPD_EINVAL, SPD_ESTATE, SPD_ECTX, SPD_EHIP, SPD_EDEVICE = 0, -1, -2, -3, -4, -5
 SPD_DTYPE_F32, SPD_DTYPE_BF16 = 0, 1
@@ -37,7 +38,7 @@ class spd_config(Structure):
         ("anchors", c_int32 * SPD_MAX_ANCHORS),
         ("dtype", c_int32), ("max_ctx", c_int32), ("max_new", c_int32), ("mode", c_int32),
         ("rms_eps", c_float), ("rope_base", c_float), ("temperature", c_float),
-        ("schedule", c_int32),
+        ("schedule", c_int32), ("top_k", c_int32),
     ]
 
 

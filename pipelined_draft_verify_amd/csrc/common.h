@@ -189,6 +189,7 @@ struct Geo {
   int max_new;
   int max_ctx;   // positions must stay below this (uniform-table rows, KV capacity)
   int post;      // draft module on post-step features (SPD_SCHED_POST)
+  int topk;      // sample mode: top-k truncation of P and Q (0: none)
   float eps;
   int anchor_of_layer[SPD_MAX_LAYERS + 1];  // anchor index of boundary b, or -1
   int fpat[SPD_MAX_STAGES + 1];             // f(k) for k = 0..n

@@ -276,6 +276,184 @@ struct StoredWeights {
   }
 };
 
+// ---- top-k sampling ---------------------------------------------------------
+// Only the k largest logits keep their weight (equal logits rank by the lower
+// id).  An element's rank key is 64 bits: an order-preserving image of its
+// logit above the complement of its id, so a larger key is a higher logit or,
+// on a tie, a lower id; 0 is "no element".  Each wave keeps the 64 best keys
+// it has seen as one sorted register per lane and streams its share of the
+// vocabulary: an element enters only if it beats the wave's current k-th key
+// (after the first blocks almost none does); a few entrants are shifted in
+// one at a time, many are sorted and merged.  Wave 0 then merges the 16 wave
+// lists; the k kept (id, logit) pairs end up in wave 0's lanes in ascending id
+// order, so weights, running sums and the draw are register work.
+constexpr int kTopK = SPD_MAX_TOPK;
+static_assert(kTopK == kWave, "one kept entry per lane of a wave");
+
+// Draft distribution Q of one slot under top-k: the kept ids in ascending
+// order, their fp32 weights and the count (its fp64 sum is kept in qz).
+struct SparseQ {
+  int32_t ids[kTopK];
+  float w[kTopK];
+  int32_t cnt;
+  int32_t pad[3];
+};
+
+struct TopkShared {
+  unsigned long long lists[kCtlWaves][kWave];
+};
+
+// Order-preserving unsigned image of a float; -0 ranks with +0, NaN lowest.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) return 0u;
+  if (f == 0.f) f = 0.f;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ unsigned long long rank_key(float l, int id) {
+  return ((unsigned long long)order_key(l) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ int rank_key_id(unsigned long long k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+__device__ __forceinline__ unsigned long long umin64(unsigned long long a, unsigned long long b) { return a < b ? a : b; }
+
+// Bitonic sort of one value per lane, descending over the 64 lanes.
+__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const unsigned long long o = __shfl_xor(v, stride, kWave);
+      const bool desc = (lane & size) == 0;
+      const bool lower = (lane & stride) == 0;
+      v = (lower == desc) ? umax64(v, o) : umin64(v, o);
+    }
+  return v;
+}
+
+// The 64 largest of two descending lane-sorted lists, descending.
+__device__ __forceinline__ unsigned long long wave_merge_desc(unsigned long long a, unsigned long long b) {
+  const int lane = threadIdx.x & (kWave - 1);
+  unsigned long long v = umax64(a, __shfl(b, kWave - 1 - lane, kWave));  // bitonic
+#pragma unroll
+  for (int stride = kWave / 2; stride > 0; stride >>= 1) {
+    const unsigned long long o = __shfl_xor(v, stride, kWave);
+    v = ((lane & stride) == 0) ? umax64(v, o) : umin64(v, o);
+  }
+  return v;
+}
+
+// Key x into the descending list (the smallest entry drops out).
+__device__ __forceinline__ unsigned long long wave_insert_desc(unsigned long long lst, unsigned long long x) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int pos = __popcll(__ballot(lst > x));
+  const unsigned long long up = __shfl_up(lst, 1, kWave);
+  return lane < pos ? lst : (lane == pos ? x : up);
+}
+
+// Wave w streams blocks w, w + 16, ... of kCdfBlock ids (lane l: ids 4l..4l+3)
+// and keeps the best 64 keys it sees (at least the best k).
+__device__ __forceinline__ unsigned long long wave_topk_pass(const float* logits, int V, int k) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nb = (V + kCdfBlock - 1) / kCdfBlock;
+  const bool vec = aligned16(logits);
+  unsigned long long lst = 0ull;
+  unsigned long long thr = 0ull;  // the list's k-th key
+  for (int b0 = wave; b0 < nb; b0 += kCtlWaves * kCdfUnroll) {
+    float l[kCdfUnroll][4];
+#pragma unroll
+    for (int u = 0; u < kCdfUnroll; ++u) {
+      const int b = b0 + u * kCtlWaves;
+      if (b < nb) {
+        load4(logits, b * kCdfBlock + lane * kCdfPer, V, vec, l[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCdfUnroll; ++u) {
+      const int b = b0 + u * kCtlWaves;
+      if (b >= nb) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int id = b * kCdfBlock + lane * kCdfPer + e;
+        const unsigned long long key = id < V ? rank_key(l[u][e], id) : 0ull;
+        const unsigned long long cand = key > thr ? key : 0ull;
+        unsigned long long m = __ballot(cand != 0ull);
+        if (m == 0ull) continue;
+        if (__popcll(m) > 8) {
+          lst = wave_merge_desc(lst, wave_sort_desc(cand));
+        } else {
+          while (m) {
+            const int src = first_lane(m);
+            m &= m - 1;
+            lst = wave_insert_desc(lst, __shfl(cand, src, kWave));
+          }
+        }
+        thr = __shfl(lst, k - 1, kWave);
+      }
+    }
+  }
+  return lst;
+}
+
+// Top-k of logits[0, V): called by every thread; in wave 0, lane i < k ends
+// with the i-th kept id in ascending id order and its logit (lanes >= k: id
+// -1).  `k` <= min(64, V).
+__device__ __forceinline__ void topk_select(const float* logits, int V, int k, TopkShared& S, int& id,
+                                            float& val) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const unsigned long long lst = wave_topk_pass(logits, V, k);
+  S.lists[wave][lane] = lst;
+  __syncthreads();
+  id = -1;
+  val = 0.f;
+  if (wave == 0) {
+    unsigned long long all = S.lists[0][lane];
+    for (int w = 1; w < kCtlWaves; ++w) all = wave_merge_desc(all, S.lists[w][lane]);
+    // the k best, re-sorted by ascending id (descending complement), logit carried along
+    const bool kept = lane < k && all != 0ull;
+    const uint32_t cid = kept ? (uint32_t)all : 0u;  // 0xFFFFFFFF - id
+    const unsigned long long byid = kept ? (((unsigned long long)cid << 32) | (all >> 32)) : 0ull;
+    const unsigned long long s = wave_sort_desc(byid);
+    if (s != 0ull) {
+      id = (int)(0xFFFFFFFFu - (uint32_t)(s >> 32));
+      val = order_value((uint32_t)s);
+    }
+  }
+  __syncthreads();
+}
+
+// In wave 0 after topk_select: fp32 weight exp(l/T - lmax/T) of the lane's
+// kept id (0 for empty lanes), as in the dense softmax.
+__device__ __forceinline__ float topk_weight(int id, float val, float T, float lmax) {
+  if (id < 0) return 0.f;
+  const float mt = (T == 1.0f) ? lmax : lmax / T;
+  const float lt = (T == 1.0f) ? val : val / T;
+  return expf(lt - mt);
+}
+
+// In wave 0: the smallest kept id whose running sum (ascending ids, fp64)
+// exceeds u * total, else the last id with positive weight, else -1; also
+// returns the total.  x = the lane's weight (0 for empty lanes).
+__device__ __forceinline__ int topk_draw(int id, double x, double u, double* total) {
+  const double inc = wave_scan_d(x);
+  const double tot = __shfl(inc, kWave - 1, kWave);
+  if (total) *total = tot;
+  const double thr = u * tot;
+  unsigned long long m = __ballot(id >= 0 && inc > thr);
+  if (m) return __shfl(id, first_lane(m), kWave);
+  m = __ballot(id >= 0 && x > 0.0);
+  if (m) return __shfl(id, last_lane(m), kWave);
+  return -1;
+}
+
 // ---- tables -----------------------------------------------------------------
 // cos/sin of pos * base^(-2i/hd), computed in fp64 and rounded to fp32.
 __global__ void k_rope_table(float* cosv, float* sinv, int ctx, int hd, double base) {
@@ -390,6 +568,7 @@ struct VerifyArgs {
 __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
   __shared__ ArgPair sh_ap[kCtlThreads / kWave];
   __shared__ CdfShared S;
+  __shared__ TopkShared TS;
   __shared__ int s_y, s_acc;
   Ctrl* C = A.ctrl;
   const Geo& g = A.g;
@@ -416,6 +595,44 @@ __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
     if (threadIdx.x == 0) {
       s_y = best.i;
       s_acc = (xd == best.i);
+    }
+  } else if (g.topk > 0) {
+    // P and Q truncated to their top k: P from this exit's logits, Q as drafted
+    int pid;
+    float pl;
+    topk_select(A.logits, g.V, g.topk, TS, pid, pl);
+    if (threadIdx.x < kWave) {
+      const int lane = threadIdx.x;
+      const float pwf = topk_weight(pid, pl, A.temp, best.v);
+      const double pZ = __shfl(wave_scan_d((double)pwf), kWave - 1, kWave);
+      const SparseQ* Qs = reinterpret_cast<const SparseQ*>(A.qring) + nslot;
+      const int qn = Qs->cnt;
+      const int qid = lane < qn ? Qs->ids[lane] : -1;
+      const float qwf = lane < qn ? Qs->w[lane] : 0.f;
+      const double qZ = A.qz[nslot];
+      const unsigned long long mp = __ballot(pid >= 0 && pid == xd);
+      const unsigned long long mq = __ballot(qid >= 0 && qid == xd);
+      const double Px = mp ? (double)__shfl(pwf, first_lane(mp), kWave) / pZ : 0.0;
+      const double Qx = mq ? (double)__shfl(qwf, first_lane(mq), kWave) / qZ : 0.0;
+      const double u_acc = A.uni[(size_t)(j + 1) * SPD_U_COUNT + SPD_U_ACCEPT];
+      const bool acc = u_acc * Qx < Px;
+      int y = xd;
+      if (!acc) {
+        // max(0, P - Q) on P's kept ids, scaled by pZ * qZ > 0
+        float qv = 0.f;
+        for (int jj = 0; jj < qn; ++jj) {
+          const int oid = __shfl(qid, jj, kWave);
+          const float ow = __shfl(qwf, jj, kWave);
+          if (oid == pid) qv = ow;
+        }
+        const double r = pid >= 0 ? fma((double)pwf, qZ, -((double)qv * pZ)) : 0.0;
+        const double u_res = A.uni[(size_t)(j + 1) * SPD_U_COUNT + SPD_U_RESAMPLE];
+        y = topk_draw(pid, r > 0.0 ? r : 0.0, u_res, nullptr);
+      }
+      if (lane == 0) {
+        s_y = y;
+        s_acc = acc ? 1 : 0;
+      }
     }
   } else {
     // P = softmax(logits / T); accept iff u * Q(x) < P(x); else redraw from max(0, P - Q)
@@ -504,6 +721,7 @@ struct FinalizeArgs {
 __global__ __launch_bounds__(kCtlThreads) void k_pdm_finalize(const FinalizeArgs A) {
   __shared__ ArgPair sh_ap[kCtlThreads / kWave];
   __shared__ CdfShared S;
+  __shared__ TopkShared TS;
   Ctrl* C = A.ctrl;
   const Geo& g = A.g;
   if (!C->active) return;
@@ -513,6 +731,24 @@ __global__ __launch_bounds__(kCtlThreads) void k_pdm_finalize(const FinalizeArgs
   int raw;
   if (A.mode == SPD_MODE_GREEDY) {
     raw = best.i;
+  } else if (g.topk > 0) {
+    // Q truncated to its top k: stored as (id, weight) pairs for the verification
+    int id;
+    float val;
+    topk_select(A.logits, g.V, g.topk, TS, id, val);
+    raw = -1;
+    if (threadIdx.x < kWave) {
+      const int lane = threadIdx.x;
+      const float wf = topk_weight(id, val, A.temp, best.v);
+      SparseQ* Qs = reinterpret_cast<SparseQ*>(A.qring) + slot;
+      Qs->ids[lane] = id;
+      Qs->w[lane] = wf;
+      if (lane == 0) Qs->cnt = g.topk;
+      double Z;
+      const double u = A.uni[(size_t)q * SPD_U_COUNT + SPD_U_DRAFT];
+      raw = topk_draw(id, (double)wf, u, &Z);
+      if (lane == 0) A.qz[slot] = Z;
+    }
   } else {
     float* qw = A.qring + (size_t)slot * g.V;
     const double Z = softmax_weights(A.logits, qw, g.V, A.temp, best.v, S);
@@ -569,13 +805,23 @@ __global__ __launch_bounds__(kWG) void k_embed_rows(const int32_t* tokens, int p
 // tokens[pos] = argmax (greedy) or a draw from softmax(logits/T) with
 // u[pos][SPD_U_TARGET]; optionally also the control block's seed token.
 __global__ __launch_bounds__(kCtlThreads) void k_pick_token(const ArgPair* parts, int nparts, const float* logits,
-                                                            float* pw, int V, int mode, float temp, const float* uni,
-                                                            int32_t* tokens, int pos, Ctrl* C, uint32_t* flags) {
+                                                            float* pw, int V, int mode, float temp, int topk,
+                                                            const float* uni, int32_t* tokens, int pos, Ctrl* C,
+                                                            uint32_t* flags) {
   __shared__ ArgPair sh_ap[kCtlThreads / kWave];
   __shared__ CdfShared S;
+  __shared__ TopkShared TS;
   const ArgPair best = block_argmax_parts(parts, nparts, sh_ap);
   int y = best.i;
-  if (mode == SPD_MODE_SAMPLE) {
+  if (mode == SPD_MODE_SAMPLE && topk > 0) {
+    int id;
+    float val;
+    topk_select(logits, V, topk, TS, id, val);
+    if (threadIdx.x < kWave) {
+      const double u = uni[(size_t)pos * SPD_U_COUNT + SPD_U_TARGET];
+      y = topk_draw(id, (double)topk_weight(id, val, temp, best.v), u, nullptr);
+    }
+  } else if (mode == SPD_MODE_SAMPLE) {
     softmax_weights(logits, pw, V, temp, best.v, S);
     const double u = uni[(size_t)pos * SPD_U_COUNT + SPD_U_TARGET];
     y = cdf_draw(StoredWeights{pw, V, aligned16(pw)}, V, u, S);

@@ -69,6 +69,7 @@ bool valid_config(const spd_config* c) {
   if (align_up((size_t)c->max_ctx, kSplit) / kSplit > (size_t)kMaxSplit) return false;
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 1.f)) return false;
   if (c->schedule != SPD_SCHED_PRE && c->schedule != SPD_SCHED_POST) return false;
+  if (c->top_k < 0 || c->top_k > SPD_MAX_TOPK || c->top_k > c->vocab) return false;
   return true;
 }
 
@@ -120,7 +121,8 @@ Layout make_layout(const spd_config* c) {
   L.tokens = take(sizeof(int32_t) * L.ctx_cap);
   L.dring = take(sizeof(int32_t) * nslots);
   const bool smp = c->mode == SPD_MODE_SAMPLE;
-  L.qring = take(smp ? sizeof(float) * nslots * (size_t)V : 0);
+  // draft distributions Q by slot: dense [V] weights, or the top-k (id, weight) pairs
+  L.qring = take(!smp ? 0 : c->top_k ? sizeof(SparseQ) * nslots : sizeof(float) * nslots * (size_t)V);
   L.qz = take(sizeof(double) * nslots);
   const size_t kvl = (size_t)Hkv * hd * L.ctx_cap * es;
   L.kc = take(kvl * c->n_layers);
@@ -937,7 +939,8 @@ int do_prefill(spd_t* h, int P) {
       const int grid = head_fixed<WT>(h, h->Xt + (size_t)(M - 1) * g.d, w.lm_head, w.final_norm, h->logits,
                                       h->parts, s);
       hipLaunchKernelGGL(k_pick_token, dim3(1), dim3(kCtlThreads), 0, s, h->parts, grid, h->logits, h->pw, g.V,
-                         h->cfg.mode, h->cfg.temperature, h->uni, h->tokens, P, h->ctrl, &h->ctrl->flags);
+                         h->cfg.mode, h->cfg.temperature, g.topk, h->uni, h->tokens, P, h->ctrl,
+                         &h->ctrl->flags);
     }
   }
   HIPCHK(h, hipGetLastError());
@@ -957,7 +960,7 @@ int do_ar(spd_t* h, int s0, int n) {
       rows_layer<WT>(h, w.layers[l], h->kc, h->vc, l, h->Xt, 1, pos, 0, h->kv_len, nullptr, -1, s);
     const int grid = head_fixed<WT>(h, h->Xt, w.lm_head, w.final_norm, h->logits, h->parts, s);
     hipLaunchKernelGGL(k_pick_token, dim3(1), dim3(kCtlThreads), 0, s, h->parts, grid, h->logits, h->pw, g.V,
-                       SPD_MODE_GREEDY, 1.0f, h->uni, h->tokens, pos + 1, (Ctrl*)nullptr, &h->ctrl->flags);
+                       SPD_MODE_GREEDY, 1.0f, 0, h->uni, h->tokens, pos + 1, (Ctrl*)nullptr, &h->ctrl->flags);
   }
   HIPCHK(h, hipGetLastError());
   return SPD_OK;
@@ -1042,6 +1045,7 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   g.max_new = cfg->max_new;
   g.max_ctx = cfg->max_ctx;
   g.post = cfg->schedule == SPD_SCHED_POST ? 1 : 0;
+  g.topk = cfg->mode == SPD_MODE_SAMPLE ? cfg->top_k : 0;
   g.eps = cfg->rms_eps;
   for (int b = 0; b <= SPD_MAX_LAYERS; ++b) g.anchor_of_layer[b] = -1;
   for (int i = 0; i < g.m; ++i) g.anchor_of_layer[cfg->anchors[i]] = i;

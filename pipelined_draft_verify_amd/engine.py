@@ -35,6 +35,7 @@ def make_config(w, max_ctx: Optional[int] = None) -> A.spd_config:
     c.mode = A.SPD_MODE_SAMPLE if w.mode == "sample" else A.SPD_MODE_GREEDY
     c.rms_eps, c.rope_base, c.temperature = w.eps, w.rope_base, w.temperature
     c.schedule = A.SPD_SCHED_POST if getattr(w, "schedule", "pre") == "post" else A.SPD_SCHED_PRE
+    c.top_k = getattr(w, "top_k", 0)
     return c
 
 

@@ -212,8 +212,9 @@ def check_sampling(run: dict, view: OracleView, reps, k: int = 32) -> Decisions:
     T = w.temperature
     teacher = {("first", 0): run["first"]}
     dec = Decisions(teacher, TOL[w.dtype], STOL[w.dtype])
-    pw0, _ = sampling.softmax_weights(view.logits_at(w.P - 1), T, w.top_k)
-    dec.sample(("first", 0), pw0, float(uni[w.P, U_TARGET]))
+    l0 = view.logits_at(w.P - 1)
+    pw0, _ = sampling.softmax_weights(l0, T, w.top_k)
+    dec.sample(("first", 0), pw0, float(uni[w.P, U_TARGET]), sampling.top_k_margin(l0, w.top_k))
     exits = [i for i, q in enumerate(reps) if q["exit_pos"] >= 0]
     chosen = sample_indices(exits, k)
     for i in chosen:
@@ -221,15 +222,19 @@ def check_sampling(run: dict, view: OracleView, reps, k: int = 32) -> Decisions:
         j, c2 = q["exit_pos"], q["drafted_at"]
         qd = reps[c2]
         assert qd["t"] == j and view.survived(qd)
-        qw, qZ = sampling.softmax_weights(view.pdm_logits(qd), T, w.top_k)
+        ql = view.pdm_logits(qd)
+        qw, qZ = sampling.softmax_weights(ql, T, w.top_k)
+        qm = sampling.top_k_margin(ql, w.top_k)
         teacher[("draft", c2)] = int(recs[c2]["pdm_argmax"])
-        dec.sample(("draft", c2), qw, float(uni[j + 1, U_DRAFT]))
-        pw, pZ = sampling.softmax_weights(view.logits_at(j), T, w.top_k)
+        dec.sample(("draft", c2), qw, float(uni[j + 1, U_DRAFT]), qm)
+        pl = view.logits_at(j)
+        pw, pZ = sampling.softmax_weights(pl, T, w.top_k)
+        sm = min(qm, sampling.top_k_margin(pl, w.top_k))
         teacher[("accept", i)] = bool(recs[i]["accepted"])
-        ok = dec.accept(("accept", i), pw, pZ, qw, qZ, qd["draft"], float(uni[j + 1, U_ACCEPT]))
+        ok = dec.accept(("accept", i), pw, pZ, qw, qZ, qd["draft"], float(uni[j + 1, U_ACCEPT]), sm)
         if not ok:
             teacher[("resample", i)] = int(recs[i]["target_token"])
-            dec.sample(("resample", i), sampling.residual(pw, pZ, qw, qZ), float(uni[j + 1, U_RESAMPLE]))
+            dec.sample(("resample", i), sampling.residual(pw, pZ, qw, qZ), float(uni[j + 1, U_RESAMPLE]), sm)
     dec.checked = len(chosen)
     return dec
 

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_sizes_match_header_layout():
     # spd_cycle_rec: 12 words + 64 KV lengths
     assert ctypes.sizeof(A.spd_cycle_rec) == 4 * (12 + A.SPD_MAX_LAYERS) == REC_DTYPE.itemsize
-    assert ctypes.sizeof(A.spd_config) == 4 * (10 + A.SPD_MAX_ANCHORS + 4 + 3 + 1)
+    assert ctypes.sizeof(A.spd_config) == 4 * (10 + A.SPD_MAX_ANCHORS + 4 + 3 + 2)
     assert ctypes.sizeof(A.spd_weights) == 8 * (1 + 6 * A.SPD_MAX_LAYERS + 2 + A.SPD_MAX_ANCHORS
                                                 + 6 * A.SPD_MAX_PDM_LAYERS + 2)
 
@@ -102,3 +102,20 @@ def test_vocab_limit():
     with pytest.raises(A.SPDError) as e:
         A.spd_workspace_bytes(c)
     assert e.value.code == A.SPD_EINVAL
+
+
+def test_top_k_limits():
+    """top_k within [0, min(SPD_MAX_TOPK, vocab)]; a schedule outside SPD_SCHED_* is rejected."""
+    c = make_config(si.workload("9b_sample"))
+    for k in (0, 1, 50, A.SPD_MAX_TOPK):
+        c.top_k = k
+        assert A.spd_workspace_bytes(c) > 0
+    for k in (-1, A.SPD_MAX_TOPK + 1):
+        c.top_k = k
+        with pytest.raises(A.SPDError) as e:
+            A.spd_workspace_bytes(c)
+        assert e.value.code == A.SPD_EINVAL
+    c.top_k = 0
+    c.schedule = 2
+    with pytest.raises(A.SPDError):
+        A.spd_workspace_bytes(c)

@@ -19,7 +19,7 @@ from tests import full_size as fs
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = ["4b_n8", "9b_n8", "4b_n16", "9b_sample", "4b_n8_post"]
+WORKLOADS = ["4b_n8", "9b_n8", "4b_n16", "9b_sample", "4b_n8_post", "9b_sample_topk50"]
 PARTS = ["replay", "verifications", "draft_module_and_floats"]
 _C = {}
 
@@ -66,7 +66,10 @@ def test_full_size(name, part):
         print(f"{name}: {len(recs)} cycles, {len(ex)} verifications, {R} rejections")
         assert len(ex) == w.G - 1
         assert len(recs) == schedule.cycle_count(w.n, w.G, R)
-        assert (ex["accepted"] == 1).any() and (ex["accepted"] == 0).any()
+        assert (ex["accepted"] == 0).any()
+        # random-init top-50 sets of P and Q over 151936 ids are (almost)
+        # disjoint: drafts are then (almost) never accepted
+        assert (ex["accepted"] == 1).any() or w.top_k > 0
         # each exit verifies the next position: the output is the first token and the exits' tokens
         assert [q["exit_pos"] for q in reps if q["exit_pos"] >= 0] == list(range(w.P, w.P + w.G - 1))
         assert run["toks"][w.P:w.P + w.G] == [run["first"]] + [q["y"] for q in reps if q["exit_pos"] >= 0]
