@@ -122,7 +122,10 @@ extern "C" {
  * increasing with anchors[0] == 0 and anchors[n_anchors-1] <= n_layers;
  * n_heads % n_kv_heads == 0; head_dim in {64, 128}; d_model, d_ffn and
  * n_heads*head_dim multiples of 256; max_ctx <= 32768; 2 <= vocab <=
- * SPD_MAX_VOCAB; schedule one of SPD_SCHED_*; 0 <= top_k <= min(SPD_MAX_TOPK, vocab).
+ * SPD_MAX_VOCAB; schedule one of SPD_SCHED_* (SPD_SCHED_POST needs n_stages >= 2);
+ * 0 <= top_k <= min(SPD_MAX_TOPK, vocab).  With n_stages = 1 every token exits in
+ * the cycle it enters and verifies the draft made in that cycle: the draft
+ * module then runs ahead of the stage step on the stage stream.
  */
 typedef struct spd_config {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab;

@@ -160,6 +160,9 @@ class SPDOracle:
         self.pdm = PDM(w, W)
         self.sample = w.mode == "sample"
         self.post = getattr(w, "schedule", "pre") == "post"
+        if self.post and w.n < 2:
+            raise ValueError("the post-step schedule needs n >= 2: with one stage the draft "
+                             "would come after its own verification")
         self.T = w.temperature
         self.top_k = getattr(w, "top_k", 0)
         self.policy = policy or NaturalPolicy()
@@ -266,6 +269,8 @@ class SPDOracle:
             else:
                 y = self.dec.argmax(("y", c), lg)
                 accept = int(xd == y)
+            if len(self.tokens) <= j + 1:  # n = 1: the successor was drafted this cycle
+                self.tokens.extend([-1] * (j + 2 - len(self.tokens)))
             self.tokens[j + 1] = int(y)
             self.emitted += 1
             if not post:

@@ -69,6 +69,9 @@ bool valid_config(const spd_config* c) {
   if (align_up((size_t)c->max_ctx, kSplit) / kSplit > (size_t)kMaxSplit) return false;
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 1.f)) return false;
   if (c->schedule != SPD_SCHED_PRE && c->schedule != SPD_SCHED_POST) return false;
+  // one stage: the exiting token verifies the draft made in its own cycle,
+  // which the post-step schedule would make only after that verification
+  if (c->schedule == SPD_SCHED_POST && c->n_stages < 2) return false;
   if (c->top_k < 0 || c->top_k > SPD_MAX_TOPK || c->top_k > c->vocab) return false;
   return true;
 }
@@ -843,8 +846,11 @@ int enqueue_cycle(spd_t* h) {
   // stage step (it reads only pre-step state, so the result is unchanged).
   // Post-step schedule: it reads the stage step's output and the verdict, so
   // it follows them on the stage stream.
+  // One stage (n = 1): the token entering a cycle also exits in it and
+  // verifies the draft made in the same cycle, so the draft chain goes
+  // first on the stage stream as well.
   const bool post = g.post != 0;
-  if (h->serialized || post) ps = ss;
+  if (h->serialized || post || g.n == 1) ps = ss;
   hipEvent_t e_start = nullptr, e_stage = nullptr, e_pdm_t = nullptr;
   if (h->timing) {
     e_start = pool_event(h);

@@ -119,3 +119,13 @@ def test_top_k_limits():
     c.schedule = 2
     with pytest.raises(A.SPDError):
         A.spd_workspace_bytes(c)
+
+
+def test_post_step_needs_two_stages():
+    c = make_config(si.workload("4b_n8"))
+    c.n_layers, c.n_stages, c.pdm_layers, c.n_anchors = 4, 1, 1, 2
+    c.anchors[0], c.anchors[1] = 0, 4
+    assert A.spd_workspace_bytes(c) > 0
+    c.schedule = A.SPD_SCHED_POST
+    with pytest.raises(A.SPDError):
+        A.spd_workspace_bytes(c)

@@ -167,3 +167,9 @@ def test_post_incremental_pdm_equals_full_recompute(mi):
     o.hook = hook
     o.run(prompt, w.G)
     assert len(checked) == len(o.logs)
+
+
+def test_post_step_needs_two_stages():
+    w, W, prompt, u = _setup(G=6, L=4, n=1, Ls=1, anchors=[0, 2, 4], seed=25)
+    with pytest.raises(ValueError):
+        SPDOracle(w.replace(schedule="post"), W, uniforms=u)

@@ -25,6 +25,8 @@ MODELS = [
     dict(L=8, n=4, Ls=2, anchors=[0, 2, 4, 6, 7], Hq=4, Hkv=4, seed=14, dtype="bf16"),
     dict(L=8, n=8, Ls=1, anchors=[0, 3, 8], Hq=6, Hkv=3, seed=15, norm_gain="random"),
     dict(L=6, n=2, Ls=3, anchors=[0, 5], Hq=2, Hkv=1, seed=16, dtype="bf16"),
+    # one stage: every token exits in the cycle it enters (one token per cycle)
+    dict(L=4, n=1, Ls=2, anchors=[0, 2, 4], Hq=2, Hkv=1, seed=17),
 ]
 
 
