@@ -83,7 +83,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="4b_n8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-cycles", type=int, default=64)
+    ap.add_argument("--cpu-cycles", type=int, default=192)
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host in the timed region (no HIP graphs)")
     ap.add_argument("--serialized", action="store_true",

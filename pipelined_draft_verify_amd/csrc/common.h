@@ -81,6 +81,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <>
 struct WVec<uint16_t> {
   static constexpr int N = 8;
+  typedef u32x4 Raw;
+  __device__ __forceinline__ static Raw ld(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  __device__ __forceinline__ static void cvt(const Raw& v, float* out) {
+    out[0] = __uint_as_float(v.x << 16);
+    out[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    out[2] = __uint_as_float(v.y << 16);
+    out[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    out[4] = __uint_as_float(v.z << 16);
+    out[5] = __uint_as_float(v.z & 0xFFFF0000u);
+    out[6] = __uint_as_float(v.w << 16);
+    out[7] = __uint_as_float(v.w & 0xFFFF0000u);
+  }
   __device__ __forceinline__ static void load(const uint16_t* p, float* out) {
     u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     out[0] = __uint_as_float(v.x << 16);
@@ -96,6 +110,16 @@ struct WVec<uint16_t> {
 template <>
 struct WVec<float> {
   static constexpr int N = 4;
+  typedef f32x4 Raw;
+  __device__ __forceinline__ static Raw ld(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  }
+  __device__ __forceinline__ static void cvt(const Raw& v, float* out) {
+    out[0] = v.x;
+    out[1] = v.y;
+    out[2] = v.z;
+    out[3] = v.w;
+  }
   __device__ __forceinline__ static void load(const float* p, float* out) {
     f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
     out[0] = v.x;

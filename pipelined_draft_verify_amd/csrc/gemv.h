@@ -92,6 +92,22 @@ struct StageGemv {
 // instead of being staged in LDS -- for un-normalised long inputs (the down
 // projection), so that the kernel holds no LDS and the draft stream's kernels
 // can share its CUs.  The arithmetic is the same either way.
+// One k-step of four weight rows: fp32 FMAs in element order into acc[r].
+template <typename WT>
+__device__ __forceinline__ void gemv_step(const typename WVec<WT>::Raw* rw, const float* x, float* acc) {
+  constexpr int VEC = WVec<WT>::N;
+  float xv[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) xv[e] = x[e];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float w[VEC];
+    WVec<WT>::cvt(rw[r], w);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[r] = fmaf(w[e], xv[e], acc[r]);
+  }
+}
+
 template <typename WT, int EPI, bool XG = false>
 __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
   extern __shared__ float xs_lds[];  // [K] (unless XG)
@@ -190,18 +206,26 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
     const WT* p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = W + (size_t)rows[r] * A.K;
-#pragma unroll 2
-    for (int k0 = lane * VEC; k0 < A.K; k0 += kWave * VEC) {
-      float wv[4][VEC];
+    // two k-steps per trip: the eight 16-byte weight loads are all issued
+    // before the first is used; the odd last step (if any) likewise
+    constexpr int kStep = kWave * VEC;
+    int k0 = lane * VEC;
+    for (; k0 + kStep < A.K; k0 += 2 * kStep) {
+      typename WVec<WT>::Raw ra[4], rb[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) WVec<WT>::load(p[r] + k0, wv[r]);
-      float xv[VEC];
+      for (int r = 0; r < 4; ++r) ra[r] = WVec<WT>::ld(p[r] + k0);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) xv[e] = xs[k0 + e];
+      for (int r = 0; r < 4; ++r) rb[r] = WVec<WT>::ld(p[r] + k0 + kStep);
+      __builtin_amdgcn_sched_barrier(0);
+      gemv_step<WT>(ra, xs + k0, acc);
+      gemv_step<WT>(rb, xs + k0 + kStep, acc);
+    }
+    if (k0 < A.K) {
+      typename WVec<WT>::Raw ra[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[r] = fmaf(wv[r][e], xv[e], acc[r]);
+      for (int r = 0; r < 4; ++r) ra[r] = WVec<WT>::ld(p[r] + k0);
+      __builtin_amdgcn_sched_barrier(0);
+      gemv_step<WT>(ra, xs + k0, acc);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = wave_sum(acc[r]);
