@@ -81,3 +81,30 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
         p = p / p.sum(dtype=F32)
         out[h] = p @ V[:, kv, :]
     return out
+
+
+def elu_plus_one(x: np.ndarray) -> np.ndarray:
+    """phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise (> 0 everywhere)."""
+    x = np.asarray(x, F32)
+    return np.where(x > 0, x + F32(1), np.exp(np.minimum(x, F32(0)))).astype(F32)
+
+
+def linear_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """Causal linear attention of one query position over keys K, V.
+
+    The hybrid target's linear layers (reading: the textbook kernelised
+    attention, with feature map phi = elu + 1): query head h reads kv head
+    h // (Hq/Hkv) and returns sum_i w_i v_i / sum_i w_i with weights
+    w_i = phi(q_h) . phi(k_i) in place of the softmax scores -- no scale, no
+    normalisation beyond the weight sum.  q [Hq, hd]; K, V [T, Hkv, hd].
+    """
+    Hq, hd = q.shape
+    Hkv = K.shape[1]
+    grp = Hq // Hkv
+    out = np.empty((Hq, hd), dtype=F32)
+    pk = elu_plus_one(K)
+    for h in range(Hq):
+        kv = h // grp
+        w = pk[:, kv, :] @ elu_plus_one(q[h])
+        out[h] = (w @ V[:, kv, :]) / w.sum(dtype=F32)
+    return out

@@ -5,7 +5,8 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from .layers import F32, apply_rope, attention, bf16_round, rmsnorm, rope_cos_sin, rope_tables, silu
+from .layers import (F32, apply_rope, attention, bf16_round, elu_plus_one, linear_attention, rmsnorm,
+                     rope_cos_sin, rope_tables, silu)
 from .schedule import pattern, stage_layers
 
 
@@ -52,13 +53,24 @@ class _Shape:
         self.eps, self.base = w.eps, w.rope_base
         self.bf16 = w.dtype == "bf16"
         self.max_ctx = w.max_ctx
+        self.attn_period = getattr(w, "attn_period", 0)
+
+    def linear(self, layer: int) -> bool:
+        """Hybrid target ([RB] limitations, [TW] §11: each block of 4
+        layers holds 1 standard and 3 linear-attention layers).  Reading: with
+        period P, layer l uses full softmax attention iff l % P == P - 1 (the
+        last of each block), linear attention otherwise; P = 0: all full."""
+        P = self.attn_period
+        return P > 0 and layer % P != P - 1
 
 
-def layer_step(s: _Shape, lw, h: np.ndarray, pos: int, kv: KVCache, check_len: bool = True):
+def layer_step(s: _Shape, lw, h: np.ndarray, pos: int, kv: KVCache, check_len: bool = True,
+               linear: bool = False):
     """One decoder layer for one token at position `pos` (pre-norm, GQA, SwiGLU).
 
     Appends the token's k, v at index pos (asserting the cache holds exactly
-    positions 0..pos-1 when `check_len`) and attends over 0..pos.
+    positions 0..pos-1 when `check_len`) and attends over 0..pos (softmax
+    attention, or linear attention for a hybrid target's linear layers).
     """
     u = rmsnorm(h, lw["attn_norm"], s.eps)
     q, k, v = _qkv(lw, u, s.Hq, s.Hkv, s.hd)
@@ -68,12 +80,12 @@ def layer_step(s: _Shape, lw, h: np.ndarray, pos: int, kv: KVCache, check_len: b
         assert kv.length == pos, f"KV length {kv.length} != position {pos}"
     kv.write(pos, k, v)
     kv.length = pos + 1
-    o = attention(q, kv.K[: pos + 1], kv.V[: pos + 1])
+    o = (linear_attention if linear else attention)(q, kv.K[: pos + 1], kv.V[: pos + 1])
     h = h + lw["w_o"] @ o.reshape(-1)
     return _ffn(lw, h, s.F, s.eps)
 
 
-def layer_rows(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache) -> np.ndarray:
+def layer_rows(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache, linear: bool = False) -> np.ndarray:
     """One decoder layer over M consecutive positions pos0..pos0+M-1 (causal).
 
     Row i attends to cached positions 0..pos0-1 and to rows 0..i.  The rows'
@@ -91,13 +103,13 @@ def layer_rows(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache) -> np.ndarr
     out = np.empty_like(X)
     for i in range(M):
         p = pos0 + i
-        o = attention(Q[i], kv.K[: p + 1], kv.V[: p + 1])
+        o = (linear_attention if linear else attention)(Q[i], kv.K[: p + 1], kv.V[: p + 1])
         h = X[i] + lw["w_o"] @ o.reshape(-1)
         out[i] = _ffn(lw, h, s.F, s.eps)
     return out
 
 
-def layer_matrix(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache) -> np.ndarray:
+def layer_matrix(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache, linear: bool = False) -> np.ndarray:
     """`layer_rows` written with matrix products over all M rows at once.
 
     The same definition (row i attends to cached positions and rows <= i,
@@ -130,6 +142,13 @@ def layer_matrix(s: _Shape, lw, X: np.ndarray, pos0: int, kv: KVCache) -> np.nda
     for h in range(Hq):
         k_ = torch.from_numpy(np.ascontiguousarray(kv.K[:T, h // grp, :]))
         v_ = torch.from_numpy(np.ascontiguousarray(kv.V[:T, h // grp, :]))
+        if linear:
+            # linear attention: weights phi(q).phi(k), masked to 0, normalised by their sum
+            Wt = (torch.from_numpy(np.ascontiguousarray(elu_plus_one(Q[:, h, :])))
+                  @ torch.from_numpy(np.ascontiguousarray(elu_plus_one(kv.K[:T, h // grp, :]))).T)
+            Wt.masked_fill_(mask, 0.0)
+            O[:, h, :] = ((Wt @ v_) / Wt.sum(dim=1, keepdim=True)).numpy()
+            continue
         S = (torch.from_numpy(np.ascontiguousarray(Q[:, h, :])) @ k_.T) * float(scale)
         S.masked_fill_(mask, float("-inf"))
         O[:, h, :] = (torch.softmax(S, dim=1) @ v_).numpy()
@@ -158,7 +177,7 @@ class Target:
                    taps: Optional[List] = None) -> np.ndarray:
         """Run `layers` for one token; record anchors h^(b) into `taps`."""
         for l in layers:
-            h = layer_step(self.s, self.W["layers"][l], h, pos, self.kv[l])
+            h = layer_step(self.s, self.W["layers"][l], h, pos, self.kv[l], linear=self.s.linear(l))
             if taps is not None and (l + 1) in self.anchor_at:
                 taps[self.anchor_at[l + 1]] = h.copy()
         return h
@@ -201,7 +220,7 @@ class Target:
         for l in range(self.s.L):
             kv = self.kv[l]
             assert kv.length == 0
-            H = layer_matrix(self.s, self.W["layers"][l], H, 0, kv)
+            H = layer_matrix(self.s, self.W["layers"][l], H, 0, kv, linear=self.s.linear(l))
             kv.length = P
             if (l + 1) in self.anchor_at:
                 for p in range(P):

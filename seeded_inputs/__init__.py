@@ -59,6 +59,7 @@ class Workload:
     norm_gain: str = "ones"  # "ones" or "random" (1 + 0.1 N(0,1), for tests)
     schedule: str = "pre"   # draft-module features: "pre" (before the stage step) or "post"
     top_k: int = 0          # sample mode: keep the k largest logits (0: the whole vocabulary)
+    attn_period: int = 0    # hybrid target: layer l is softmax attention iff l % P == P-1, else linear (0: all softmax)
 
     @property
     def max_ctx(self) -> int:
