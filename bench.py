@@ -44,18 +44,25 @@ def cycle_bytes(w, rec, es):
     qkv = (w.Hq + 2 * w.Hkv) * w.hd
     W_layer = (qkv * d + d * w.Hq * w.hd + 2 * F * d + d * F) * es
     kv_pos = 2 * w.Hkv * w.hd * es
+    P_attn = getattr(w, "attn_period", 0)
+    lin_state = 2 * w.Hkv * (w.hd * w.hd + w.hd) * 4  # a linear layer reads and writes its fp32 state
     t, a = int(rec["t"]), int(rec["occupancy"])
     b = a * per * W_layer
     for k in range(a):
-        b += per * (t - k + 1) * kv_pos
+        for l in range(k * per, (k + 1) * per):
+            linear = P_attn > 0 and l % P_attn != P_attn - 1
+            b += lin_state if linear else (t - k + 1) * kv_pos
     if rec["exit_pos"] >= 0:
         b += V * d * es
     # draft module: FC patterns present, Ls layers, head, KV reads
     def pattern(k):  # last anchor b_i <= min(L, k L/n)
         return max(i for i, bb in enumerate(w.anchors) if bb <= min(L, k * per))
-    pats = {pattern(k) for k in range(a)}
-    if rec["pending_row"]:
-        pats.add(pattern(n))
+    if getattr(w, "schedule", "pre") == "post":
+        pats = {pattern(k) for k in range(1, a + 1)}  # rows at depths a .. 1
+    else:
+        pats = {pattern(k) for k in range(a)}
+        if rec["pending_row"]:
+            pats.add(pattern(n))
     b += sum((f + 1) * d * d * es for f in pats)
     b += w.Ls * W_layer + V * d * es
     b += w.Ls * (t + 1) * kv_pos

@@ -141,6 +141,14 @@ typedef struct spd_config {
   float rope_base;    /* RoPE base */
   float temperature;  /* sample mode only */
   int32_t schedule;   /* SPD_SCHED_* */
+  int32_t attn_period; /* hybrid target ([RB] limitations, [TW] §11: one standard and three
+                          linear-attention layers per block of four): layer l uses softmax
+                          attention iff attn_period == 0 or l % attn_period == attn_period - 1,
+                          else causal linear attention with feature map elu + 1 over the same
+                          q/k/v (o = phi(q)^T S / phi(q)^T z, S = sum phi(k) v^T, z = sum phi(k),
+                          per kv head, fp32 state).  0 <= attn_period <= n_layers.  With linear
+                          layers spd_rollback accepts only lengths whose state is still held:
+                          the last n_stages + 1 positions, or the prefill length. */
   int32_t top_k;      /* sample mode: only the top_k largest logits keep their weight, in the
                          target's P and the draft module's Q alike (equal logits rank by the lower
                          id; selection before the temperature); 0 = the whole vocabulary.

@@ -58,6 +58,7 @@ __device__ __forceinline__ bool attn_problem(const Attn& A, int z, int& pos0, in
   const Ctrl* C = A.ctrl;
   if (A.pmode == PM_STAGE) {
     if (!C->active || z >= C->a) return false;
+    if (layer_is_linear(A.g, A.layer[z])) return false;  // the linear-attention kernel's group
     pos0 = C->t - z;
     nrows = 1;
     layer = A.layer[z];
@@ -486,6 +487,7 @@ __global__ __launch_bounds__(HD) void k_attn_merge(const Attn A) {
   int pos;
   if (A.pmode == PM_STAGE) {
     if (!C->active || prow >= C->a) return;
+    if (layer_is_linear(g, A.layer[prow])) return;  // written by the linear-attention kernel
     pos = C->t - prow;
   } else {
     int pos0, nrows;

@@ -214,10 +214,18 @@ struct Geo {
   int max_ctx;   // positions must stay below this (uniform-table rows, KV capacity)
   int post;      // draft module on post-step features (SPD_SCHED_POST)
   int topk;      // sample mode: top-k truncation of P and Q (0: none)
+  int attn_period;  // hybrid target: softmax attention iff layer % P == P - 1, else linear (0: all softmax)
   float eps;
   int anchor_of_layer[SPD_MAX_LAYERS + 1];  // anchor index of boundary b, or -1
   int fpat[SPD_MAX_STAGES + 1];             // f(k) for k = 0..n
 };
+
+// Hybrid target ([RB] limitations, [TW] §11: one standard and three linear
+// attention layers per block of four): layer l is a linear-attention layer
+// unless attn_period is 0 or l is the last layer of its block.
+__device__ __host__ __forceinline__ bool layer_is_linear(const Geo& g, int layer) {
+  return g.attn_period > 0 && (layer % g.attn_period) != g.attn_period - 1;
+}
 
 // Depth (stages completed) of the feature of draft-module row i, position p.
 // Pre-step ([PL] §3.3): the just-verified row (pending) at depth n, in-flight

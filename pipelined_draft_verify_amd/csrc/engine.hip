@@ -22,6 +22,7 @@
 #include "common.h"
 #include "control.h"
 #include "gemv.h"
+#include "linattn.h"
 #include "mfma.h"
 
 using namespace spd;
@@ -40,6 +41,7 @@ struct Layout {
   size_t Xt, Xp, r_q, r_pacc, r_pml, r_o, r_act, taps;
   size_t logits, plogits, pw, parts, pparts, ring;
   size_t ssq_t, ssq_p, mpart;
+  size_t lin_state, lin_ckpt;
   size_t total;
   int ctx_cap, nsplit, mr, log_cap, nparts_max;
 };
@@ -73,6 +75,7 @@ bool valid_config(const spd_config* c) {
   // which the post-step schedule would make only after that verification
   if (c->schedule == SPD_SCHED_POST && c->n_stages < 2) return false;
   if (c->top_k < 0 || c->top_k > SPD_MAX_TOPK || c->top_k > c->vocab) return false;
+  if (c->attn_period < 0 || c->attn_period > c->n_layers) return false;
   return true;
 }
 
@@ -175,6 +178,11 @@ Layout make_layout(const spd_config* c) {
     pf = std::max(pf, mfma_part_floats(d, full, 1, rows));
   }
   L.mpart = take(sizeof(float) * std::max<size_t>(pf, 1));
+  // hybrid target: linear-attention state ring [L][nslots][Hkv][hd*hd + hd]
+  // and its copy at the end of prefill [L][Hkv][hd*hd + hd]
+  const size_t lin_one = (size_t)Hkv * ((size_t)hd * hd + hd);
+  L.lin_state = take(c->attn_period > 0 ? sizeof(float) * (size_t)c->n_layers * nslots * lin_one : 0);
+  L.lin_ckpt = take(c->attn_period > 0 ? sizeof(float) * (size_t)c->n_layers * lin_one : 0);
   L.total = off;
   return L;
 }
@@ -201,6 +209,10 @@ struct spd_handle {
   ArgPair *parts, *pparts;
   spd_cycle_rec* ring;
   float *ssq_t, *ssq_p, *mpart;
+  float *lin_state = nullptr, *lin_ckpt = nullptr;
+  int ckpt_len = 0;     // prefill length whose linear-attention states lin_ckpt holds
+  int lin_newest = -1;  // newest position whose linear-attention state a row pass wrote
+  int lin_keep_from = 0;
   int policy = SPD_DRAFT_NATURAL;
   float p_accept = 0.f;
   const int32_t* ref = nullptr;
@@ -338,6 +350,34 @@ hipError_t attn_lds_limits() {
   return e;
 }
 
+// Linear attention of a hybrid target's layer over consecutive rows (prefill
+// chunk or autoregressive token), output fp32 rows r_o.
+template <typename WT>
+void rows_linattn(spd_t* h, int layer, int M, int pos0, hipStream_t s) {
+  const Geo& g = h->g;
+  LinAttn t;
+  memset(&t, 0, sizeof(t));
+  t.mode = LM_ROWS;
+  t.layer[0] = layer;
+  t.kc = h->kc;
+  t.vc = h->vc;
+  t.q = h->r_q;
+  t.ldq = g.Hq * g.hd;
+  t.o = h->r_o;
+  t.ldo = g.Hq * g.hd;
+  t.state = h->lin_state;
+  t.pos0 = pos0;
+  t.nrows = M;
+  t.keep_from = h->lin_keep_from;
+  t.ctrl = h->ctrl;
+  t.g = g;
+  if (g.hd == 128)
+    hipLaunchKernelGGL((k_linattn<WT, 128>), dim3(g.Hkv, 1), dim3(kWG), 0, s, t);
+  else
+    hipLaunchKernelGGL((k_linattn<WT, 64>), dim3(g.Hkv, 1), dim3(kWG), 0, s, t);
+  h->lin_newest = std::max(h->lin_newest, pos0 + M - 1);
+}
+
 // Attention over row-batched queries (prefill chunk, AR token or the draft
 // module's trailing rows); output fp32 rows r_o.
 template <typename WT>
@@ -378,7 +418,8 @@ void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, in
 // matches the stage kernels bit for bit).
 template <typename WT>
 void rows_layer(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int layer, float* X, int M,
-                int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s) {
+                int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s,
+                bool linear = false) {
   const Geo& g = h->g;
   const int max_rows = from_ctrl ? g.n + 1 : M;
   const int qd = g.Hq * g.hd;
@@ -401,7 +442,10 @@ void rows_layer(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int l
   a.vc = vc;
   a.kv_len = kv_len;
   launch_rows<WT, EPI_QKV>(h, a, max_rows, s);
-  rows_attention<WT>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, true, s);
+  if (linear)
+    rows_linattn<WT>(h, layer, M, pos0, s);
+  else
+    rows_attention<WT>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, true, s);
   // output projection + residual
   a = rows_base(h);
   a.from_ctrl = from_ctrl;
@@ -486,7 +530,8 @@ void launch_mfma(spd_t* h, MfmaArgs a, int nprob, int max_rows, hipStream_t s) {
 // trailing rows and prefill chunks.  X rows are updated in place; ssqX holds
 // their per-row partial sums of squares (written by whoever wrote X).
 void rows_layer_mfma(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int layer, float* X, float* ssqX,
-                     int M, int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s) {
+                     int M, int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s,
+                     bool linear = false) {
   const Geo& g = h->g;
   const int max_rows = from_ctrl ? g.n + 1 : M;
   const int qd = g.Hq * g.hd;
@@ -510,16 +555,26 @@ void rows_layer_mfma(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, 
   a.vc = vc;
   a.kv_len = kv_len;
   launch_mfma<EPI_QKV>(h, a, 1, max_rows, s);
-  // attention splits; the output projection merges them as it stages its input
-  rows_attention<uint16_t>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, false, s);
+  // attention splits; the output projection merges them as it stages its
+  // input (linear attention writes its rows whole)
+  if (linear)
+    rows_linattn<uint16_t>(h, layer, M, pos0, s);
+  else
+    rows_attention<uint16_t>(h, kc, vc, layer, M, pos0, from_ctrl, max_rows, false, s);
   // output projection + residual
   a.kv_len = nullptr;
   a.W[0] = (const uint16_t*)lw.w_o;
   a.K[0] = qd;
   a.N = g.d;
-  a.rmode = RM_ATTN;
-  a.apacc = h->r_pacc;
-  a.apml = h->r_pml;
+  if (linear) {
+    a.rmode = RM_CONTIG;
+    a.x = h->r_o;
+    a.ldx = qd;
+  } else {
+    a.rmode = RM_ATTN;
+    a.apacc = h->r_pacc;
+    a.apml = h->r_pml;
+  }
   a.gamma = nullptr;
   a.ssq = nullptr;
   a.out = X;
@@ -558,11 +613,11 @@ void rows_layer_mfma(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, 
 template <typename WT>
 void layer_rows_any(spd_t* h, bool mfma, const spd_layer_weights& lw, void* kc, void* vc, int layer, float* X,
                     float* ssqX, int M, int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx,
-                    hipStream_t s) {
+                    hipStream_t s, bool linear = false) {
   if (mfma && sizeof(WT) == 2)
-    rows_layer_mfma(h, lw, kc, vc, layer, X, ssqX, M, pos0, from_ctrl, kv_len, taps, anchor_idx, s);
+    rows_layer_mfma(h, lw, kc, vc, layer, X, ssqX, M, pos0, from_ctrl, kv_len, taps, anchor_idx, s, linear);
   else
-    rows_layer<WT>(h, lw, kc, vc, layer, X, M, pos0, from_ctrl, kv_len, taps, anchor_idx, s);
+    rows_layer<WT>(h, lw, kc, vc, layer, X, M, pos0, from_ctrl, kv_len, taps, anchor_idx, s, linear);
 }
 
 // Head GEMV (final norm + LM head + per-workgroup argmax) on a fixed input row.
@@ -708,7 +763,30 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     t.o = h->s_o;
     t.ctrl = h->ctrl;
     t.g = g;
-    attention_any<WT>(t, dim3(g.nsplit, g.Hkv, g.n), 1, g.n, ss);
+    // a hybrid target's sub-step may hold softmax and linear layers: each
+    // kernel takes its own groups (the layer types are fixed per sub-step)
+    bool any_soft = false, any_lin = false;
+    for (int k = 0; k < g.n; ++k) (layer_is_linear(g, a.layer[k]) ? any_lin : any_soft) = true;
+    if (any_soft) attention_any<WT>(t, dim3(g.nsplit, g.Hkv, g.n), 1, g.n, ss);
+    if (any_lin) {
+      LinAttn la;
+      memset(&la, 0, sizeof(la));
+      la.mode = LM_STAGE;
+      for (int k = 0; k < g.n; ++k) la.layer[k] = a.layer[k];
+      la.kc = h->kc;
+      la.vc = h->vc;
+      la.q = h->s_q;
+      la.ldq = qd;
+      la.o = h->s_o;
+      la.ldo = qd;
+      la.state = h->lin_state;
+      la.ctrl = h->ctrl;
+      la.g = g;
+      if (g.hd == 128)
+        hipLaunchKernelGGL((k_linattn<WT, 128>), dim3(g.Hkv, g.n), dim3(kWG), 0, ss, la);
+      else
+        hipLaunchKernelGGL((k_linattn<WT, 64>), dim3(g.Hkv, g.n), dim3(kWG), 0, ss, la);
+    }
     // output projection + residual
     StageGemv o = stage_base(h);
     o.n_groups = g.n;
@@ -904,13 +982,14 @@ int do_prefill(spd_t* h, int P) {
   const Geo& g = h->g;
   const spd_weights& w = h->w;
   hipStream_t s = h->ss;
+  h->lin_keep_from = P - g.nslots;
   for (int s0 = 0; s0 < P; s0 += kRowsMR) {
     const int M = std::min(kRowsMR, P - s0);
     hipLaunchKernelGGL((k_embed_rows<WT>), dim3(M), dim3(kWG), 0, s, h->tokens, s0, (const WT*)w.embed, g.d, h->Xt,
                        h->taps, g.m, h->ssq_t);
     for (int l = 0; l < g.L; ++l)
       layer_rows_any<WT>(h, true, w.layers[l], h->kc, h->vc, l, h->Xt, h->ssq_t, M, s0, 0, h->kv_len, h->taps,
-                         g.anchor_of_layer[l + 1], s);
+                         g.anchor_of_layer[l + 1], s, layer_is_linear(g, l));
     // draft module prefill on the full-depth features of the chunk
     if (sizeof(WT) == 2) {
       MfmaArgs a = mfma_base(h);
@@ -949,6 +1028,17 @@ int do_prefill(spd_t* h, int P) {
                          &h->ctrl->flags);
     }
   }
+  // linear-attention states after the prompt: a rollback to this length
+  // (after an autoregressive run past the ring) restores them from here
+  if (g.attn_period > 0) {
+    const size_t one = (size_t)g.Hkv * ((size_t)g.hd * g.hd + g.hd);
+    for (int l = 0; l < g.L; ++l)
+      if (layer_is_linear(g, l))
+        HIPCHK(h, hipMemcpyAsync(h->lin_ckpt + (size_t)l * one,
+                                 h->lin_state + lin_state_index(g, l, (P - 1) % g.nslots, 0), one * sizeof(float),
+                                 hipMemcpyDeviceToDevice, s));
+    h->ckpt_len = P;
+  }
   HIPCHK(h, hipGetLastError());
   return SPD_OK;
 }
@@ -962,8 +1052,10 @@ int do_ar(spd_t* h, int s0, int n) {
     const int pos = s0 + i;
     hipLaunchKernelGGL((k_embed_rows<WT>), dim3(1), dim3(kWG), 0, s, h->tokens, pos, (const WT*)w.embed, g.d,
                        h->Xt, (float*)nullptr, g.m, (float*)nullptr);
+    h->lin_keep_from = pos;
     for (int l = 0; l < g.L; ++l)
-      rows_layer<WT>(h, w.layers[l], h->kc, h->vc, l, h->Xt, 1, pos, 0, h->kv_len, nullptr, -1, s);
+      rows_layer<WT>(h, w.layers[l], h->kc, h->vc, l, h->Xt, 1, pos, 0, h->kv_len, nullptr, -1, s,
+                     layer_is_linear(g, l));
     const int grid = head_fixed<WT>(h, h->Xt, w.lm_head, w.final_norm, h->logits, h->parts, s);
     hipLaunchKernelGGL(k_pick_token, dim3(1), dim3(kCtlThreads), 0, s, h->parts, grid, h->logits, h->pw, g.V,
                        SPD_MODE_GREEDY, 1.0f, 0, h->uni, h->tokens, pos + 1, (Ctrl*)nullptr, &h->ctrl->flags);
@@ -1052,6 +1144,7 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   g.max_ctx = cfg->max_ctx;
   g.post = cfg->schedule == SPD_SCHED_POST ? 1 : 0;
   g.topk = cfg->mode == SPD_MODE_SAMPLE ? cfg->top_k : 0;
+  g.attn_period = cfg->attn_period;
   g.eps = cfg->rms_eps;
   for (int b = 0; b <= SPD_MAX_LAYERS; ++b) g.anchor_of_layer[b] = -1;
   for (int i = 0; i < g.m; ++i) g.anchor_of_layer[cfg->anchors[i]] = i;
@@ -1102,6 +1195,10 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   h->ssq_t = (float*)(ws + L.ssq_t);
   h->ssq_p = (float*)(ws + L.ssq_p);
   h->mpart = (float*)(ws + L.mpart);
+  if (cfg->attn_period > 0) {
+    h->lin_state = (float*)(ws + L.lin_state);
+    h->lin_ckpt = (float*)(ws + L.lin_ckpt);
+  }
 
   auto fail = [&](hipError_t e) {
     h->hip_err = (int)e;
@@ -1257,7 +1354,23 @@ int spd_rollback(spd_t* h, int32_t keep_len, int32_t reseed_token) {
   } else if (C != keep_len) {
     return SPD_ESTATE;
   }
+  // hybrid target: the linear-attention state after keep_len - 1 must still
+  // be in its ring slot, or be the one kept at the end of prefill
+  const bool restore = h->g.attn_period > 0 && keep_len == h->ckpt_len;
+  if (h->g.attn_period > 0 && !restore) {
+    const int newest = std::max(h->lin_newest, c.t);
+    if (keep_len - 1 > newest || newest - (keep_len - 1) >= h->g.nslots) return SPD_ESTATE;
+  }
   if (keep_len < h->P) h->P = keep_len;
+  if (restore) {
+    const Geo& g = h->g;
+    const size_t one = (size_t)g.Hkv * ((size_t)g.hd * g.hd + g.hd);
+    for (int l = 0; l < g.L; ++l)
+      if (layer_is_linear(g, l))
+        HIPCHK(h, hipMemcpy(h->lin_state + lin_state_index(g, l, (keep_len - 1) % g.nslots, 0),
+                            h->lin_ckpt + (size_t)l * one, one * sizeof(float), hipMemcpyDeviceToDevice));
+  }
+  if (h->g.attn_period > 0) h->lin_newest = keep_len - 1;
   Ctrl n;
   memset(&n, 0, sizeof(n));
   n.t = keep_len - 1;

@@ -36,6 +36,7 @@ def make_config(w, max_ctx: Optional[int] = None) -> A.spd_config:
     c.rms_eps, c.rope_base, c.temperature = w.eps, w.rope_base, w.temperature
     c.schedule = A.SPD_SCHED_POST if getattr(w, "schedule", "pre") == "post" else A.SPD_SCHED_PRE
     c.top_k = getattr(w, "top_k", 0)
+    c.attn_period = getattr(w, "attn_period", 0)
     return c
 
 

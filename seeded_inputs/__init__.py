@@ -92,6 +92,11 @@ WORKLOADS: Dict[str, Workload] = {
     "9b_sample_topk50": Workload("9b_sample_topk50", "bf16", 32, 4096, 32, 8, 128, 12288, 151936, 8, 4,
                                  [0, 8, 16, 24, 31], P=2048, G=512, mode="sample",
                                  temperature=1.0, seed=5, top_k=50),
+    # 4b_n8 shapes as a hybrid target: one softmax layer per block of four,
+    # the others linear attention
+    "4b_hybrid_n8": Workload("4b_hybrid_n8", "bf16", 32, 2560, 20, 4, 128, 9728, 151936, 8, 4,
+                             [0, 8, 16, 24, 31], P=512, G=256, policy="forced",
+                             p_accept=0.8, seed=6, attn_period=4),
     # 4b_n8 with the draft module on post-step features (scheduling ablation)
     "4b_n8_post": Workload("4b_n8_post", "bf16", 32, 2560, 20, 4, 128, 9728, 151936, 8, 4,
                            [0, 8, 16, 24, 31], P=512, G=256, policy="forced",

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_sizes_match_header_layout():
     # spd_cycle_rec: 12 words + 64 KV lengths
     assert ctypes.sizeof(A.spd_cycle_rec) == 4 * (12 + A.SPD_MAX_LAYERS) == REC_DTYPE.itemsize
-    assert ctypes.sizeof(A.spd_config) == 4 * (10 + A.SPD_MAX_ANCHORS + 4 + 3 + 2)
+    assert ctypes.sizeof(A.spd_config) == 4 * (10 + A.SPD_MAX_ANCHORS + 4 + 3 + 3)
     assert ctypes.sizeof(A.spd_weights) == 8 * (1 + 6 * A.SPD_MAX_LAYERS + 2 + A.SPD_MAX_ANCHORS
                                                 + 6 * A.SPD_MAX_PDM_LAYERS + 2)
 
@@ -129,3 +129,14 @@ def test_post_step_needs_two_stages():
     c.schedule = A.SPD_SCHED_POST
     with pytest.raises(A.SPDError):
         A.spd_workspace_bytes(c)
+
+
+def test_attn_period_limits():
+    c = make_config(si.workload("4b_n8"))
+    for p in (0, 1, 4, 32):
+        c.attn_period = p
+        assert A.spd_workspace_bytes(c) > 0
+    for p in (-1, 33):
+        c.attn_period = p
+        with pytest.raises(A.SPDError):
+            A.spd_workspace_bytes(c)
