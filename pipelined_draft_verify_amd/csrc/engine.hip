@@ -520,7 +520,7 @@ void launch_mfma(spd_t* h, MfmaArgs a, int nprob, int max_rows, hipStream_t s) {
     if (split)
       hipLaunchKernelGGL((k_mfma_reduce<EPI, 1>), dim3(a.N / kMGroup, 16, nprob), dim3(kWave), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_mfma_gemv<EPI, 2>), grid, dim3(kWG), 0, s, a);
+    hipLaunchKernelGGL((k_mfma_gemv<EPI, 2, kMKC / 2>), grid, dim3(kWG), 0, s, a);
     if (split)
       hipLaunchKernelGGL((k_mfma_reduce<EPI, 2>), dim3(a.N / kMGroup, 32, nprob), dim3(kWave), 0, s, a);
   }

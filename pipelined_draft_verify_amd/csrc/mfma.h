@@ -10,7 +10,9 @@
 //
 // Work decomposition: a workgroup of four waves owns a 64-row group of W
 // (one 16-row MFMA tile per wave) and one of S consecutive K ranges; it walks
-// its range in chunks of kMKC.  Per chunk:
+// its range in chunks of KC = 256 (128 for two activation tiles, which keeps
+// the workgroup's LDS near 50 KB so that two or more fit on a CU beside the
+// stage kernels).  Per chunk:
 //  * each wave loads its 16 weight rows with row-contiguous 16-byte loads
 //    (the next chunk's loads are in flight while this one is multiplied) and
 //    re-lays them through LDS into the MFMA operand layout (lane l holds row
@@ -36,7 +38,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4m __attribute__((ext_vector_type(4)));
 
 constexpr int kMKC = 256;          // K per chunk
-constexpr int kMPad = kMKC + 8;    // LDS row pitch (elements): breaks bank aliasing of the 16 rows
 constexpr int kMGroup = 64;        // weight rows per workgroup
 constexpr int kMMaxSplit = 64;     // K ranges per product
 constexpr int kSsqCols = 64;       // columns per partial sum of squares
@@ -195,13 +196,15 @@ __device__ __forceinline__ void mfma_kv_len(const MfmaArgs& A, int M, int pos0, 
   *len = pos0 + rsrc[M - 1] + 1;
 }
 
-template <int EPI, int MT>
+template <int EPI, int MT, int KC = kMKC>
 __global__ __launch_bounds__(kWG) void k_mfma_gemv(const MfmaArgs A) {
-  constexpr int R = 16 * MT;  // activation rows per pass
-  __shared__ __align__(16) uint16_t bh[2][R][kMPad];
-  __shared__ __align__(16) uint16_t bl[2][R][kMPad];
-  __shared__ __align__(16) uint16_t wl[kWG / kWave][16][kMPad];
-  __shared__ float dt[R][kMGroup + 1];
+  constexpr int R = 16 * MT;    // activation rows per pass
+  constexpr int KP = KC + 8;    // LDS row pitch (elements): breaks bank aliasing of the 16 rows
+  static_assert(kMKC % KC == 0 && KC % 128 == 0, "chunks divide the split unit");
+  __shared__ __align__(16) uint16_t bh[2][R][KP];
+  __shared__ __align__(16) uint16_t bl[2][R][KP];
+  __shared__ __align__(16) uint16_t wl[kWG / kWave][16][KP];
+  static_assert(sizeof(bh) >= sizeof(float) * R * (kMGroup + 1), "the epilogue tile reuses bh");
   __shared__ float srstd[R];
   __shared__ int rsrc[R];
   __shared__ int s_M, s_pos0;
@@ -214,21 +217,25 @@ __global__ __launch_bounds__(kWG) void k_mfma_gemv(const MfmaArgs A) {
   const int K = A.K[prob];
   const int KR = K / S;
   const int kb = sp * KR;
-  const int nch = KR / kMKC;
+  const int nch = KR / KC;
   const Geo& g = A.g;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r = lane & 15, kq = lane >> 4;
 
   // weight loads of the first chunk go out before anything else
+  constexpr int LPR = KC / 8;        // lanes per weight row (8 bf16 each)
+  constexpr int RPI = kWave / LPR;   // weight rows per load instruction
+  constexpr int NI = 16 / RPI;       // load instructions per chunk
   const int tile = rg * 4 + wave;
-  const int lr = lane >> 5, lk = (lane & 31) * 8;  // instruction i: tile rows 2i + lr, k = lk..lk+7
+  const int lr = lane / LPR, lk = (lane % LPR) * 8;  // instruction i: tile rows RPI i + lr, k = lk..lk+7
   const uint16_t* W = A.W[prob];
-  const uint16_t* wrow[8];
+  const uint16_t* wrow[NI];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) wrow[i] = W + (size_t)mfma_tile_row<EPI>(g, A.N, tile, 2 * i + lr) * K + kb + lk;
-  u32x4 wr[8];
+  for (int i = 0; i < NI; ++i)
+    wrow[i] = W + (size_t)mfma_tile_row<EPI>(g, A.N, tile, RPI * i + lr) * K + kb + lk;
+  u32x4 wr[NI];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[i]));
+  for (int i = 0; i < NI; ++i) wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[i]));
 
   mfma_select_rows(A, prob, R, &s_M, &s_pos0, rsrc);
   __syncthreads();
@@ -263,14 +270,17 @@ __global__ __launch_bounds__(kWG) void k_mfma_gemv(const MfmaArgs A) {
   }
   __syncthreads();
 
-  // activation staging: thread t covers row t/16 (+16 per pass), 16 consecutive k
-  const int br = threadIdx.x >> 4, bk = (threadIdx.x & 15) * 16;
-  f32x4 xr[MT][4];
+  // activation staging: thread t covers row t/TPR (+RPP per pass), 16 consecutive k
+  constexpr int TPR = KC / 16;               // threads per activation row
+  constexpr int RPP = kWG / TPR;             // rows per staging pass
+  constexpr int NP = (R + RPP - 1) / RPP;    // staging passes
+  const int br = threadIdx.x / TPR, bk = (threadIdx.x % TPR) * 16;
+  f32x4 xr[NP][4];
   auto load_x = [&](int c) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = br + 16 * mt;
-      const int k = kb + c * kMKC + bk;
+    for (int mt = 0; mt < NP; ++mt) {
+      const int m = br + RPP * mt;
+      const int k = kb + c * KC + bk;
       if (m < M && A.rmode == RM_ATTN) {
         // merge the row's attention splits for the 16 dims k..k+15 (one head):
         // the same arithmetic, in split order, as the split-merge kernel
@@ -318,8 +328,9 @@ __global__ __launch_bounds__(kWG) void k_mfma_gemv(const MfmaArgs A) {
   };
   auto store_x = [&](int buf) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = br + 16 * mt;
+    for (int mt = 0; mt < NP; ++mt) {
+      const int m = br + RPP * mt;
+      if (m >= R) continue;
       uint16_t h[16], l[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -346,16 +357,16 @@ __global__ __launch_bounds__(kWG) void k_mfma_gemv(const MfmaArgs A) {
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&wl[wave][2 * i + lr][lk]) = wr[i];
+    for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(&wl[wave][RPI * i + lr][lk]) = wr[i];
     if (c + 1 < nch) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[i] + (c + 1) * kMKC));
+      for (int i = 0; i < NI; ++i)
+        wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[i] + (c + 1) * KC));
       load_x(c + 1);
     }
     __syncthreads();  // weights of chunk c and activations buffer `buf` are in LDS
 #pragma unroll
-    for (int s = 0; s < kMKC / 32; ++s) {
+    for (int s = 0; s < KC / 32; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&wl[wave][r][32 * s + 8 * kq]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -371,6 +382,7 @@ __global__ __launch_bounds__(kWG) void k_mfma_gemv(const MfmaArgs A) {
 
   // D lane layout: lane (r, kq) holds tile rows 4kq..4kq+3 of activation row 16mt + r
   if (S == 1) {
+    float (*dt)[kMGroup + 1] = reinterpret_cast<float (*)[kMGroup + 1]>(&bh[0][0][0]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
