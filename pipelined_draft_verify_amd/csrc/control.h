@@ -86,18 +86,17 @@ __device__ __forceinline__ void load4(const float* p, int v0, int V, bool vec, f
 __device__ __forceinline__ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Block sums of the weights given by w4(v0, x[4]) (the fp64 weights of ids
-// v0..v0+3, zero beyond V) into S.bs, then the superblock sums and the total.
-// Ends with a barrier; S.total is then valid in every thread.
+// v0..v0+3, zero beyond V) into bs: this wave takes blocks wave,
+// wave + nwaves, ... with kCdfUnroll of them in flight.
 template <typename W4>
-__device__ __forceinline__ void cdf_sums(W4 w4, int V, CdfShared& S) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+__device__ __forceinline__ void cdf_block_pass(W4 w4, int V, double* bs, int wave, int nwaves) {
+  const int lane = threadIdx.x & (kWave - 1);
   const int nb = (V + kCdfBlock - 1) / kCdfBlock;
-  const int nsb = (nb + kWave - 1) / kWave;
-  for (int b0 = wave; b0 < nb; b0 += kCtlWaves * kCdfUnroll) {
+  for (int b0 = wave; b0 < nb; b0 += nwaves * kCdfUnroll) {
     double x[kCdfUnroll][4];
 #pragma unroll
     for (int u = 0; u < kCdfUnroll; ++u) {
-      const int b = b0 + u * kCtlWaves;
+      const int b = b0 + u * nwaves;
       if (b < nb) {
         w4(b * kCdfBlock + lane * kCdfPer, x[u]);
       } else {
@@ -107,12 +106,19 @@ __device__ __forceinline__ void cdf_sums(W4 w4, int V, CdfShared& S) {
     }
 #pragma unroll
     for (int u = 0; u < kCdfUnroll; ++u) {
-      const int b = b0 + u * kCtlWaves;
+      const int b = b0 + u * nwaves;
       const double s = wave_scan_d(lane_sum4(x[u]));
-      if (lane == kWave - 1 && b < nb) S.bs[b] = s;
+      if (lane == kWave - 1 && b < nb) bs[b] = s;
     }
   }
-  __syncthreads();
+}
+
+// From the block sums in S.bs: superblock sums, their inclusive scan and the
+// total.  Ends with a barrier; S.total is then valid in every thread.
+__device__ __forceinline__ void cdf_super_sums(int V, CdfShared& S) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nb = (V + kCdfBlock - 1) / kCdfBlock;
+  const int nsb = (nb + kWave - 1) / kWave;
   for (int sb = wave; sb < nsb; sb += kCtlWaves) {
     const int b = sb * kWave + lane;
     const double s = wave_scan_d(b < nb ? S.bs[b] : 0.0);
@@ -125,6 +131,16 @@ __device__ __forceinline__ void cdf_sums(W4 w4, int V, CdfShared& S) {
     if (lane == nsb - 1) S.total = s;
   }
   __syncthreads();
+}
+
+// The whole pass in one workgroup: block sums into S.bs, then the superblock
+// sums and the total.  Ends with a barrier; S.total is then valid in every
+// thread.
+template <typename W4>
+__device__ __forceinline__ void cdf_sums(W4 w4, int V, CdfShared& S) {
+  cdf_block_pass(w4, V, S.bs, threadIdx.x / kWave, kCtlWaves);
+  __syncthreads();
+  cdf_super_sums(V, S);
 }
 
 // Highest set lane of a nonzero ballot.
@@ -236,31 +252,73 @@ __device__ __forceinline__ int cdf_draw(W4 w4, int V, double u, CdfShared& S) {
 // Softmax weights w_v = exp(l_v / T - max_v l_v / T) stored to `w` (fp32);
 // their block sums go to S and the fp64 total Z = sum_v w_v is returned.
 // `lmax` is max_v l_v.
+// The softmax weights of ids v0..v0+3 (stored to w, returned in x as fp64).
+struct SoftmaxWeights4 {
+  const float* logits;
+  float* w;
+  int V;
+  float T, mt;
+  bool vec;
+  __device__ void operator()(int v0, double x[4]) const {
+    float l[4];
+    load4(logits, v0, V, vec, l);
+    float e[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float lt = (T == 1.0f) ? l[k] : l[k] / T;
+      e[k] = (v0 + k < V) ? expf(lt - mt) : 0.f;
+      x[k] = (double)e[k];
+    }
+    if (vec && v0 + 4 <= V) {
+      *reinterpret_cast<f32x4*>(w + v0) = f32x4{e[0], e[1], e[2], e[3]};
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (v0 + k < V) w[v0 + k] = e[k];
+    }
+  }
+};
+__device__ __forceinline__ SoftmaxWeights4 softmax4(const float* logits, float* w, int V, float T, float lmax) {
+  return SoftmaxWeights4{logits, w, V, T, (T == 1.0f) ? lmax : lmax / T, aligned16(logits) && aligned16(w)};
+}
+
 __device__ __forceinline__ double softmax_weights(const float* logits, float* w, int V, float T, float lmax,
                                                   CdfShared& S) {
-  const float mt = (T == 1.0f) ? lmax : lmax / T;
-  const bool vec = aligned16(logits) && aligned16(w);
-  cdf_sums(
-      [&](int v0, double x[4]) {
-        float l[4];
-        load4(logits, v0, V, vec, l);
-        float e[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float lt = (T == 1.0f) ? l[k] : l[k] / T;
-          e[k] = (v0 + k < V) ? expf(lt - mt) : 0.f;
-          x[k] = (double)e[k];
-        }
-        if (vec && v0 + 4 <= V) {
-          *reinterpret_cast<f32x4*>(w + v0) = f32x4{e[0], e[1], e[2], e[3]};
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            if (v0 + k < V) w[v0 + k] = e[k];
-        }
-      },
-      V, S);
+  cdf_sums(softmax4(logits, w, V, T, lmax), V, S);
   return S.total;
+}
+
+// Softmax weights and their block sums over many workgroups (the dense
+// sampling path of the cycle): wave w of workgroup b takes block 4b + w.
+// The max logit comes from the head's per-workgroup argmax parts; the
+// weights go to `w` or, with `qring`, to the ring slot of position t + 1.
+// The finalisation and verification kernels then start from the block sums.
+struct SoftmaxArgs {
+  const ArgPair* parts;
+  int nparts;
+  const float* logits;
+  float* w;
+  float* qring;
+  double* bs;
+  int exit_only;  // only when a token exits this cycle
+  float temp;
+  const Ctrl* ctrl;
+  Geo g;
+};
+
+__global__ __launch_bounds__(kWG) void k_softmax_blocks(const SoftmaxArgs A) {
+  __shared__ float red[kWG / kWave];
+  const Ctrl* C = A.ctrl;
+  const Geo& g = A.g;
+  if (!C->active) return;
+  if (A.exit_only && C->a != g.n) return;
+  float v = -INFINITY;
+  for (int k = threadIdx.x; k < A.nparts; k += kWG) v = fmaxf(v, A.parts[k].v);
+  const float lmax = block_max(v, red);
+  float* w = A.qring ? A.qring + (size_t)((C->t + 1) % g.nslots) * g.V : A.w;
+  const int nwaves = kWG / kWave;
+  cdf_block_pass(softmax4(A.logits, w, g.V, A.temp, lmax), g.V, A.bs,
+                 blockIdx.x * nwaves + (int)(threadIdx.x / kWave), gridDim.x * nwaves);
 }
 
 // Reads the stored fp32 weights back as the fp64 weights of a draw.
@@ -549,6 +607,7 @@ __global__ __launch_bounds__(kWG) void k_entry(Ctrl* C, const Geo g, int32_t* to
 struct VerifyArgs {
   const ArgPair* parts;
   int nparts;
+  const double* bs;     // dense sampling: block sums of P from k_softmax_blocks (weights already in pw)
   const float* logits;  // [V] target logits of the exiting token
   float* pw;            // [V] scratch: target softmax weights (sample mode)
   const int32_t* dring; // drafts by position mod nslots
@@ -636,7 +695,16 @@ __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
     }
   } else {
     // P = softmax(logits / T); accept iff u * Q(x) < P(x); else redraw from max(0, P - Q)
-    const double pZ = softmax_weights(A.logits, A.pw, g.V, A.temp, best.v, S);
+    double pZ;
+    if (A.bs) {
+      const int nb = (g.V + kCdfBlock - 1) / kCdfBlock;
+      for (int b = threadIdx.x; b < nb; b += kCtlThreads) S.bs[b] = A.bs[b];
+      __syncthreads();
+      cdf_super_sums(g.V, S);
+      pZ = S.total;
+    } else {
+      pZ = softmax_weights(A.logits, A.pw, g.V, A.temp, best.v, S);
+    }
     const float* qw = A.qring + (size_t)nslot * g.V;
     const double qZ = A.qz[nslot];
     const double u_acc = A.uni[(size_t)(j + 1) * SPD_U_COUNT + SPD_U_ACCEPT];
@@ -701,6 +769,7 @@ __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
 struct FinalizeArgs {
   const ArgPair* parts;
   int nparts;
+  const double* bs;     // dense sampling: block sums from k_softmax_blocks (weights already in qring)
   const float* logits;  // [V] PDM logits of the newest row
   int32_t* dring;
   float* qring;
@@ -751,7 +820,16 @@ __global__ __launch_bounds__(kCtlThreads) void k_pdm_finalize(const FinalizeArgs
     }
   } else {
     float* qw = A.qring + (size_t)slot * g.V;
-    const double Z = softmax_weights(A.logits, qw, g.V, A.temp, best.v, S);
+    double Z;
+    if (A.bs) {  // weights and block sums from k_softmax_blocks
+      const int nb = (g.V + kCdfBlock - 1) / kCdfBlock;
+      for (int b = threadIdx.x; b < nb; b += kCtlThreads) S.bs[b] = A.bs[b];
+      __syncthreads();
+      cdf_super_sums(g.V, S);
+      Z = S.total;
+    } else {
+      Z = softmax_weights(A.logits, qw, g.V, A.temp, best.v, S);
+    }
     const double u = A.uni[(size_t)q * SPD_U_COUNT + SPD_U_DRAFT];
     raw = cdf_draw(StoredWeights{qw, g.V, aligned16(qw)}, g.V, u, S);
     if (threadIdx.x == 0) A.qz[slot] = Z;

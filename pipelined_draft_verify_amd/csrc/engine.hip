@@ -42,6 +42,7 @@ struct Layout {
   size_t logits, plogits, pw, parts, pparts, ring;
   size_t ssq_t, ssq_p, mpart;
   size_t lin_state, lin_ckpt;
+  size_t bsq, bsp;
   size_t total;
   int ctx_cap, nsplit, mr, log_cap, nparts_max;
 };
@@ -183,6 +184,10 @@ Layout make_layout(const spd_config* c) {
   const size_t lin_one = (size_t)Hkv * ((size_t)hd * hd + hd);
   L.lin_state = take(c->attn_period > 0 ? sizeof(float) * (size_t)c->n_layers * nslots * lin_one : 0);
   L.lin_ckpt = take(c->attn_period > 0 ? sizeof(float) * (size_t)c->n_layers * lin_one : 0);
+  // dense sampling: block sums of Q (draft) and P (target) from k_softmax_blocks
+  const size_t nbs = smp && !c->top_k ? (size_t)(V + kCdfBlock - 1) / kCdfBlock : 0;
+  L.bsq = take(sizeof(double) * nbs);
+  L.bsp = take(sizeof(double) * nbs);
   L.total = off;
   return L;
 }
@@ -210,6 +215,7 @@ struct spd_handle {
   spd_cycle_rec* ring;
   float *ssq_t, *ssq_p, *mpart;
   float *lin_state = nullptr, *lin_ckpt = nullptr;
+  double *bsq = nullptr, *bsp = nullptr;  // dense sampling block sums (Q, P)
   int ckpt_len = 0;     // prefill length whose linear-attention states lin_ckpt holds
   int lin_newest = -1;  // newest position whose linear-attention state a row pass wrote
   int lin_keep_from = 0;
@@ -696,10 +702,25 @@ int pdm_chain(spd_t* h, hipStream_t ps) {
     hd.parts = h->pparts;
     int grid = 0;
     launch_stage<WT, EPI_ARGMAX>(h, hd, 1, ps, &grid);
+    if (h->bsq) {
+      SoftmaxArgs sm;
+      memset(&sm, 0, sizeof(sm));
+      sm.parts = h->pparts;
+      sm.nparts = grid;
+      sm.logits = h->plogits;
+      sm.qring = h->qring;
+      sm.bs = h->bsq;
+      sm.temp = h->cfg.temperature;
+      sm.ctrl = h->ctrl;
+      sm.g = g;
+      const int nb = (g.V + kCdfBlock - 1) / kCdfBlock;
+      hipLaunchKernelGGL(k_softmax_blocks, dim3((nb + kWG / kWave - 1) / (kWG / kWave)), dim3(kWG), 0, ps, sm);
+    }
     FinalizeArgs f;
     memset(&f, 0, sizeof(f));
     f.parts = h->pparts;
     f.nparts = grid;
+    f.bs = h->bsq;
     f.logits = h->plogits;
     f.dring = h->dring;
     f.qring = h->qring;
@@ -869,10 +890,26 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
   hd.parts = h->parts;
   int grid = 0;
   launch_stage<WT, EPI_ARGMAX>(h, hd, 1, ss, &grid);
+  if (h->bsp) {
+    SoftmaxArgs sm;
+    memset(&sm, 0, sizeof(sm));
+    sm.parts = h->parts;
+    sm.nparts = grid;
+    sm.logits = h->logits;
+    sm.w = h->pw;
+    sm.bs = h->bsp;
+    sm.exit_only = 1;
+    sm.temp = h->cfg.temperature;
+    sm.ctrl = h->ctrl;
+    sm.g = g;
+    const int nb = (g.V + kCdfBlock - 1) / kCdfBlock;
+    hipLaunchKernelGGL(k_softmax_blocks, dim3((nb + kWG / kWave - 1) / (kWG / kWave)), dim3(kWG), 0, ss, sm);
+  }
   VerifyArgs v;
   memset(&v, 0, sizeof(v));
   v.parts = h->parts;
   v.nparts = grid;
+  v.bs = h->bsp;
   v.logits = h->logits;
   v.pw = h->pw;
   v.dring = h->dring;
@@ -1195,6 +1232,10 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   h->ssq_t = (float*)(ws + L.ssq_t);
   h->ssq_p = (float*)(ws + L.ssq_p);
   h->mpart = (float*)(ws + L.mpart);
+  if (cfg->mode == SPD_MODE_SAMPLE && !cfg->top_k) {
+    h->bsq = (double*)(ws + L.bsq);
+    h->bsp = (double*)(ws + L.bsp);
+  }
   if (cfg->attn_period > 0) {
     h->lin_state = (float*)(ws + L.lin_state);
     h->lin_ckpt = (float*)(ws + L.lin_ckpt);
