@@ -191,6 +191,7 @@ def main():
     cyc_end = cyc_arr[:, 2].reshape(reps, K_c).mean(axis=0)
     bubble = float(np.maximum(0.0, cyc_arr[:, 1] - cyc_arr[:, 0]).sum() / cyc_arr[:, 2].sum())
     hbm_frac = float(per_cycle_bytes.sum() / (cyc_end.sum() * 1e-3) / PEAK_HBM)
+    per_cycle_frac = per_cycle_bytes / (cyc_end * 1e-3) / PEAK_HBM
     occ = recs["occupancy"]
     full = occ == w.n
     # where the time and the bubble go, by occupancy (stderr diagnostics)
@@ -237,6 +238,10 @@ def main():
         "tokens_per_s": round(tokens_per_s, 3),
         "hbm_frac_per_cycle": round(hbm_frac, 4),
         "hbm_frac_full_cycles": round(hbm_full, 4) if hbm_full is not None else None,
+        "hbm_frac_cycle_median": round(float(np.median(per_cycle_frac)), 4),
+        "hbm_frac_cycle_p10": round(float(np.percentile(per_cycle_frac, 10)), 4),
+        "tokens_per_cycle": round((w.G - 1) / K_c, 4),
+        "L_acc": round((w.G - 1) / K_c * w.n, 4),
         "bubble_frac": round(bubble, 4),
         "accepted_verifications": int((acc["accepted"] == 1).sum()),
         "verifications": int(len(acc)),
