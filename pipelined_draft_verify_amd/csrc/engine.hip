@@ -959,7 +959,7 @@ int enqueue_cycle(spd_t* h) {
   const bool graph = h->launch_mode == 1;
   // serialized: the draft module is enqueued on the stage stream ahead of the
   // stage step (it reads only pre-step state, so the result is unchanged).
-  // Post-step schedule: it reads the stage step's output and the verdict, so
+  // Post-step schedule: it reads the stage step's output and the verification result, so
   // it follows them on the stage stream.
   // One stage (n = 1): the token entering a cycle also exits in it and
   // verifies the draft made in the same cycle, so the draft chain goes
