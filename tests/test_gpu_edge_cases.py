@@ -11,7 +11,9 @@
   * the longest context (max_ctx = 32768: 128 attention splits): the oracle
     cannot attend over 32k positions in seconds, so the check is a property
     that holds at any size -- natural and forced drafts emit exactly the
-    GPU's own autoregressive greedy decode.
+    GPU's own autoregressive greedy decode;
+  * the largest vocabulary (SPD_MAX_VOCAB = 2^20 ids) in sample mode, dense
+    and with top-64 truncation.
 Every run through the oracle must agree cycle by cycle as in the other
 small-workload parity tests.
 """
@@ -112,3 +114,25 @@ def test_longest_context_is_lossless():
         assert len(ex) == G - 1 and int(ex["exit_pos"][-1]) == P + G - 2
         assert int(recs["t"].max()) < w.max_ctx
     eng.close()
+
+
+@pytest.mark.parametrize("top_k", [0, 64])
+def test_sampling_at_the_largest_vocabulary(top_k):
+    """V = SPD_MAX_VOCAB = 2^20: 4096 sampler blocks in 64 superblocks (dense),
+    or the top-64 selection over 2^20 ids.  Near-uniform random-init
+    distributions put ~1e-6 of the mass on each id, so differing draws may
+    land on a neighbouring id; each must lie within the sampling tolerance."""
+    from tests.test_gpu_parity_small import STOL, TOL
+    from tests.gpu_common import teacher_of
+    from oracle import SPDOracle
+
+    w = gpu_workload_tiny(mode="sample", temperature=1.0, V=1 << 20, L=2, n=2, Ls=1, anchors=[0, 1, 2], G=10,
+                          top_k=top_k, seed=60 + top_k)
+    T, W, prompt, uni = _inputs(w)
+    eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni)
+    eng.close()
+    o = SPDOracle(w, W, uniforms=uni, teacher=teacher_of(recs, first), tol=TOL[w.dtype], sample_tol=STOL[w.dtype])
+    otoks, ologs = o.run(prompt, w.G)
+    assert not o.dec.mismatch, o.dec.mismatch
+    assert toks == otoks
+    compare_logs(recs, ologs, w.L)
