@@ -195,11 +195,13 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 // Sum of squares of x[0..K) by kWG threads, fixed order; returns
 // 1/sqrt(mean + eps).  Every kernel that normalises a row uses this, so the
 // same row gets the same scale everywhere.
+__device__ __forceinline__ float rstd_of(float sumsq, int K, float eps) {
+  return 1.0f / sqrtf(sumsq / (float)K + eps);
+}
 __device__ __forceinline__ float row_rstd(const float* __restrict__ x, int K, float eps, float* red) {
   float s = 0.f;
   for (int i = threadIdx.x; i < K; i += kWG) s = fmaf(x[i], x[i], s);
-  s = block_sum(s, red);
-  return 1.0f / sqrtf(s / (float)K + eps);
+  return rstd_of(block_sum(s, red), K, eps);
 }
 
 // Geometry of the engine, passed by value to kernels.

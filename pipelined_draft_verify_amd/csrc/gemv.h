@@ -108,6 +108,48 @@ __device__ __forceinline__ void gemv_step(const typename WVec<WT>::Raw* rw, cons
   }
 }
 
+// xs[i] = x[i] * rstd * gm[i] (no gain: xs[i] = x[i]) for i < K, by kWG
+// threads.  Rows of up to kWG * kXRegs elements are read once, row and gain
+// loads all in flight together; the sum of squares runs in row_rstd's order
+// and the scale is the same expression, so the staged values are the same
+// bits as on the two-pass path used for longer rows.
+constexpr int kXRegs = 16;
+__device__ __forceinline__ void stage_input(const float* __restrict__ x, const float* __restrict__ gm, int K,
+                                            float eps, float* red, float* xs) {
+  if (K <= kWG * kXRegs) {
+    float xr[kXRegs], gr[kXRegs];
+#pragma unroll
+    for (int j = 0; j < kXRegs; ++j) {
+      const int i = threadIdx.x + j * kWG;
+      xr[j] = i < K ? x[i] : 0.f;
+      gr[j] = (gm != nullptr && i < K) ? gm[i] : 0.f;
+    }
+    if (gm) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < kXRegs; ++j)
+        if (threadIdx.x + j * kWG < K) s = fmaf(xr[j], xr[j], s);
+      const float rstd = rstd_of(block_sum(s, red), K, eps);
+#pragma unroll
+      for (int j = 0; j < kXRegs; ++j) {
+        const int i = threadIdx.x + j * kWG;
+        if (i < K) xs[i] = xr[j] * rstd * gr[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kXRegs; ++j) {
+        const int i = threadIdx.x + j * kWG;
+        if (i < K) xs[i] = xr[j];
+      }
+    }
+  } else if (gm) {
+    const float rstd = row_rstd(x, K, eps, red);
+    for (int i = threadIdx.x; i < K; i += kWG) xs[i] = x[i] * rstd * gm[i];
+  } else {
+    for (int i = threadIdx.x; i < K; i += kWG) xs[i] = x[i];
+  }
+}
+
 template <typename WT, int EPI, bool XG = false>
 __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
   extern __shared__ float xs_lds[];  // [K] (unless XG)
@@ -159,32 +201,6 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
   for (long long tile = t0; tile < t1; ++tile) {
     const int grp = (int)(tile / tpg);
     const int ut = (int)(tile - (long long)grp * tpg);
-    if (grp != cur) {
-      cur = grp;
-      pos = pos_base - grp;
-      const bool fixed = (A.gmode == GM_FIXED || A.gmode == GM_PDMLAST);
-      slot = fixed ? 0 : pos % g.nslots;
-      const float* x = fixed ? xfix : A.x + (A.x_by_slot ? slot : grp) * A.x_stride;
-      const float* gm = A.gamma[grp];
-      if (XG) {
-        xs = x;
-      } else {
-        __syncthreads();
-        if (gm) {
-          const float rstd = row_rstd(x, A.K, g.eps, red);
-          for (int i = threadIdx.x; i < A.K; i += kWG) xs_lds[i] = x[i] * rstd * gm[i];
-        } else {
-          for (int i = threadIdx.x; i < A.K; i += kWG) xs_lds[i] = x[i];
-        }
-        __syncthreads();
-      }
-      W = reinterpret_cast<const WT*>(A.W[grp]);
-      if (EPI == EPI_QKV && ut == 0 && threadIdx.x == 0 && A.kv_len) {
-        int* len = A.kv_len + A.layer[grp];
-        if (*len != pos) atomicOr(&A.ctrl->flags, SPD_FLAG_KVLEN);
-        *len = pos + 1;
-      }
-    }
     // four rows of this wave
     int rows[4];
     bool ok[4];
@@ -202,29 +218,67 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
         ok[j] = u < A.units;
       }
     }
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    W = reinterpret_cast<const WT*>(A.W[grp]);
     const WT* p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = W + (size_t)rows[r] * A.K;
     // two k-steps per trip: the eight 16-byte weight loads are all issued
-    // before the first is used; the odd last step (if any) likewise
+    // before the first is used; the odd last step (if any) likewise.  The
+    // first trip's loads go out before a new group's input row is staged,
+    // so the staging overlaps their latency.
     constexpr int kStep = kWave * VEC;
     int k0 = lane * VEC;
-    for (; k0 + kStep < A.K; k0 += 2 * kStep) {
-      typename WVec<WT>::Raw ra[4], rb[4];
+    const bool pair0 = k0 + kStep < A.K;
+    typename WVec<WT>::Raw ra[4], rb[4];
+    if (k0 < A.K) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) ra[r] = WVec<WT>::ld(p[r] + k0);
+    }
+    if (pair0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) rb[r] = WVec<WT>::ld(p[r] + k0 + kStep);
-      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp != cur) {
+      cur = grp;
+      pos = pos_base - grp;
+      const bool fixed = (A.gmode == GM_FIXED || A.gmode == GM_PDMLAST);
+      slot = fixed ? 0 : pos % g.nslots;
+      const float* x = fixed ? xfix : A.x + (A.x_by_slot ? slot : grp) * A.x_stride;
+      if (XG) {
+        xs = x;
+      } else {
+        __syncthreads();
+        stage_input(x, A.gamma[grp], A.K, g.eps, red, xs_lds);
+        __syncthreads();
+      }
+      if (EPI == EPI_QKV && ut == 0 && threadIdx.x == 0 && A.kv_len) {
+        int* len = A.kv_len + A.layer[grp];
+        if (*len != pos) atomicOr(&A.ctrl->flags, SPD_FLAG_KVLEN);
+        *len = pos + 1;
+      }
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (pair0) {
       gemv_step<WT>(ra, xs + k0, acc);
       gemv_step<WT>(rb, xs + k0 + kStep, acc);
-    }
-    if (k0 < A.K) {
-      typename WVec<WT>::Raw ra[4];
+      k0 += 2 * kStep;
+      for (; k0 + kStep < A.K; k0 += 2 * kStep) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ra[r] = WVec<WT>::ld(p[r] + k0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < 4; ++r) ra[r] = WVec<WT>::ld(p[r] + k0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rb[r] = WVec<WT>::ld(p[r] + k0 + kStep);
+        __builtin_amdgcn_sched_barrier(0);
+        gemv_step<WT>(ra, xs + k0, acc);
+        gemv_step<WT>(rb, xs + k0 + kStep, acc);
+      }
+      if (k0 < A.K) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ra[r] = WVec<WT>::ld(p[r] + k0);
+        __builtin_amdgcn_sched_barrier(0);
+        gemv_step<WT>(ra, xs + k0, acc);
+      }
+    } else if (k0 < A.K) {
       gemv_step<WT>(ra, xs + k0, acc);
     }
 #pragma unroll
