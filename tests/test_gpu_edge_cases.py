@@ -5,6 +5,8 @@
     (SPD_MAX_PDM_LAYERS = 8) and with bf16;
   * the most anchors (SPD_MAX_ANCHORS = 8, one fusion matrix each) and the
     most target layers and stages (SPD_MAX_LAYERS = 64, SPD_MAX_STAGES = 16);
+  * GEMV inputs longer than 4096 elements, which the stage GEMV stages in two
+    passes instead of from registers (bf16 and fp32);
   * a generation of one token (prefill only: the cycles that follow are
     idle) and of two (one verification);
   * an empty prompt is refused;
@@ -34,6 +36,11 @@ EDGE = {
     "n1_Ls8_f32": dict(L=8, n=1, Ls=8, anchors=[0, 4, 8], G=14, p=0.6, seed=52),
     "m8_anchors_bf16": dict(dtype="bf16", L=8, n=2, Ls=2, anchors=[0, 1, 2, 3, 4, 5, 6, 7], p=0.6, seed=53),
     "L64_n16_f32": dict(L=64, n=16, Ls=4, anchors=[0, 16, 32, 48, 64], G=40, p=0.7, seed=54),
+    # GEMV inputs longer than the register-staged 4096 elements (model width
+    # and query heads x head dim 4608): the two-pass staging path
+    "d4608_bf16": dict(dtype="bf16", L=4, n=2, Ls=1, d=4608, Hq=72, Hkv=9, F=512, anchors=[0, 2, 4], p=0.6,
+                       seed=55),
+    "d4352_f32": dict(L=4, n=2, Ls=1, d=4352, F=512, anchors=[0, 2, 4], p=0.6, seed=56),
 }
 
 
