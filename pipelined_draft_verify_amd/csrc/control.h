@@ -414,20 +414,41 @@ __device__ __forceinline__ unsigned long long wave_insert_desc(unsigned long lon
   return lane < pos ? lst : (lane == pos ? x : up);
 }
 
-// Wave w streams blocks w, w + 16, ... of kCdfBlock ids (lane l: ids 4l..4l+3)
-// and keeps the best 64 keys it sees (at least the best k).
-__device__ __forceinline__ unsigned long long wave_topk_pass(const float* logits, int V, int k) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int nb = (V + kCdfBlock - 1) / kCdfBlock;
+// One round of offers to a wave's list: each lane's key that beats the
+// list's k-th key enters (a few are shifted in one at a time, more than 8 are
+// sorted and merged).
+__device__ __forceinline__ void wave_topk_offer(unsigned long long& lst, unsigned long long& thr,
+                                                unsigned long long key, int k) {
+  const unsigned long long cand = key > thr ? key : 0ull;
+  unsigned long long m = __ballot(cand != 0ull);
+  if (m == 0ull) return;
+  if (__popcll(m) > 8) {
+    lst = wave_merge_desc(lst, wave_sort_desc(cand));
+  } else {
+    while (m) {
+      const int src = first_lane(m);
+      m &= m - 1;
+      lst = wave_insert_desc(lst, __shfl(cand, src, kWave));
+    }
+  }
+  thr = __shfl(lst, k - 1, kWave);
+}
+
+// Wave w of nwaves streams blocks b_lo + w, b_lo + w + nwaves, ... (below
+// b_hi) of kCdfBlock ids (lane l: ids 4l..4l+3) and keeps the best 64 keys it
+// sees (at least the best k).
+__device__ __forceinline__ unsigned long long wave_topk_pass(const float* logits, int V, int k, int b_lo, int b_hi,
+                                                             int w, int nwaves) {
+  const int lane = threadIdx.x & (kWave - 1);
   const bool vec = aligned16(logits);
   unsigned long long lst = 0ull;
   unsigned long long thr = 0ull;  // the list's k-th key
-  for (int b0 = wave; b0 < nb; b0 += kCtlWaves * kCdfUnroll) {
+  for (int b0 = b_lo + w; b0 < b_hi; b0 += nwaves * kCdfUnroll) {
     float l[kCdfUnroll][4];
 #pragma unroll
     for (int u = 0; u < kCdfUnroll; ++u) {
-      const int b = b0 + u * kCtlWaves;
-      if (b < nb) {
+      const int b = b0 + u * nwaves;
+      if (b < b_hi) {
         load4(logits, b * kCdfBlock + lane * kCdfPer, V, vec, l[u]);
       } else {
 #pragma unroll
@@ -436,38 +457,79 @@ __device__ __forceinline__ unsigned long long wave_topk_pass(const float* logits
     }
 #pragma unroll
     for (int u = 0; u < kCdfUnroll; ++u) {
-      const int b = b0 + u * kCtlWaves;
-      if (b >= nb) break;
+      const int b = b0 + u * nwaves;
+      if (b >= b_hi) break;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int id = b * kCdfBlock + lane * kCdfPer + e;
-        const unsigned long long key = id < V ? rank_key(l[u][e], id) : 0ull;
-        const unsigned long long cand = key > thr ? key : 0ull;
-        unsigned long long m = __ballot(cand != 0ull);
-        if (m == 0ull) continue;
-        if (__popcll(m) > 8) {
-          lst = wave_merge_desc(lst, wave_sort_desc(cand));
-        } else {
-          while (m) {
-            const int src = first_lane(m);
-            m &= m - 1;
-            lst = wave_insert_desc(lst, __shfl(cand, src, kWave));
-          }
-        }
-        thr = __shfl(lst, k - 1, kWave);
+        wave_topk_offer(lst, thr, id < V ? rank_key(l[u][e], id) : 0ull, k);
       }
     }
   }
   return lst;
 }
 
-// Top-k of logits[0, V): called by every thread; in wave 0, lane i < k ends
-// with the i-th kept id in ascending id order and its logit (lanes >= k: id
-// -1).  `k` <= min(64, V).
-__device__ __forceinline__ void topk_select(const float* logits, int V, int k, TopkShared& S, int& id,
-                                            float& val) {
+// The same over candidate keys cand[0, n) (0: no element), kCdfBlock keys
+// per wave step (lane l: keys 4l..4l+3 of the step).
+__device__ __forceinline__ unsigned long long wave_topk_keys(const unsigned long long* cand, int n, int k, int w,
+                                                             int nwaves) {
+  const int lane = threadIdx.x & (kWave - 1);
+  unsigned long long lst = 0ull;
+  unsigned long long thr = 0ull;
+  for (int i0 = w * kCdfBlock; i0 < n; i0 += nwaves * kCdfBlock) {
+    unsigned long long c[kCdfPer];
+#pragma unroll
+    for (int e = 0; e < kCdfPer; ++e) {
+      const int i = i0 + lane * kCdfPer + e;
+      c[e] = i < n ? cand[i] : 0ull;
+    }
+#pragma unroll
+    for (int e = 0; e < kCdfPer; ++e) wave_topk_offer(lst, thr, c[e], k);
+  }
+  return lst;
+}
+
+// Candidate pass over many workgroups: workgroup b keeps the best 64 keys of
+// blocks [b * kTopkBlocksPerWG, (b + 1) * kTopkBlocksPerWG) in cand[b][0..63]
+// (descending, 0 for missing entries).  The k best of all candidates are the
+// k best of the vocabulary, because every workgroup keeps at least its k
+// best: the final selection over the candidates gives the same set as a pass
+// over the logits.
+constexpr int kTopkBlocksPerWG = 16;  // 4096 ids per workgroup
+
+struct TopkArgs {
+  const float* logits;
+  unsigned long long* cand;  // [gridDim.x][kWave]
+  int exit_only;             // only when a token exits this cycle
+  const Ctrl* ctrl;
+  Geo g;
+};
+
+__global__ __launch_bounds__(kWG) void k_topk_blocks(const TopkArgs A) {
+  __shared__ unsigned long long lists[kWG / kWave][kWave];
+  const Ctrl* C = A.ctrl;
+  const Geo& g = A.g;
+  if (!C->active) return;
+  if (A.exit_only && C->a != g.n) return;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const unsigned long long lst = wave_topk_pass(logits, V, k);
+  const int nb = (g.V + kCdfBlock - 1) / kCdfBlock;
+  const int b_lo = blockIdx.x * kTopkBlocksPerWG;
+  const int b_hi = min(nb, b_lo + kTopkBlocksPerWG);
+  lists[wave][lane] = wave_topk_pass(A.logits, g.V, g.topk, b_lo, b_hi, wave, kWG / kWave);
+  __syncthreads();
+  if (wave == 0) {
+    unsigned long long all = lists[0][lane];
+#pragma unroll
+    for (int w = 1; w < kWG / kWave; ++w) all = wave_merge_desc(all, lists[w][lane]);
+    A.cand[(size_t)blockIdx.x * kWave + lane] = all;
+  }
+}
+
+// Wave 0 merges the kCtlWaves lists `lst` (one per wave, called by every
+// thread); lane i < k of wave 0 ends with the i-th kept id in ascending id
+// order and its logit (lanes >= k, and every other thread: id -1).
+__device__ __forceinline__ void topk_merge(unsigned long long lst, int k, TopkShared& S, int& id, float& val) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   S.lists[wave][lane] = lst;
   __syncthreads();
   id = -1;
@@ -486,6 +548,20 @@ __device__ __forceinline__ void topk_select(const float* logits, int V, int k, T
     }
   }
   __syncthreads();
+}
+
+// Top-k of logits[0, V) by the kCtlWaves waves of the workgroup (results as
+// topk_merge).  `k` <= min(64, V).
+__device__ __forceinline__ void topk_select(const float* logits, int V, int k, TopkShared& S, int& id,
+                                            float& val) {
+  const int nb = (V + kCdfBlock - 1) / kCdfBlock;
+  topk_merge(wave_topk_pass(logits, V, k, 0, nb, threadIdx.x / kWave, kCtlWaves), k, S, id, val);
+}
+
+// The same selection from k_topk_blocks' candidate keys cand[0, n).
+__device__ __forceinline__ void topk_select_keys(const unsigned long long* cand, int n, int k, TopkShared& S,
+                                                 int& id, float& val) {
+  topk_merge(wave_topk_keys(cand, n, k, threadIdx.x / kWave, kCtlWaves), k, S, id, val);
 }
 
 // In wave 0 after topk_select: fp32 weight exp(l/T - lmax/T) of the lane's
@@ -608,6 +684,8 @@ struct VerifyArgs {
   const ArgPair* parts;
   int nparts;
   const double* bs;     // dense sampling: block sums of P from k_softmax_blocks (weights already in pw)
+  const unsigned long long* tk;  // top-k: k_topk_blocks' candidate keys of P (ntk of them), or null
+  int ntk;
   const float* logits;  // [V] target logits of the exiting token
   float* pw;            // [V] scratch: target softmax weights (sample mode)
   const int32_t* dring; // drafts by position mod nslots
@@ -659,7 +737,10 @@ __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
     // P and Q truncated to their top k: P from this exit's logits, Q as drafted
     int pid;
     float pl;
-    topk_select(A.logits, g.V, g.topk, TS, pid, pl);
+    if (A.tk)
+      topk_select_keys(A.tk, A.ntk, g.topk, TS, pid, pl);
+    else
+      topk_select(A.logits, g.V, g.topk, TS, pid, pl);
     if (threadIdx.x < kWave) {
       const int lane = threadIdx.x;
       const float pwf = topk_weight(pid, pl, A.temp, best.v);
@@ -770,6 +851,8 @@ struct FinalizeArgs {
   const ArgPair* parts;
   int nparts;
   const double* bs;     // dense sampling: block sums from k_softmax_blocks (weights already in qring)
+  const unsigned long long* tk;  // top-k: k_topk_blocks' candidate keys of Q (ntk of them), or null
+  int ntk;
   const float* logits;  // [V] PDM logits of the newest row
   int32_t* dring;
   float* qring;
@@ -804,7 +887,10 @@ __global__ __launch_bounds__(kCtlThreads) void k_pdm_finalize(const FinalizeArgs
     // Q truncated to its top k: stored as (id, weight) pairs for the verification
     int id;
     float val;
-    topk_select(A.logits, g.V, g.topk, TS, id, val);
+    if (A.tk)
+      topk_select_keys(A.tk, A.ntk, g.topk, TS, id, val);
+    else
+      topk_select(A.logits, g.V, g.topk, TS, id, val);
     raw = -1;
     if (threadIdx.x < kWave) {
       const int lane = threadIdx.x;

@@ -43,6 +43,7 @@ struct Layout {
   size_t ssq_t, ssq_p, mpart;
   size_t lin_state, lin_ckpt;
   size_t bsq, bsp;
+  size_t tkq, tkp;
   size_t total;
   int ctx_cap, nsplit, mr, log_cap, nparts_max;
 };
@@ -79,6 +80,14 @@ bool valid_config(const spd_config* c) {
   if (c->attn_period < 0 || c->attn_period > c->n_layers) return false;
   return true;
 }
+
+// Workgroups of k_topk_blocks over a vocabulary of V ids, and the candidate
+// keys they leave (64 each).
+int topk_groups(int V) {
+  const int nb = (V + kCdfBlock - 1) / kCdfBlock;
+  return (nb + kTopkBlocksPerWG - 1) / kTopkBlocksPerWG;
+}
+int topk_candidates(int V) { return topk_groups(V) * kWave; }
 
 // K ranges of one matrix-core product (N weight rows, K inputs): one when
 // the 64-row groups alone cover the CUs (the epilogue then stays in the
@@ -188,6 +197,10 @@ Layout make_layout(const spd_config* c) {
   const size_t nbs = smp && !c->top_k ? (size_t)(V + kCdfBlock - 1) / kCdfBlock : 0;
   L.bsq = take(sizeof(double) * nbs);
   L.bsp = take(sizeof(double) * nbs);
+  // top-k sampling: candidate keys of Q and P from k_topk_blocks
+  const size_t ntk = smp && c->top_k ? (size_t)topk_candidates(V) : 0;
+  L.tkq = take(sizeof(unsigned long long) * ntk);
+  L.tkp = take(sizeof(unsigned long long) * ntk);
   L.total = off;
   return L;
 }
@@ -216,6 +229,7 @@ struct spd_handle {
   float *ssq_t, *ssq_p, *mpart;
   float *lin_state = nullptr, *lin_ckpt = nullptr;
   double *bsq = nullptr, *bsp = nullptr;  // dense sampling block sums (Q, P)
+  unsigned long long *tkq = nullptr, *tkp = nullptr;  // top-k candidate keys (Q, P)
   int ckpt_len = 0;     // prefill length whose linear-attention states lin_ckpt holds
   int lin_newest = -1;  // newest position whose linear-attention state a row pass wrote
   int lin_keep_from = 0;
@@ -716,11 +730,22 @@ int pdm_chain(spd_t* h, hipStream_t ps) {
       const int nb = (g.V + kCdfBlock - 1) / kCdfBlock;
       hipLaunchKernelGGL(k_softmax_blocks, dim3((nb + kWG / kWave - 1) / (kWG / kWave)), dim3(kWG), 0, ps, sm);
     }
+    if (h->tkq) {
+      TopkArgs tk;
+      memset(&tk, 0, sizeof(tk));
+      tk.logits = h->plogits;
+      tk.cand = h->tkq;
+      tk.ctrl = h->ctrl;
+      tk.g = g;
+      hipLaunchKernelGGL(k_topk_blocks, dim3(topk_groups(g.V)), dim3(kWG), 0, ps, tk);
+    }
     FinalizeArgs f;
     memset(&f, 0, sizeof(f));
     f.parts = h->pparts;
     f.nparts = grid;
     f.bs = h->bsq;
+    f.tk = h->tkq;
+    f.ntk = h->tkq ? topk_candidates(g.V) : 0;
     f.logits = h->plogits;
     f.dring = h->dring;
     f.qring = h->qring;
@@ -905,11 +930,23 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     const int nb = (g.V + kCdfBlock - 1) / kCdfBlock;
     hipLaunchKernelGGL(k_softmax_blocks, dim3((nb + kWG / kWave - 1) / (kWG / kWave)), dim3(kWG), 0, ss, sm);
   }
+  if (h->tkp) {
+    TopkArgs tk;
+    memset(&tk, 0, sizeof(tk));
+    tk.logits = h->logits;
+    tk.cand = h->tkp;
+    tk.exit_only = 1;
+    tk.ctrl = h->ctrl;
+    tk.g = g;
+    hipLaunchKernelGGL(k_topk_blocks, dim3(topk_groups(g.V)), dim3(kWG), 0, ss, tk);
+  }
   VerifyArgs v;
   memset(&v, 0, sizeof(v));
   v.parts = h->parts;
   v.nparts = grid;
   v.bs = h->bsp;
+  v.tk = h->tkp;
+  v.ntk = h->tkp ? topk_candidates(g.V) : 0;
   v.logits = h->logits;
   v.pw = h->pw;
   v.dring = h->dring;
@@ -1235,6 +1272,10 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   if (cfg->mode == SPD_MODE_SAMPLE && !cfg->top_k) {
     h->bsq = (double*)(ws + L.bsq);
     h->bsp = (double*)(ws + L.bsp);
+  }
+  if (cfg->mode == SPD_MODE_SAMPLE && cfg->top_k) {
+    h->tkq = (unsigned long long*)(ws + L.tkq);
+    h->tkp = (unsigned long long*)(ws + L.tkp);
   }
   if (cfg->attn_period > 0) {
     h->lin_state = (float*)(ws + L.lin_state);
