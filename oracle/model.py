@@ -54,6 +54,7 @@ class _Shape:
         self.bf16 = w.dtype == "bf16"
         self.max_ctx = w.max_ctx
         self.attn_period = getattr(w, "attn_period", 0)
+        self.split = tuple(getattr(w, "split", ()) or ())
 
     def linear(self, layer: int) -> bool:
         """Hybrid target ([RB] limitations, [TW] §11: each block of 4
@@ -183,7 +184,7 @@ class Target:
         return h
 
     def run_stage(self, h, pos, k, taps=None):
-        return self.run_layers(h, pos, stage_layers(k, self.s.L, self.s.n), taps)
+        return self.run_layers(h, pos, stage_layers(k, self.s.L, self.s.n, self.s.split), taps)
 
     def logits(self, h: np.ndarray) -> np.ndarray:
         """Full-depth logits W_lm * rmsnorm(h^(L)) (float32)."""
@@ -248,13 +249,13 @@ class PDM:
 
     def feature(self, taps: Sequence[np.ndarray], k: int) -> np.ndarray:
         """g(p, k) = W_fc[f(k)] * concat(A[p][0..f(k)]) ([RB] core method)."""
-        f = pattern(k, self.s.anchors, self.s.L, self.s.n)
+        f = pattern(k, self.s.anchors, self.s.L, self.s.n, self.s.split)
         x = np.concatenate([taps[i] for i in range(f + 1)]).astype(F32)
         return self.W["fc"][f] @ x
 
     def feature_rows(self, taps_rows: Sequence[Sequence[np.ndarray]], k: int) -> np.ndarray:
         """`feature` of many positions at one depth k with one matrix product: [M, d_pdm]."""
-        f = pattern(k, self.s.anchors, self.s.L, self.s.n)
+        f = pattern(k, self.s.anchors, self.s.L, self.s.n, self.s.split)
         X = np.stack([np.concatenate([taps[i] for i in range(f + 1)]) for taps in taps_rows]).astype(F32)
         return (X @ self.W["fc"][f].T).astype(F32)
 

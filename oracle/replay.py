@@ -25,6 +25,8 @@ from __future__ import annotations
 
 from typing import Dict, List, Optional
 
+from .schedule import stage_layers
+
 
 class ReplayError(AssertionError):
     pass
@@ -32,10 +34,11 @@ class ReplayError(AssertionError):
 
 class Replay:
     def __init__(self, n: int, L: int, P: int, first: int, policy=None, sample: bool = False,
-                 post: bool = False):
-        if L % n:
+                 post: bool = False, split=()):
+        if not split and L % n:
             raise ValueError("n must divide L")
-        self.n, self.L, self.per = n, L, L // n
+        self.n, self.L = n, L
+        self.layers = [stage_layers(k, L, n, split) for k in range(n)]
         self.policy = policy
         self.sample = sample
         self.post = post
@@ -74,7 +77,7 @@ class Replay:
         # stage step: every in-flight token appends one KV entry to each layer of its stage
         for item in self.inflight:
             p, k, _ = item
-            for l in range(k * self.per, (k + 1) * self.per):
+            for l in self.layers[k]:
                 if self.kv[l] != p:
                     raise ReplayError(f"cycle {self.c}: layer {l} holds {self.kv[l]} entries before position {p}")
                 self.kv[l] = p + 1

@@ -1,50 +1,69 @@
 """Closed forms of the SPD schedule (test infrastructure only).
 
 Conventions: positions and layers are 0-indexed; stage k (0..n-1) holds
-layers k*L/n .. (k+1)*L/n - 1; the depth of a token is the number of stages
-it has completed (0..n); anchor b means the residual stream after b layers
-(b = 0 is the token embedding).
+layers k*L/n .. (k+1)*L/n - 1 under the uniform split, or the next `split[k]`
+layers under a non-uniform split; the depth of a token is the number of
+stages it has completed (0..n); anchor b means the residual stream after b
+layers (b = 0 is the token embedding).
+
+Non-uniform split ([RB] limitations and future work: splits such as
+"5+4;9;9;9", whose first rank holds a 5-layer stage and the 4-layer draft
+module beside three 9-layer stages, to fit 4- or 8-GPU nodes; [TW] §11 on
+balancing stages of a hybrid model).  Reading: `split` lists the layers of
+stages 0..n-1 (each >= 1, summing to L); a token at depth k has run the
+first split[0] + ... + split[k-1] layers, and every definition below that
+the pages state with k*L/n takes that cumulative count instead.
 """
 from __future__ import annotations
 
-from typing import List, Sequence
+from typing import List, Optional, Sequence
 
 
-def lmax(k: int, L: int, n: int) -> int:
-    """Deepest layer index a token at depth k has reached: min(L, k*L/n).
+def stage_sizes(L: int, n: int, split: Optional[Sequence[int]] = None) -> List[int]:
+    """Layers per stage: `split` when given, else L/n each ([RB] core method)."""
+    if split:
+        return [int(x) for x in split]
+    return [L // n] * n
 
-    [RB] core method (bounded incompleteness); [PL] §3.2.
-    """
+
+def lmax(k: int, L: int, n: int, split: Optional[Sequence[int]] = None) -> int:
+    """Deepest layer index a token at depth k has reached: min(L, k*L/n)
+    ([RB] core method, bounded incompleteness; [PL] §3.2), or the first k
+    stages' layers under a non-uniform split."""
+    if split:
+        return sum(split[:k])
     return min(L, k * (L // n))
 
 
-def pattern(k: int, anchors: Sequence[int], L: int, n: int) -> int:
+def pattern(k: int, anchors: Sequence[int], L: int, n: int, split: Optional[Sequence[int]] = None) -> int:
     """f(k) = max{i : b_i <= lmax(k)}: the last anchor reachable at depth k.
 
     The feature of a depth-k token concatenates anchors 0..f(k).  [RB] core
     method; [PL] §3.2 (k = 0 reduces to the embedding alone).
     """
-    lm = lmax(k, L, n)
+    lm = lmax(k, L, n, split)
     return max(i for i, b in enumerate(anchors) if b <= lm)
 
 
-def pattern_table(anchors: Sequence[int], L: int, n: int) -> List[int]:
-    return [pattern(k, anchors, L, n) for k in range(n + 1)]
+def pattern_table(anchors: Sequence[int], L: int, n: int, split: Optional[Sequence[int]] = None) -> List[int]:
+    return [pattern(k, anchors, L, n, split) for k in range(n + 1)]
 
 
-def n_patterns(anchors: Sequence[int], L: int, n: int) -> int:
+def n_patterns(anchors: Sequence[int], L: int, n: int, split: Optional[Sequence[int]] = None) -> int:
     """Number of distinct fusion projections the depths 0..n use.
 
     [RB] method step 3: several depths share one fusion pattern when m < n+1;
     [RB] technical novelty: the L=32, n=8 example needs m = 5 projections.
     """
-    return len(set(pattern_table(anchors, L, n)))
+    return len(set(pattern_table(anchors, L, n, split)))
 
 
-def stage_layers(k: int, L: int, n: int) -> range:
-    """Layers of stage k under the uniform split ([RB] core method: L/n each)."""
-    per = L // n
-    return range(k * per, (k + 1) * per)
+def stage_layers(k: int, L: int, n: int, split: Optional[Sequence[int]] = None) -> range:
+    """Layers of stage k: L/n each under the uniform split ([RB] core method),
+    the next split[k] layers under a non-uniform one."""
+    sizes = stage_sizes(L, n, split)
+    start = sum(sizes[:k])
+    return range(start, start + sizes[k])
 
 
 def depth_layout(a: int, pending: bool, n: int) -> List[int]:
@@ -99,13 +118,23 @@ def cycle_count(n: int, G: int, rejects: int) -> int:
     return n + (G - 2) + (n - 1) * rejects
 
 
-def validate_shape(L: int, n: int, Ls: int, anchors: Sequence[int]) -> None:
+def validate_shape(L: int, n: int, Ls: int, anchors: Sequence[int], split: Optional[Sequence[int]] = None) -> None:
     """Constraints the pages fix: n | L ([RB] core method), Ls <= L/n
     ([RB] core method / technical novelty: S = S0 iff Ls <= L/n), anchors
-    strictly increasing from 0 and within L ([RB] core method)."""
-    if L % n:
-        raise ValueError("n must divide L")
-    if Ls > L // n:
-        raise ValueError("draft module deeper than one stage")
+    strictly increasing from 0 and within L ([RB] core method).  A
+    non-uniform split lists n stages of >= 1 layers summing to L, and the
+    draft module may be as deep as the longest stage (reading: a cycle lasts
+    as long as its longest stage; the "5+4;9;9;9" example pairs a 4-layer
+    module with 9-layer stages)."""
+    if split:
+        if len(split) != n or min(split) < 1 or sum(split) != L:
+            raise ValueError("a split lists n stages of >= 1 layers summing to L")
+        if Ls > max(split):
+            raise ValueError("draft module deeper than the longest stage")
+    else:
+        if L % n:
+            raise ValueError("n must divide L")
+        if Ls > L // n:
+            raise ValueError("draft module deeper than one stage")
     if anchors[0] != 0 or any(b >= c for b, c in zip(anchors, anchors[1:])) or anchors[-1] > L:
         raise ValueError("anchors must increase strictly from 0 and stay <= L")

@@ -60,6 +60,7 @@ class Workload:
     schedule: str = "pre"   # draft-module features: "pre" (before the stage step) or "post"
     top_k: int = 0          # sample mode: keep the k largest logits (0: the whole vocabulary)
     attn_period: int = 0    # hybrid target: layer l is softmax attention iff l % P == P-1, else linear (0: all softmax)
+    split: tuple = ()       # layers of stages 0..n-1 (empty: L/n each)
 
     @property
     def max_ctx(self) -> int:

@@ -110,7 +110,7 @@ def replay(run: dict):
     if w.mode == "greedy" and w.policy == "forced":
         pol = ForcedPolicy(run["ref"], w.p_accept, run["uni"], w.V)
     rp = Replay(w.n, w.L, w.P, run["first"], policy=pol, sample=(w.mode == "sample"),
-                post=(w.schedule == "post"))
+                post=(w.schedule == "post"), split=w.split)
     out = []
     for i, r in enumerate(recs):
         ex = int(r["exit_pos"]) >= 0

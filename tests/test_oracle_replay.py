@@ -19,7 +19,7 @@ FIELDS = ["t", "a", "pending_row", "draft", "exit_pos", "y", "accept", "kv_len",
 
 
 def _replay(w, first, logs, policy, sample=False):
-    r = Replay(w.n, w.L, w.P, first, policy=policy, sample=sample, post=w.schedule == "post")
+    r = Replay(w.n, w.L, w.P, first, policy=policy, sample=sample, post=w.schedule == "post", split=w.split)
     out = []
     for l in logs:
         ex = l["exit_pos"] >= 0

@@ -203,7 +203,7 @@ def test_stage_skipping_a_layer_is_caught(monkeypatch):
     # a stage that runs one layer too few: AR is untouched, SPD must notice
     from oracle import model
 
-    def bad(k, L, n):
+    def bad(k, L, n, split=None):
         per = L // n
         return range(k * per, (k + 1) * per - 1)
     assert _run_mutated(monkeypatch, (model, "stage_layers"), bad, mi=2) != "same"
