@@ -38,25 +38,34 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def stage_ranges(w):
+    """Layers of each stage: L/n each, or the workload's non-uniform split."""
+    sizes = list(w.split) if getattr(w, "split", ()) else [w.L // w.n] * w.n
+    starts = [sum(sizes[:k]) for k in range(w.n + 1)]
+    return [range(starts[k], starts[k + 1]) for k in range(w.n)]
+
+
 def cycle_bytes(w, rec, es):
     """Algorithmic HBM bytes of one executed cycle (weights + KV reads)."""
-    L, d, F, V, n, per = w.L, w.d, w.F, w.V, w.n, w.L // w.n
+    L, d, F, V, n = w.L, w.d, w.F, w.V, w.n
+    stages = stage_ranges(w)
     qkv = (w.Hq + 2 * w.Hkv) * w.hd
     W_layer = (qkv * d + d * w.Hq * w.hd + 2 * F * d + d * F) * es
     kv_pos = 2 * w.Hkv * w.hd * es
     P_attn = getattr(w, "attn_period", 0)
     lin_state = 2 * w.Hkv * (w.hd * w.hd + w.hd) * 4  # a linear layer reads and writes its fp32 state
     t, a = int(rec["t"]), int(rec["occupancy"])
-    b = a * per * W_layer
+    b = sum(len(stages[k]) for k in range(a)) * W_layer
     for k in range(a):
-        for l in range(k * per, (k + 1) * per):
+        for l in stages[k]:
             linear = P_attn > 0 and l % P_attn != P_attn - 1
             b += lin_state if linear else (t - k + 1) * kv_pos
     if rec["exit_pos"] >= 0:
         b += V * d * es
     # draft module: FC patterns present, Ls layers, head, KV reads
-    def pattern(k):  # last anchor b_i <= min(L, k L/n)
-        return max(i for i, bb in enumerate(w.anchors) if bb <= min(L, k * per))
+    def pattern(k):  # last anchor b_i <= lmax(k), the layers of the first k stages
+        lm = stages[k].start if k < n else L
+        return max(i for i, bb in enumerate(w.anchors) if bb <= lm)
     if getattr(w, "schedule", "pre") == "post":
         pats = {pattern(k) for k in range(1, a + 1)}  # rows at depths a .. 1
     else:
@@ -204,8 +213,10 @@ def main():
             f"share of the bubble {np.maximum(0, pd[sel] - st[sel]).sum() / cyc_end.sum():.4f}")
     hbm_full = float(per_cycle_bytes[full].sum() / (cyc_end[full].sum() * 1e-3) / PEAK_HBM) if full.any() else None
     # dominant kernel: stage gate/up GEMV; algorithmic bytes = a * 2F * d * es per launch
-    gu_bytes_step = float(sum(int(r["occupancy"]) for r in recs) * (w.L // w.n) * 2 * w.F * w.d * es)
-    gu_launches_step = K_c * (w.L // w.n)
+    stages = stage_ranges(w)
+    gu_bytes_step = float(sum(sum(len(stages[k]) for k in range(int(r["occupancy"]))) for r in recs)
+                          * 2 * w.F * w.d * es)
+    gu_launches_step = K_c * max(len(r) for r in stages)  # one launch per sub-step
     assert gu_n == gu_launches_step, (gu_n, gu_launches_step)
     gu_avg_s = gu_ms * 1e-3 / gu_n
     gu_bytes_launch = gu_bytes_step / gu_launches_step

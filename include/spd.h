@@ -118,7 +118,8 @@ extern "C" {
  * residual; no biases.  The PDM layers have the same shape with their own
  * weights.  Constraints checked by spd_init ([RB] core method): n_stages
  * divides n_layers and is at most SPD_MAX_STAGES (the draft module batches
- * up to n_stages + 1 rows); pdm_layers <= n_layers / n_stages; anchors strictly
+ * up to n_stages + 1 rows); pdm_layers <= n_layers / n_stages (for a
+ * non-uniform split see stage_layers); anchors strictly
  * increasing with anchors[0] == 0 and anchors[n_anchors-1] <= n_layers;
  * n_heads % n_kv_heads == 0; head_dim in {64, 128}; d_model, d_ffn and
  * n_heads*head_dim multiples of 256; max_ctx <= 32768; 2 <= vocab <=
@@ -154,6 +155,16 @@ typedef struct spd_config {
                          id; selection before the temperature); 0 = the whole vocabulary.
                          0 <= top_k <= min(SPD_MAX_TOPK, vocab).  [RB] reproducibility assessment:
                          the evaluation decodes with top-k 50, top-p 1.0 (no nucleus cut). */
+  int32_t stage_layers[SPD_MAX_STAGES]; /* non-uniform split ([RB] limitations and future
+                         work: splits such as "5+4;9;9;9" -- a 5-layer first stage beside the
+                         4-layer draft module, then three 9-layer stages -- to fit 4- or
+                         8-GPU nodes): stage k runs the next stage_layers[k] layers, so a token
+                         at depth k has run stage_layers[0] + ... + stage_layers[k-1] layers,
+                         which takes the place of k * n_layers / n_stages in the anchor
+                         patterns.  All zero: the uniform split.  Otherwise entries
+                         0..n_stages-1 are >= 1 and sum to n_layers, the rest are 0, and
+                         pdm_layers is at most the longest stage (the cycle lasts as long as
+                         its longest stage). */
 } spd_config;
 
 /* Device pointers of one decoder layer.  Row-major, output features first:

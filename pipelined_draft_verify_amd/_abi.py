@@ -39,6 +39,7 @@ class spd_config(Structure):
         ("dtype", c_int32), ("max_ctx", c_int32), ("max_new", c_int32), ("mode", c_int32),
         ("rms_eps", c_float), ("rope_base", c_float), ("temperature", c_float),
         ("schedule", c_int32), ("attn_period", c_int32), ("top_k", c_int32),
+        ("stage_layers", c_int32 * SPD_MAX_STAGES),
     ]
 
 

@@ -41,6 +41,7 @@ constexpr int kMaxSplit = 128;  // splits of kSplit positions per context (max_c
 struct Attn {
   int pmode;
   int layer[SPD_MAX_STAGES];  // stage: layer of group g; rows: layer[0]
+  int stage[SPD_MAX_STAGES];  // stage: pipeline stage of group g (increasing)
   const void* kc;
   const void* vc;
   const float* q;  // [prow][Hq*hd]
@@ -57,9 +58,9 @@ struct Attn {
 __device__ __forceinline__ bool attn_problem(const Attn& A, int z, int& pos0, int& nrows, int& layer) {
   const Ctrl* C = A.ctrl;
   if (A.pmode == PM_STAGE) {
-    if (!C->active || z >= C->a) return false;
+    if (!C->active || A.stage[z] >= C->a) return false;
     if (layer_is_linear(A.g, A.layer[z])) return false;  // the linear-attention kernel's group
-    pos0 = C->t - z;
+    pos0 = C->t - A.stage[z];
     nrows = 1;
     layer = A.layer[z];
   } else {
@@ -486,9 +487,9 @@ __global__ __launch_bounds__(HD) void k_attn_merge(const Attn A) {
   const int prow = blockIdx.x, head = blockIdx.y;
   int pos;
   if (A.pmode == PM_STAGE) {
-    if (!C->active || prow >= C->a) return;
+    if (!C->active || A.stage[prow] >= C->a) return;
     if (layer_is_linear(g, A.layer[prow])) return;  // written by the linear-attention kernel
-    pos = C->t - prow;
+    pos = C->t - A.stage[prow];
   } else {
     int pos0, nrows;
     if (A.from_ctrl) {

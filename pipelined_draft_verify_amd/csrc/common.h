@@ -207,7 +207,7 @@ __device__ __forceinline__ float row_rstd(const float* __restrict__ x, int K, fl
 // Geometry of the engine, passed by value to kernels.
 struct Geo {
   int L, d, Hq, Hkv, hd, F, V, n, Ls, m;
-  int per;       // layers per stage
+  int per;       // layers of the longest stage (sub-steps of a stage step)
   int nslots;    // n + 1: position-indexed ring of in-flight slots
   int ctx_cap;   // KV capacity (positions), multiple of kSplit
   int nsplit;    // ctx_cap / kSplit
@@ -220,6 +220,7 @@ struct Geo {
   float eps;
   int anchor_of_layer[SPD_MAX_LAYERS + 1];  // anchor index of boundary b, or -1
   int fpat[SPD_MAX_STAGES + 1];             // f(k) for k = 0..n
+  int sstart[SPD_MAX_STAGES + 1];           // first layer of stage k; sstart[n] = L
 };
 
 // Hybrid target ([RB] limitations, [TW] §11: one standard and three linear

@@ -48,12 +48,34 @@ struct Layout {
   int ctx_cap, nsplit, mr, log_cap, nparts_max;
 };
 
+bool has_split(const spd_config* c) {
+  for (int k = 0; k < SPD_MAX_STAGES; ++k)
+    if (c->stage_layers[k] != 0) return true;
+  return false;
+}
+
 bool valid_config(const spd_config* c) {
   if (!c) return false;
   if (c->n_layers < 1 || c->n_layers > SPD_MAX_LAYERS) return false;
-  if (c->n_stages < 1 || c->n_stages > SPD_MAX_STAGES || c->n_layers % c->n_stages) return false;
-  if (c->pdm_layers < 1 || c->pdm_layers > SPD_MAX_PDM_LAYERS || c->pdm_layers > c->n_layers / c->n_stages)
+  if (c->n_stages < 1 || c->n_stages > SPD_MAX_STAGES) return false;
+  if (c->pdm_layers < 1 || c->pdm_layers > SPD_MAX_PDM_LAYERS) return false;
+  if (has_split(c)) {
+    // non-uniform split: n_stages entries >= 1 summing to n_layers, zeros after
+    int sum = 0, longest = 0;
+    for (int k = 0; k < SPD_MAX_STAGES; ++k) {
+      const int v = c->stage_layers[k];
+      if (k >= c->n_stages) {
+        if (v != 0) return false;
+      } else {
+        if (v < 1) return false;
+        sum += v;
+        longest = std::max(longest, v);
+      }
+    }
+    if (sum != c->n_layers || c->pdm_layers > longest) return false;
+  } else if (c->n_layers % c->n_stages || c->pdm_layers > c->n_layers / c->n_stages) {
     return false;
+  }
   if (c->n_anchors < 1 || c->n_anchors > SPD_MAX_ANCHORS || c->anchors[0] != 0) return false;
   for (int i = 1; i < c->n_anchors; ++i)
     if (c->anchors[i] <= c->anchors[i - 1]) return false;
@@ -311,7 +333,10 @@ void launch_rows(spd_t* h, RowsGemv a, int max_rows, hipStream_t s) {
 StageGemv stage_base(spd_t* h) {
   StageGemv a;
   memset(&a, 0, sizeof(a));
-  for (int i = 0; i < SPD_MAX_STAGES; ++i) a.anchor_idx[i] = -1;
+  for (int i = 0; i < SPD_MAX_STAGES; ++i) {
+    a.anchor_idx[i] = -1;
+    a.stage[i] = i;
+  }
   a.ctrl = h->ctrl;
   a.g = h->g;
   a.rcos = h->rcos;
@@ -775,12 +800,24 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
   // ---------------- stage step on the stage stream ----------------
   const int qd = g.Hq * g.hd;
   for (int j = 0; j < g.per; ++j) {
+    // groups of sub-step j: the stages that still have a layer, in stage
+    // order (all n stages under the uniform split)
+    int ng = 0, gstage[SPD_MAX_STAGES], glayer[SPD_MAX_STAGES];
+    for (int k = 0; k < g.n; ++k)
+      if (g.sstart[k] + j < g.sstart[k + 1]) {
+        gstage[ng] = k;
+        glayer[ng] = g.sstart[k] + j;
+        ++ng;
+      }
     StageGemv a = stage_base(h);
-    a.n_groups = g.n;
+    a.n_groups = ng;
     a.gmode = GM_STAGE;
-    for (int k = 0; k < g.n; ++k) a.layer[k] = k * g.per + j;
+    for (int k = 0; k < ng; ++k) {
+      a.layer[k] = glayer[k];
+      a.stage[k] = gstage[k];
+    }
     // q/k/v + RoPE + KV append
-    for (int k = 0; k < g.n; ++k) {
+    for (int k = 0; k < ng; ++k) {
       a.W[k] = w.layers[a.layer[k]].w_qkv;
       a.gamma[k] = (const float*)w.layers[a.layer[k]].attn_norm;
     }
@@ -795,12 +832,15 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     a.kc = h->kc;
     a.vc = h->vc;
     a.kv_len = h->kv_len;
-    launch_stage<WT, EPI_QKV>(h, a, g.n, ss);
+    launch_stage<WT, EPI_QKV>(h, a, ng, ss);
     // attention over each group's own layer cache
     Attn t;
     memset(&t, 0, sizeof(t));
     t.pmode = PM_STAGE;
-    for (int k = 0; k < g.n; ++k) t.layer[k] = a.layer[k];
+    for (int k = 0; k < ng; ++k) {
+      t.layer[k] = a.layer[k];
+      t.stage[k] = a.stage[k];
+    }
     t.kc = h->kc;
     t.vc = h->vc;
     t.q = h->s_q;
@@ -812,13 +852,16 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     // a hybrid target's sub-step may hold softmax and linear layers: each
     // kernel takes its own groups (the layer types are fixed per sub-step)
     bool any_soft = false, any_lin = false;
-    for (int k = 0; k < g.n; ++k) (layer_is_linear(g, a.layer[k]) ? any_lin : any_soft) = true;
-    if (any_soft) attention_any<WT>(t, dim3(g.nsplit, g.Hkv, g.n), 1, g.n, ss);
+    for (int k = 0; k < ng; ++k) (layer_is_linear(g, a.layer[k]) ? any_lin : any_soft) = true;
+    if (any_soft) attention_any<WT>(t, dim3(g.nsplit, g.Hkv, ng), 1, ng, ss);
     if (any_lin) {
       LinAttn la;
       memset(&la, 0, sizeof(la));
       la.mode = LM_STAGE;
-      for (int k = 0; k < g.n; ++k) la.layer[k] = a.layer[k];
+      for (int k = 0; k < ng; ++k) {
+        la.layer[k] = a.layer[k];
+        la.stage[k] = a.stage[k];
+      }
       la.kc = h->kc;
       la.vc = h->vc;
       la.q = h->s_q;
@@ -829,15 +872,16 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
       la.ctrl = h->ctrl;
       la.g = g;
       if (g.hd == 128)
-        hipLaunchKernelGGL((k_linattn<WT, 128>), dim3(g.Hkv, g.n), dim3(kWG), 0, ss, la);
+        hipLaunchKernelGGL((k_linattn<WT, 128>), dim3(g.Hkv, ng), dim3(kWG), 0, ss, la);
       else
-        hipLaunchKernelGGL((k_linattn<WT, 64>), dim3(g.Hkv, g.n), dim3(kWG), 0, ss, la);
+        hipLaunchKernelGGL((k_linattn<WT, 64>), dim3(g.Hkv, ng), dim3(kWG), 0, ss, la);
     }
     // output projection + residual
     StageGemv o = stage_base(h);
-    o.n_groups = g.n;
+    o.n_groups = ng;
     o.gmode = GM_STAGE;
-    for (int k = 0; k < g.n; ++k) {
+    for (int k = 0; k < ng; ++k) {
+      o.stage[k] = a.stage[k];
       o.layer[k] = a.layer[k];
       o.W[k] = w.layers[a.layer[k]].w_o;
     }
@@ -849,12 +893,13 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     o.out = h->hslots;
     o.out_stride = g.d;
     o.out_by_slot = 1;
-    launch_stage<WT, EPI_RESID>(h, o, g.n, ss);
+    launch_stage<WT, EPI_RESID>(h, o, ng, ss);
     // norm + gate/up + SwiGLU
     StageGemv u = stage_base(h);
-    u.n_groups = g.n;
+    u.n_groups = ng;
     u.gmode = GM_STAGE;
-    for (int k = 0; k < g.n; ++k) {
+    for (int k = 0; k < ng; ++k) {
+      u.stage[k] = a.stage[k];
       u.layer[k] = a.layer[k];
       u.W[k] = w.layers[a.layer[k]].w_gu;
       u.gamma[k] = (const float*)w.layers[a.layer[k]].ffn_norm;
@@ -873,7 +918,7 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
       g1 = pool_event(h);
       HIPCHK(h, hipEventRecord(g0, ss));
     }
-    launch_stage<WT, EPI_SWIGLU>(h, u, g.n, ss);
+    launch_stage<WT, EPI_SWIGLU>(h, u, ng, ss);
     if (g1) {
       HIPCHK(h, hipEventRecord(g1, ss));
       h->gu_ev.push_back(g0);
@@ -881,9 +926,10 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     }
     // down + residual + anchor taps
     StageGemv dn = stage_base(h);
-    dn.n_groups = g.n;
+    dn.n_groups = ng;
     dn.gmode = GM_STAGE;
-    for (int k = 0; k < g.n; ++k) {
+    for (int k = 0; k < ng; ++k) {
+      dn.stage[k] = a.stage[k];
       dn.layer[k] = a.layer[k];
       dn.W[k] = w.layers[a.layer[k]].w_down;
       dn.anchor_idx[k] = g.anchor_of_layer[a.layer[k] + 1];
@@ -897,7 +943,7 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     dn.out_stride = g.d;
     dn.out_by_slot = 1;
     dn.anchors = h->anchors;
-    launch_stage<WT, EPI_RESID>(h, dn, g.n, ss);
+    launch_stage<WT, EPI_RESID>(h, dn, ng, ss);
   }
   // verification head on the exiting token, then verify / rollback
   StageGemv hd = stage_base(h);
@@ -1209,7 +1255,16 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   g.n = cfg->n_stages;
   g.Ls = cfg->pdm_layers;
   g.m = cfg->n_anchors;
-  g.per = g.L / g.n;
+  // stage k runs layers sstart[k] .. sstart[k+1]-1; per = the longest stage
+  // (the number of sub-steps of a stage step)
+  g.per = 0;
+  for (int k = 0, acc = 0; k < g.n; ++k) {
+    const int sz = has_split(cfg) ? cfg->stage_layers[k] : g.L / g.n;
+    g.sstart[k] = acc;
+    acc += sz;
+    g.per = std::max(g.per, sz);
+  }
+  g.sstart[g.n] = g.L;
   g.nslots = g.n + 1;
   g.ctx_cap = L.ctx_cap;
   g.nsplit = L.nsplit;
@@ -1223,9 +1278,10 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   for (int b = 0; b <= SPD_MAX_LAYERS; ++b) g.anchor_of_layer[b] = -1;
   for (int i = 0; i < g.m; ++i) g.anchor_of_layer[cfg->anchors[i]] = i;
   g.anchor_of_layer[0] = -1;  // anchor 0 (embedding) is written at entry
-  // f(k) = max{i : b_i <= lmax(k)}, lmax(k) = min(L, k L/n)
+  // f(k) = max{i : b_i <= lmax(k)}, lmax(k) = layers of the first k stages
+  // (min(L, k L/n) under the uniform split)
   for (int k = 0; k <= g.n; ++k) {
-    const int lmax = std::min(g.L, k * g.per);
+    const int lmax = g.sstart[k];
     int f = 0;
     for (int i = 0; i < g.m; ++i)
       if (cfg->anchors[i] <= lmax) f = i;

@@ -69,6 +69,7 @@ struct StageGemv {
   const void* W[SPD_MAX_STAGES];
   const float* gamma[SPD_MAX_STAGES];  // RMSNorm gain of the input (nullptr: no norm)
   int layer[SPD_MAX_STAGES];           // layer of group g (KV epilogue)
+  int stage[SPD_MAX_STAGES];           // pipeline stage of group g (increasing; GM_STAGE)
   int anchor_idx[SPD_MAX_STAGES];      // anchor to tap after this layer, or -1
   int N, K, units, n_groups, gmode;
   const float* x;
@@ -164,7 +165,9 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
   int n_act, pos_base;
   if (A.gmode == GM_STAGE) {
     if (!C->active) return;
-    n_act = C->a;
+    // the groups whose stage holds a token: a prefix, stages being increasing
+    n_act = 0;
+    for (int k = 0; k < A.n_groups; ++k) n_act += A.stage[k] < C->a ? 1 : 0;
     pos_base = C->t;
   } else if (A.gmode == GM_EXIT) {
     if (!C->active || C->a != g.n) return;
@@ -186,7 +189,8 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
   // grid (at least one workgroup per CU): the step takes about as long, and
   // the draft stream's latency-bound kernels find free CUs
   int nwg = gridDim.x;
-  if (A.gmode == GM_STAGE) nwg = max(min((int)gridDim.x, kStageMinWG), (int)((long long)gridDim.x * n_act / g.n));
+  if (A.gmode == GM_STAGE)
+    nwg = max(min((int)gridDim.x, kStageMinWG), (int)((long long)gridDim.x * n_act / A.n_groups));
   if ((int)blockIdx.x >= nwg) return;
   const long long t0 = T * blockIdx.x / nwg;
   const long long t1 = T * (blockIdx.x + 1) / nwg;
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
     __builtin_amdgcn_sched_barrier(0);
     if (grp != cur) {
       cur = grp;
-      pos = pos_base - grp;
+      pos = pos_base - A.stage[grp];
       const bool fixed = (A.gmode == GM_FIXED || A.gmode == GM_PDMLAST);
       slot = fixed ? 0 : pos % g.nslots;
       const float* x = fixed ? xfix : A.x + (A.x_by_slot ? slot : grp) * A.x_stride;

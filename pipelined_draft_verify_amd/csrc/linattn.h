@@ -36,6 +36,7 @@ __device__ __forceinline__ float elu_plus_one(float x) { return x > 0.f ? x + 1.
 struct LinAttn {
   int mode;                   // LM_STAGE or LM_ROWS
   int layer[SPD_MAX_STAGES];  // stage: layer of each group; rows: layer[0]
+  int stage[SPD_MAX_STAGES];  // stage: pipeline stage of each group (increasing)
   const void* kc;
   const void* vc;
   const float* q;             // [row][Hq * hd], after RoPE
@@ -69,10 +70,10 @@ __global__ __launch_bounds__(kWG) void k_linattn(const LinAttn A) {
     const Ctrl* C = A.ctrl;
     if (!C->active) return;
     const int grp = blockIdx.y;
-    if (grp >= C->a) return;
+    if (A.stage[grp] >= C->a) return;
     layer = A.layer[grp];
     if (!layer_is_linear(g, layer)) return;
-    pos = C->t - grp;
+    pos = C->t - A.stage[grp];
     row = grp;
     nitems = 1;
   } else {

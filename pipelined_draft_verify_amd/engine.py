@@ -37,6 +37,8 @@ def make_config(w, max_ctx: Optional[int] = None) -> A.spd_config:
     c.schedule = A.SPD_SCHED_POST if getattr(w, "schedule", "pre") == "post" else A.SPD_SCHED_PRE
     c.top_k = getattr(w, "top_k", 0)
     c.attn_period = getattr(w, "attn_period", 0)
+    for k, n_k in enumerate(getattr(w, "split", ()) or ()):
+        c.stage_layers[k] = n_k
     return c
 
 

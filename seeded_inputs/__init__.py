@@ -102,6 +102,11 @@ WORKLOADS: Dict[str, Workload] = {
     "4b_n8_post": Workload("4b_n8_post", "bf16", 32, 2560, 20, 4, 128, 9728, 151936, 8, 4,
                            [0, 8, 16, 24, 31], P=512, G=256, policy="forced",
                            p_accept=0.8, seed=2, schedule="post"),
+    # 4B shapes on the pages' non-uniform 4-stage split 5+4;9;9;9 (a 5-layer
+    # first stage, three 9-layer stages, a 4-layer draft module)
+    "4b_split_n4": Workload("4b_split_n4", "bf16", 32, 2560, 20, 4, 128, 9728, 151936, 4, 4,
+                            [0, 8, 16, 24, 31], P=512, G=256, policy="forced",
+                            p_accept=0.8, seed=7, split=(5, 9, 9, 9)),
 }
 
 

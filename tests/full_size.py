@@ -258,7 +258,7 @@ def check_floats(run: dict, view: OracleView, reps) -> dict:
         for i, p in enumerate(range(t, t - a, -1)):  # newest first; depth after the step = i + 1
             if p >= view.N or not view.survived(q, upto=p):
                 continue
-            f = schedule.pattern(i + 1, w.anchors, w.L, w.n)
+            f = schedule.pattern(i + 1, w.anchors, w.L, w.n, w.split)
             for b in range(f + 1):
                 worst["anchors"] = max(worst["anchors"], rel_l2(snap["anchors"][p][b], view.taps[p][b]))
                 seen["anchors"] += 1

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_sizes_match_header_layout():
     # spd_cycle_rec: 12 words + 64 KV lengths
     assert ctypes.sizeof(A.spd_cycle_rec) == 4 * (12 + A.SPD_MAX_LAYERS) == REC_DTYPE.itemsize
-    assert ctypes.sizeof(A.spd_config) == 4 * (10 + A.SPD_MAX_ANCHORS + 4 + 3 + 3)
+    assert ctypes.sizeof(A.spd_config) == 4 * (10 + A.SPD_MAX_ANCHORS + 4 + 3 + 3 + A.SPD_MAX_STAGES)
     assert ctypes.sizeof(A.spd_weights) == 8 * (1 + 6 * A.SPD_MAX_LAYERS + 2 + A.SPD_MAX_ANCHORS
                                                 + 6 * A.SPD_MAX_PDM_LAYERS + 2)
 
@@ -140,3 +140,17 @@ def test_attn_period_limits():
         c.attn_period = p
         with pytest.raises(A.SPDError):
             A.spd_workspace_bytes(c)
+
+
+def test_stage_split_constraints_are_checked():
+    w = si.workload("4b_split_n4")
+    A.spd_workspace_bytes(make_config(w))              # 5 + 9 + 9 + 9 with a 4-layer draft module
+    A.spd_workspace_bytes(make_config(w.replace(Ls=8)))  # as deep as the longest stage
+    A.spd_workspace_bytes(make_config(w.replace(n=3, split=(10, 11, 11))))  # n need not divide L
+    for kw in [dict(split=(5, 9, 9, 8)),                # sums to 31
+               dict(split=(0, 14, 9, 9)),               # an empty stage
+               dict(Ls=10),                             # deeper than the longest stage
+               dict(n=3, split=(5, 9, 9, 9))]:          # more entries than stages
+        with pytest.raises(A.SPDError) as e:
+            A.spd_workspace_bytes(make_config(w.replace(**kw)))
+        assert e.value.code == A.SPD_EINVAL

@@ -74,3 +74,23 @@ def test_post_step_patterns():
     assert post - pre == 2 * 2560 * 2560 * 2
     # full pipeline: post-step depths 8 .. 1 and pre-step depths (8), 7 .. 0 both use all five
     assert bench.cycle_bytes(post_w, _rec(600, 8, 593, 0), 2) == bench.cycle_bytes(pre_w, _rec(600, 8, 593, 1), 2)
+
+
+def test_non_uniform_split():
+    """4b_split_n4 (stages of 5, 9, 9 and 9 layers): active stages stream
+    their own layer counts, and the patterns of depths 4 .. 0 are f = 4, 2,
+    1, 0, 0 (lmax = 32, 23, 14, 5, 0), so the fusion matrices 0, 1, 2 and 4
+    are read: (1 + 2 + 3 + 5) d^2."""
+    w = si.workload("4b_split_n4")
+    t, n = 600, 4
+    sizes = [5, 9, 9, 9]
+    kv_pos = 2 * 4 * 128 * 2
+    kv = sum(sizes[k] * (t - k + 1) * kv_pos for k in range(n))
+    heads = 2 * 151936 * 2560 * 2
+    fc = 11 * 2560 * 2560 * 2
+    draft_layers = 4 * LAYER_4B * 2 + 4 * (t + 1) * kv_pos
+    assert bench.cycle_bytes(w, _rec(t, n, t - n + 1, 1), 2) == 32 * LAYER_4B * 2 + heads + fc + draft_layers + kv
+    # warm-up with one token in flight: stage 0's 5 layers, pattern 0 only
+    want = 5 * LAYER_4B * 2 + 5 * 601 * kv_pos + 2560 * 2560 * 2 + 4 * LAYER_4B * 2 + 151936 * 2560 * 2 \
+        + 4 * 601 * kv_pos
+    assert bench.cycle_bytes(w, _rec(600, 1, -1, 0), 2) == want

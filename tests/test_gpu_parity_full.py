@@ -19,7 +19,8 @@ from tests import full_size as fs
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = ["4b_n8", "9b_n8", "4b_n16", "9b_sample", "4b_n8_post", "9b_sample_topk50", "4b_hybrid_n8"]
+WORKLOADS = ["4b_n8", "9b_n8", "4b_n16", "9b_sample", "4b_n8_post", "9b_sample_topk50", "4b_hybrid_n8",
+             "4b_split_n4"]
 PARTS = ["replay", "verifications", "draft_module_and_floats"]
 _C = {}
 

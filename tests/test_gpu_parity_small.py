@@ -66,6 +66,14 @@ VARIANTS = {
     "post_bf16_gqa_forced": dict(dtype="bf16", L=6, n=3, Hq=8, Hkv=2, F=768, V=500, anchors=[0, 2, 5], Ls=2,
                                  p=0.5, seed=38, schedule="post"),
     "post_deep_n8": dict(L=8, n=8, Ls=1, anchors=[0, 3, 8], G=20, p=0.7, seed=39, schedule="post"),
+    # non-uniform stage splits: sub-steps where some stages have no layer left
+    "split_132_f32": dict(L=6, n=3, split=(1, 3, 2), Ls=2, anchors=[0, 1, 4, 6], p=0.6, seed=57),
+    "split_3122_bf16": dict(dtype="bf16", L=8, n=4, split=(3, 1, 2, 2), Ls=3, anchors=[0, 2, 4, 6, 7], Hq=8,
+                            Hkv=2, F=512, p=0.6, seed=58),
+    "split_213_post_f32": dict(L=6, n=3, split=(2, 1, 3), Ls=3, anchors=[0, 1, 4, 6], p=0.6, seed=59,
+                               schedule="post"),
+    "split_35_hybrid_bf16": dict(dtype="bf16", L=8, n=2, split=(3, 5), Ls=2, anchors=[0, 3, 8], attn_period=4,
+                                 p=0.6, seed=60),
 }
 
 
@@ -91,6 +99,8 @@ def test_variant_matches_oracle(name):
 # temperature sampling with rejection-sampling verification
 SAMPLE_VARIANTS = {
     "f32_T1": dict(dtype="f32", temperature=1.0, seed=40),
+    "split_132_f32_T1": dict(dtype="f32", temperature=1.0, L=6, n=3, split=(1, 3, 2), Ls=2, anchors=[0, 1, 4, 6],
+                             seed=61),
     "f32_T0.3": dict(dtype="f32", temperature=0.3, seed=40),
     "bf16_n4_T0.3": dict(dtype="bf16", temperature=0.3, L=4, n=4, anchors=[0, 1, 2, 3, 4], G=30, seed=41),
     "bf16_gqa_T0.5": dict(dtype="bf16", temperature=0.5, L=6, n=3, Hq=8, Hkv=2, F=768, V=500,
