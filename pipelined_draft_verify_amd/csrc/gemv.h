@@ -7,11 +7,13 @@
 // partial sums are reduced with a butterfly.  Both kernels below use exactly
 // this per-row arithmetic, so a row computed by either gives the same bits.
 //
-//  * k_gemv_stage: the stage-grouped decode GEMV.  Group g is stage g; its
-//    in-flight token's input vector is normalised once per workgroup into
-//    LDS.  The grid is persistent: the tiles of all ACTIVE groups (g < a,
-//    known only on the device) are spread over every workgroup, so warm-up
-//    cycles with few tokens in flight still use the whole chip.
+//  * k_gemv_stage: the stage-grouped decode GEMV.  Group g is pipeline stage
+//    stage[g] (g itself under the uniform split; a non-uniform split leaves
+//    out the stages that have no layer in a sub-step); its in-flight token's
+//    input vector is normalised once per workgroup into LDS.  The grid is
+//    persistent: the tiles of all ACTIVE groups (stage < a, known only on the
+//    device) are spread over every workgroup, so warm-up cycles with few
+//    tokens in flight still use the whole chip.
 //  * k_gemv_rows: up to kRowsMR activation rows share one weight stream
 //    (draft-module rows, prefill chunks, autoregressive decode); the input
 //    rows are staged through LDS in K chunks.

@@ -35,9 +35,15 @@ COPY_BYTES = 1 << 30
 
 
 def kernel_source_hash() -> str:
+    """Hash of the code (comments and blank space removed) of the sources the
+    gate/up GEMV is built from: a comment edit keeps a counter record valid,
+    any code change invalidates it."""
     h = hashlib.sha256()
     for name in ("common.h", "gemv.h"):
-        h.update(open(os.path.join(HERE, "csrc", name), "rb").read())
+        src = open(os.path.join(HERE, "csrc", name)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
