@@ -108,7 +108,7 @@ def main():
                     help="draft-module features before (pre) or after (post) the stage step")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
 
     import torch
