@@ -147,9 +147,13 @@ def test_sampling_matches_oracle(name):
     assert (acc == 1).any() or not need_accepts
 
 
-def test_eager_and_graph_launch_agree():
-    """Host-launched and graph-replayed cycles give bit-identical records and tokens."""
-    w = gpu_workload_tiny(dtype="bf16", L=4, n=4, anchors=[0, 1, 2, 3, 4], G=30, seed=45)
+@pytest.mark.parametrize("split", [(), (1, 2, 3, 2)])
+def test_eager_and_graph_launch_agree(split):
+    """Host-launched and graph-replayed cycles give bit-identical records and
+    tokens (uniform split, and uneven stages whose sub-steps hold different
+    group sets)."""
+    L = sum(split) if split else 4
+    w = gpu_workload_tiny(dtype="bf16", L=L, n=4, anchors=[0, 1, 2, 3, 4], G=30, seed=45, split=split)
     T, W, prompt, uni = _inputs(w)
     ref, _ = ar_greedy(w, W, prompt, w.G)
     from pipelined_draft_verify_amd import SPDEngine
@@ -245,8 +249,9 @@ def test_lossless_forced_natural_and_autoregressive_agree():
     assert tok_nat == [first] + ar
 
 
-def test_rollback_to_prefix_equals_fresh_prefill():
-    w = gpu_workload_tiny(dtype="f32", L=4, n=2, G=16, seed=39)
+@pytest.mark.parametrize("split", [(), (1, 3)])
+def test_rollback_to_prefix_equals_fresh_prefill(split):
+    w = gpu_workload_tiny(dtype="f32", L=4, n=2, G=16, seed=39, split=split)
     T, W, prompt, uni = _inputs(w)
     from pipelined_draft_verify_amd import SPDEngine
 
