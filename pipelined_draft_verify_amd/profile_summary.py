@@ -3,6 +3,7 @@
   python -m pipelined_draft_verify_amd.profile_summary stats <kernel_stats.csv> [--cmd "..."]
   python -m pipelined_draft_verify_amd.profile_summary timeline <kernel_trace.csv> --cycles K [--skip S] [--cmd "..."]
   python -m pipelined_draft_verify_amd.profile_summary traffic <fetch_dir> <write_dir> --cmd "..."
+  python -m pipelined_draft_verify_amd.profile_summary mfma <counter_dir> [--cmd "..."]
 
 `timeline` takes K cycles of a kernel trace, ending --skip cycles before its
 end (a cycle starts at each k_entry dispatch), and prints, per stream and per kernel/grid, the launches,
@@ -146,6 +147,42 @@ def traffic(fetch_dir: str, write_dir: str):
     return rec
 
 
+MFMA_PEAK_BF16 = 2.5e15  # dense bf16 matrix-core peak of one MI355X, flop/s
+
+
+def mfma(d: str) -> str:
+    """Matrix-core use per kernel and grid, from one counter pass with the
+    derived counters MfmaUtil (busy share of all SIMDs' matrix cores, %) and
+    MfmaFlopsBF16, over the dispatches after the first k_entry (the cycles;
+    prefill and the reference decode come before it)."""
+    per = {}
+    for r in _counter_rows(d):
+        e = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "grid": r["Grid_Size"],
+                                                   "t": (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))})
+        e[r["Counter_Name"]] = float(r["Counter_Value"])
+    ids = sorted(per)
+    first = next((i for i in ids if "k_entry" in per[i]["name"]), None)
+    if first is None:
+        raise ValueError("no k_entry dispatch: run with k_entry in the kernel filter")
+    agg = {}
+    for i in ids:
+        e = per[i]
+        if i < first or "k_entry" in e["name"]:
+            continue
+        a = agg.setdefault((_short(e["name"]), e["grid"]), [0, 0.0, 0.0, 0.0])
+        a[0] += 1
+        a[1] += e.get("MfmaUtil", 0.0)
+        a[2] += e.get("MfmaFlopsBF16", 0.0)
+        a[3] += (e["t"][1] - e["t"][0]) * 1e-9
+    out = [f"{'kernel':30s} {'grid':>8s} {'calls':>6s} {'MFMA util %':>11s} {'GFLOP/call':>10s} "
+           f"{'us/call':>8s} {'TFLOP/s':>8s} {'of peak':>8s}"]
+    for (name, grid), (n, u, f, t) in sorted(agg.items(), key=lambda kv: -kv[1][3]):
+        rate = f / t if t > 0 else 0.0
+        out.append(f"{name[:30]:30s} {grid:>8s} {n:6d} {u / n:11.2f} {f / n / 1e9:10.3f} {t / n * 1e6:8.2f} "
+                   f"{rate / 1e12:8.1f} {rate / MFMA_PEAK_BF16:8.4f}")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -162,6 +199,9 @@ def main(argv=None):
     b.add_argument("write_dir")
     b.add_argument("--cmd", default="")
     b.add_argument("--write-json", action="store_true")
+    mf = sub.add_parser("mfma")
+    mf.add_argument("dir")
+    mf.add_argument("--cmd", default="")
     args = ap.parse_args(argv)
     if args.what == "stats":
         if args.cmd:
@@ -171,6 +211,10 @@ def main(argv=None):
         if args.cmd:
             print(f"command: {args.cmd}")
         print(timeline(args.csv, args.cycles, args.skip))
+    elif args.what == "mfma":
+        if args.cmd:
+            print(f"command: {args.cmd}")
+        print(mfma(args.dir))
     else:
         rec = traffic(args.fetch_dir, args.write_dir)
         rec["command"] = args.cmd

@@ -86,3 +86,29 @@ def test_committed_traffic_record_matches_the_kernel_sources():
     rec = json.load(open(ps.TRAFFIC_JSON))
     assert rec["source_hash"] == ps.kernel_source_hash()
     assert rec["traffic_bytes_per_launch"] > 0
+
+
+def test_mfma_summary_counts_only_the_cycles(tmp_path):
+    """Dispatches before the first k_entry (prefill) are left out; per kernel
+    and grid the mean utilisation, operations per call and rate."""
+    d = tmp_path / "m"
+    os.makedirs(d)
+    fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value", "Start_Timestamp",
+              "End_Timestamp"]
+    mm = "void spd::k_mfma_gemv<2, 1, 256>(spd::MfmaArgs)"
+    rows = [(1, mm, 77824, 50.0, 9e9, 0, 10_000),                       # prefill: ignored
+            (2, "void spd::k_entry<unsigned short>(spd::Ctrl*)", 256, 0.0, 0.0, 20_000, 25_000),
+            (3, mm, 77824, 2.0, 3e9, 30_000, 60_000),
+            (4, mm, 77824, 4.0, 3e9, 70_000, 100_000)]
+    with open(d / "m_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for i, name, grid, util, flops, t0, t1 in rows:
+            for cn, cv in [("MfmaUtil", util), ("MfmaFlopsBF16", flops)]:
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Grid_Size": grid, "Counter_Name": cn,
+                            "Counter_Value": cv, "Start_Timestamp": t0, "End_Timestamp": t1})
+    lines = ps.mfma(str(d)).splitlines()
+    assert len(lines) == 2
+    # 2 calls, util (2 + 4) / 2 = 3 %, 3 GFLOP each over 30 us = 100 TFLOP/s = 0.04 of 2.5 PFLOP/s
+    assert lines[1].split() == ["k_mfma_gemv<2,", "1,", "256>", "77824", "2", "3.00", "3.000", "30.00", "100.0",
+                                "0.0400"]
