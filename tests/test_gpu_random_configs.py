@@ -1,0 +1,74 @@
+"""GPU parity over seeded random small configurations.
+
+Each case draws a valid shape and mode from a fixed seed -- dtype, stage count,
+uniform or uneven stage split, draft-module depth, anchor set, head layout,
+vocabulary, greedy with forced drafts or temperature sampling (optionally
+top-k), pre- or post-step drafting, hybrid linear-attention layers -- and must
+agree with the oracle cycle by cycle as in the hand-picked small variants.
+The point is the combinations no single variant covers.
+"""
+import numpy as np
+import pytest
+
+from oracle import SPDOracle, ar_greedy
+from tests.gpu_common import compare_logs, gpu_workload_tiny, run_gpu, teacher_of
+from tests.test_gpu_parity_small import STOL, TOL, _inputs, _oracle
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 48
+
+
+def _draw(i):
+    rng = np.random.default_rng(2026 + i)
+    n = int(rng.choice([1, 2, 3, 4, 6]))
+    if rng.random() < 0.5:
+        L = n * int(rng.integers(1, 4))
+        split = ()
+    else:
+        L = int(rng.integers(n, n + 7))
+        cuts = sorted(rng.choice(np.arange(1, L), size=n - 1, replace=False)) if n > 1 else []
+        edges = [0] + [int(c) for c in cuts] + [L]
+        split = tuple(edges[k + 1] - edges[k] for k in range(n))
+    longest = max(split) if split else L // n
+    Ls = int(rng.integers(1, min(longest, 8) + 1))
+    inner = sorted(set(int(b) for b in rng.integers(1, L + 1, size=int(rng.integers(0, 5)))))
+    anchors = [0] + inner[:7]
+    Hq, Hkv, hd = [(4, 2, 64), (4, 4, 64), (8, 2, 64), (2, 1, 128), (4, 1, 128)][int(rng.integers(0, 5))]
+    kw = dict(dtype=str(rng.choice(["f32", "bf16"])), L=L, n=n, Ls=Ls, anchors=anchors, Hq=Hq, Hkv=Hkv, hd=hd,
+              d=int(rng.choice([256, 512])), F=int(rng.choice([512, 768])), V=int(rng.choice([300, 997, 2048])),
+              P=int(rng.integers(5, 41)), G=int(rng.integers(8, 25)), seed=100 + i, split=split)
+    if n >= 2 and rng.random() < 0.25:
+        kw["schedule"] = "post"
+    if rng.random() < 0.3:
+        kw["attn_period"] = int(rng.choice([2, 4]))
+    if rng.random() < 0.35:
+        kw.update(mode="sample", temperature=float(rng.choice([0.5, 1.0])), top_k=int(rng.choice([0, 0, 8])))
+        p = None
+    else:
+        p = float(rng.choice([0.3, 0.7]))
+    return kw, p
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_configuration_matches_oracle(i):
+    kw, p = _draw(i)
+    print("case", i, kw, "p", p, flush=True)
+    w = gpu_workload_tiny(**kw)
+    T, W, prompt, uni = _inputs(w)
+    if w.mode == "sample":
+        eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni)
+        eng.close()
+        o = SPDOracle(w, W, uniforms=uni, teacher=teacher_of(recs, first), tol=TOL[w.dtype],
+                      sample_tol=STOL[w.dtype])
+        otoks, ologs = o.run(prompt, w.G)
+    else:
+        ref, _ = ar_greedy(w, W, prompt, w.G)
+        eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni, ref=ref, p_accept=p)
+        eng.close()
+        o, otoks, ologs = _oracle(w, W, prompt, uni, recs, first, ref=ref, p=p)
+        assert toks == ref
+    assert not o.dec.mismatch, o.dec.mismatch
+    assert len(o.dec.adopted) <= 2, o.dec.adopted
+    assert toks == otoks
+    compare_logs(recs, ologs, w.L)
