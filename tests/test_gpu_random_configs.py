@@ -5,7 +5,9 @@ uniform or uneven stage split, draft-module depth, anchor set, head layout,
 vocabulary, greedy with forced drafts or temperature sampling (optionally
 top-k), pre- or post-step drafting, hybrid linear-attention layers -- and must
 agree with the oracle cycle by cycle as in the hand-picked small variants.
-The point is the combinations no single variant covers.
+The point is the combinations no single variant covers.  Three medium cases
+(widths 1024-2048, prompts of 260-620 tokens, vocabularies up to 32000) add
+several tiles per stage group and multi-split attention.
 """
 import numpy as np
 import pytest
@@ -52,10 +54,39 @@ def _draw(i):
     return kw, p
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
-def test_random_configuration_matches_oracle(i):
-    kw, p = _draw(i)
-    print("case", i, kw, "p", p, flush=True)
+def _draw_medium(i):
+    """Larger shapes: several tiles per stage group, prompts long enough for
+    two or three attention splits, vocabularies of several sampler superblocks."""
+    rng = np.random.default_rng(5000 + i)
+    n = int(rng.choice([2, 4, 8]))
+    L = 8 if n < 8 else 8 * int(rng.integers(1, 3))
+    split = ()
+    if n < 8 and rng.random() < 0.5:
+        cuts = sorted(rng.choice(np.arange(1, L), size=n - 1, replace=False))
+        edges = [0] + [int(c) for c in cuts] + [L]
+        split = tuple(edges[k + 1] - edges[k] for k in range(n))
+    longest = max(split) if split else L // n
+    Hq, Hkv, hd = [(16, 4, 128), (8, 8, 128), (32, 8, 64)][int(rng.integers(0, 3))]
+    kw = dict(dtype="bf16", L=L, n=n, Ls=int(rng.integers(1, longest + 1)),
+              anchors=[0] + sorted(set(int(b) for b in rng.integers(1, L + 1, size=3))),
+              Hq=Hq, Hkv=Hkv, hd=hd, d=int(rng.choice([1024, 2048])), F=int(rng.choice([2048, 4096])),
+              V=int(rng.choice([4096, 32000])), P=int(rng.integers(260, 620)), G=int(rng.integers(10, 17)),
+              seed=300 + i, split=split)
+    if rng.random() < 0.4:
+        kw.update(mode="sample", temperature=1.0, top_k=int(rng.choice([0, 50])))
+        p = None
+    else:
+        p = float(rng.choice([0.5, 0.8]))
+    return kw, p
+
+
+CASES = [("small", i) for i in range(N_CASES)] + [("medium", i) for i in range(3)]
+
+
+@pytest.mark.parametrize("kind,i", CASES)
+def test_random_configuration_matches_oracle(kind, i):
+    kw, p = (_draw if kind == "small" else _draw_medium)(i)
+    print("case", kind, i, kw, "p", p, flush=True)
     w = gpu_workload_tiny(**kw)
     T, W, prompt, uni = _inputs(w)
     if w.mode == "sample":
