@@ -235,7 +235,7 @@ struct spd_handle {
   Geo g;
   Layout lay;
   hipStream_t ss, ps;
-  hipEvent_t ev_entry, ev_pdm;
+  hipEvent_t ev_entry = nullptr, ev_pdm = nullptr;
   char* ws;
   Ctrl* ctrl;
   int32_t *kv_len, *tokens, *dring;
@@ -1340,6 +1340,8 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
 
   auto fail = [&](hipError_t e) {
     h->hip_err = (int)e;
+    if (h->ev_entry) (void)hipEventDestroy(h->ev_entry);
+    if (h->ev_pdm) (void)hipEventDestroy(h->ev_pdm);
     delete h;
     return SPD_EHIP;
   };
