@@ -285,6 +285,12 @@ struct spd_handle {
     }                                         \
   } while (0)
 
+// Record a HIP error in the handle; the ABI result for it.
+int hip_fail(spd_t* h, hipError_t e) {
+  h->hip_err = (int)e;
+  return SPD_EHIP;
+}
+
 namespace {
 
 hipEvent_t pool_event(spd_t* h) {
@@ -1019,20 +1025,26 @@ int capture_graphs(spd_t* h) {
   if (h->gx_pdm) (void)hipGraphExecDestroy(h->gx_pdm);
   h->gx_stage = h->gx_pdm = nullptr;
   hipGraph_t gs = nullptr, gp = nullptr;
-  HIPCHK(h, hipStreamBeginCapture(h->ps, hipStreamCaptureModeThreadLocal));
+  // the captured graphs are released on every path; the executable graphs
+  // stay with the handle (spd_destroy or the next capture releases them)
+  auto done = [&](int r) {
+    if (gp) (void)hipGraphDestroy(gp);
+    if (gs) (void)hipGraphDestroy(gs);
+    return r;
+  };
+  hipError_t e;
+  if ((e = hipStreamBeginCapture(h->ps, hipStreamCaptureModeThreadLocal)) != hipSuccess) return done(hip_fail(h, e));
   int r = pdm_chain<WT>(h, h->ps);
-  HIPCHK(h, hipStreamEndCapture(h->ps, &gp));
-  if (r) return r;
-  HIPCHK(h, hipStreamBeginCapture(h->ss, hipStreamCaptureModeThreadLocal));
+  if ((e = hipStreamEndCapture(h->ps, &gp)) != hipSuccess) return done(hip_fail(h, e));
+  if (r) return done(r);
+  if ((e = hipStreamBeginCapture(h->ss, hipStreamCaptureModeThreadLocal)) != hipSuccess) return done(hip_fail(h, e));
   r = stage_chain<WT>(h, h->ss, false);
-  HIPCHK(h, hipStreamEndCapture(h->ss, &gs));
-  if (r) return r;
-  HIPCHK(h, hipGraphInstantiate(&h->gx_pdm, gp, nullptr, nullptr, 0));
-  HIPCHK(h, hipGraphInstantiate(&h->gx_stage, gs, nullptr, nullptr, 0));
-  (void)hipGraphDestroy(gp);
-  (void)hipGraphDestroy(gs);
+  if ((e = hipStreamEndCapture(h->ss, &gs)) != hipSuccess) return done(hip_fail(h, e));
+  if (r) return done(r);
+  if ((e = hipGraphInstantiate(&h->gx_pdm, gp, nullptr, nullptr, 0)) != hipSuccess) return done(hip_fail(h, e));
+  if ((e = hipGraphInstantiate(&h->gx_stage, gs, nullptr, nullptr, 0)) != hipSuccess) return done(hip_fail(h, e));
   h->graphs_valid = 1;
-  return SPD_OK;
+  return done(SPD_OK);
 }
 
 template <typename WT>
