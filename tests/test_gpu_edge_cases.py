@@ -15,7 +15,7 @@
     that holds at any size -- natural and forced drafts emit exactly the
     GPU's own autoregressive greedy decode;
   * the largest vocabulary (SPD_MAX_VOCAB = 2^20 ids) in sample mode, dense
-    and with top-64 truncation.
+    and with top-64 truncation, and the smallest (2 and 3 ids).
 Every run through the oracle must agree cycle by cycle as in the other
 small-workload parity tests.
 """
@@ -142,4 +142,34 @@ def test_sampling_at_the_largest_vocabulary(top_k):
     otoks, ologs = o.run(prompt, w.G)
     assert not o.dec.mismatch, o.dec.mismatch
     assert toks == otoks
+    compare_logs(recs, ologs, w.L)
+
+
+@pytest.mark.parametrize("V,mode,top_k", [(2, "greedy", 0), (3, "sample", 0), (3, "sample", 2)])
+def test_smallest_vocabularies(V, mode, top_k):
+    """V = 2 and 3: one partial block of the sampler and of the argmax, a
+    top-k list longer than half the vocabulary."""
+    from tests.test_gpu_parity_small import STOL, TOL
+    from tests.gpu_common import teacher_of
+    from oracle import SPDOracle
+
+    kw = dict(V=V, L=4, n=2, G=16, seed=70 + V + top_k)
+    if mode == "sample":
+        kw.update(mode="sample", temperature=1.0, top_k=top_k)
+    w = gpu_workload_tiny(**kw)
+    T, W, prompt, uni = _inputs(w)
+    if mode == "sample":
+        eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni)
+        eng.close()
+        o = SPDOracle(w, W, uniforms=uni, teacher=teacher_of(recs, first), tol=TOL[w.dtype],
+                      sample_tol=STOL[w.dtype])
+        otoks, ologs = o.run(prompt, w.G)
+    else:
+        ref, _ = ar_greedy(w, W, prompt, w.G)
+        eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni, ref=ref, p_accept=0.5)
+        eng.close()
+        o, otoks, ologs = _oracle(w, W, prompt, uni, recs, first, ref=ref, p=0.5)
+    assert not o.dec.mismatch, o.dec.mismatch
+    assert toks == otoks
+    assert all(0 <= t < V for t in toks)
     compare_logs(recs, ologs, w.L)
