@@ -31,30 +31,34 @@ def top_k_ids(logits: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[:k])
 
 
-def top_k_margin(logits: np.ndarray, k: int) -> float:
-    """Logit gap between the k-th and the (k+1)-th largest logit: how firmly
-    the top-k set is decided (inf without truncation).  The set is decided by
-    logit comparisons exactly like an argmax, so a second implementation may
-    legitimately keep a different set when this gap is within its argmax
-    tolerance."""
+def top_k_set_gap(logits: np.ndarray, ids) -> float:
+    """How far the id set `ids` is from being a top-|ids| set of `logits`:
+    the largest logit left out minus the smallest logit kept (0 when no
+    excluded id beats a kept one).  The set is decided by logit comparisons
+    like an argmax, so a second implementation whose logits differ by rounding
+    may keep another set; it is a valid top-k choice when this gap is within
+    the argmax tolerance (for k = 1 this is the argmax near-tie rule)."""
     l = np.asarray(logits, np.float32)
-    if k <= 0 or k >= len(l):
-        return float("inf")
-    s = np.sort(l)[::-1]
-    return float(s[k - 1] - s[k])
+    ids = np.asarray(ids, np.int64)
+    if len(ids) == 0 or len(ids) >= len(l):
+        return 0.0
+    out = np.ones(len(l), bool)
+    out[ids] = False
+    return float(max(0.0, float(l[out].max()) - float(l[ids].min())))
 
 
-def softmax_weights(logits: np.ndarray, temperature: float = 1.0, top_k: int = 0):
+def softmax_weights(logits: np.ndarray, temperature: float = 1.0, top_k: int = 0, keep=None):
     """(w float32, Z float64): unnormalised softmax weights and their sum;
-    with top_k > 0 only the top-k ids keep their weight."""
+    with top_k > 0 only the top-k ids keep their weight (or, when `keep` is
+    given, the ids it lists: a kept set decided elsewhere)."""
     l = logits.astype(np.float32)
     if temperature != 1.0:
         l = l / np.float32(temperature)
     w = np.exp(l - l.max()).astype(np.float32)
-    if 0 < top_k < len(w):
-        keep = np.zeros(len(w), bool)
-        keep[top_k_ids(logits, top_k)] = True
-        w = np.where(keep, w, np.float32(0)).astype(np.float32)
+    if keep is not None or 0 < top_k < len(w):
+        mask = np.zeros(len(w), bool)
+        mask[top_k_ids(logits, top_k) if keep is None else np.asarray(keep, np.int64)] = True
+        w = np.where(mask, w, np.float32(0)).astype(np.float32)
     return w, float(np.sum(w.astype(np.float64)))
 
 

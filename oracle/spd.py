@@ -98,7 +98,8 @@ class Decisions:
     Greedy argmax picks the lowest id among equal maxima.  With a teacher (the
     decisions another implementation took, keyed by (kind, cycle)), a differing
     choice is adopted when it is also valid within `tol` -- a logit within tol
-    of the maximum (`tol`, logit units), or a sampling threshold within
+    of the maximum (`tol`, logit units), a top-k kept set whose excluded ids
+    beat no kept id by more than tol, or a sampling threshold within
     `sample_tol` of the boundary it falls on (as a fraction of the total mass,
     or for the accept test of Q(x)) -- and recorded; otherwise it is recorded
     as a mismatch.  Without a teacher nothing is adopted.
@@ -126,26 +127,38 @@ class Decisions:
         y = int(np.argmax(logits))
         return self._teach(key, y, lambda t: float(logits[y] - logits[t]), self.tol)
 
-    def sample(self, key, weights: np.ndarray, u: float, set_margin: float = float("inf")) -> int:
-        """A draw; `set_margin` (top-k: the gap of the k-th and (k+1)-th
-        logits the weights were truncated with) within `tol` also makes a
-        differing draw a near-tie: the kept set itself was a near-tie."""
+    def kept_set(self, key, logits: np.ndarray, k: int) -> np.ndarray:
+        """Top-k kept ids (ascending) of `logits`; a teacher's set replaces the
+        oracle's when it is a valid top-k choice within `tol`."""
+        mine = sampling.top_k_ids(logits, k)
+        if self.teacher is None or key not in self.teacher:
+            return mine
+        theirs = np.sort(np.asarray(self.teacher[key], np.int64))
+        if len(theirs) == len(mine) and np.array_equal(theirs, mine):
+            return mine
+        ok_size = len(theirs) == len(mine) and len(np.unique(theirs)) == len(theirs) and \
+            theirs.min() >= 0 and theirs.max() < len(logits)
+        gap = sampling.top_k_set_gap(logits, theirs) if ok_size else float("inf")
+        rec = (key, "set", len(np.setdiff1d(theirs, mine)), gap)
+        (self.adopted if gap <= self.tol else self.mismatch).append(rec)
+        return theirs if ok_size else mine
+
+    def sample(self, key, weights: np.ndarray, u: float) -> int:
+        """A draw by inverse CDF; a differing teacher draw must lie within
+        `sample_tol` (fraction of the total mass) of its interval."""
         i, _ = sampling.inverse_cdf(weights, u)
         c = np.cumsum(weights.astype(np.float64))
         thr = np.float64(u) * c[-1]
 
         def gap(t):
-            if set_margin <= self.tol:
-                return 0.0
-            lo = c[t - 1] if (t > 0 and t < len(c)) else 0.0
-            hi = c[t] if t < len(c) else c[-1]
-            return float(max(lo - thr, thr - hi, 0.0) / c[-1])
+            if not 0 <= t < len(c):
+                return float("inf")
+            lo = c[t - 1] if t > 0 else 0.0
+            return float(max(lo - thr, thr - c[t], 0.0) / c[-1])
         return self._teach(key, i, gap, self.sample_tol)
 
-    def accept(self, key, p_w, p_Z, q_w, q_Z, x, u, set_margin: float = float("inf")) -> bool:
+    def accept(self, key, p_w, p_Z, q_w, q_Z, x, u) -> bool:
         acc, g = sampling.accept_test(p_w, p_Z, q_w, q_Z, x, u)
-        if set_margin <= self.tol:
-            g = 0.0
         return bool(self._teach(key, acc, lambda t: g, self.sample_tol))
 
 
@@ -197,9 +210,8 @@ class SPDOracle:
                 full.append(taps)
         lg = self.target.logits(h)
         if self.sample:
-            pw, _ = sampling.softmax_weights(lg, self.T, self.top_k)
-            first = self.dec.sample(("first", 0), pw, float(self.u[self.P, U_TARGET]),
-                                    sampling.top_k_margin(lg, self.top_k))
+            pw, _ = sampling.softmax_weights(lg, self.T, keep=self._keep(("pset_first", 0), lg))
+            first = self.dec.sample(("first", 0), pw, float(self.u[self.P, U_TARGET]))
         else:
             first = self.dec.argmax(("first", 0), lg)
         G = np.stack([self.pdm.feature(full[p], n) for p in range(self.P)])
@@ -256,15 +268,14 @@ class SPDOracle:
             assert (j + 1) in self.drafts, "successor of an exiting token must be a draft"
             xd, qinfo = self.drafts.pop(j + 1)
             if self.sample:
-                pw, pZ = sampling.softmax_weights(lg, self.T, self.top_k)
-                sm = min(sampling.top_k_margin(lg, self.top_k), qinfo[2])
+                pw, pZ = sampling.softmax_weights(lg, self.T, keep=self._keep(("pset", c), lg))
                 ok = self.dec.accept(("accept", c), pw, pZ, qinfo[0], qinfo[1], xd,
-                                     float(self.u[j + 1, U_ACCEPT]), sm)
+                                     float(self.u[j + 1, U_ACCEPT]))
                 if ok:
                     y = xd
                 else:
                     r = sampling.residual(pw, pZ, qinfo[0], qinfo[1])
-                    y = self.dec.sample(("resample", c), r, float(self.u[j + 1, U_RESAMPLE]), sm)
+                    y = self.dec.sample(("resample", c), r, float(self.u[j + 1, U_RESAMPLE]))
                 accept = int(ok)
             else:
                 y = self.dec.argmax(("y", c), lg)
@@ -313,6 +324,12 @@ class SPDOracle:
         self.ncycles += 1
         return rec
 
+    def _keep(self, key, logits):
+        """Kept ids of a top-k truncated distribution (None: the whole vocabulary)."""
+        if not 0 < self.top_k < self.V:
+            return None
+        return self.dec.kept_set(key, logits, self.top_k)
+
     def _draft(self, c: int, t: int, rows, commit: bool):
         """Draft-module step over the trailing rows [(position, depth)]: the
         features g(p, k), the Ls layers over committed + trailing rows, the
@@ -328,11 +345,10 @@ class SPDOracle:
         if self.hook is not None:
             self.hook("pdm", dict(cycle=c, rows=rows, G=Gm, X=X, logits=pl))
         if self.sample:
-            qw, qZ = sampling.softmax_weights(pl, self.T, self.top_k)
-            qm = sampling.top_k_margin(pl, self.top_k)
-            d_raw = self.dec.sample(("draft", c), qw, float(self.u[t + 1, U_DRAFT]), qm)
+            qw, qZ = sampling.softmax_weights(pl, self.T, keep=self._keep(("qset", c), pl))
+            d_raw = self.dec.sample(("draft", c), qw, float(self.u[t + 1, U_DRAFT]))
             d = d_raw
-            self.drafts[t + 1] = (d, (qw, qZ, qm))
+            self.drafts[t + 1] = (d, (qw, qZ))
         else:
             d_raw = self.dec.argmax(("pdm", c), pl)
             d = int(self.policy.draft(t + 1, d_raw))

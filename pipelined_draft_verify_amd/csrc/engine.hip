@@ -1021,6 +1021,9 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
 template <typename WT>
 int capture_graphs(spd_t* h) {
   if (h->graphs_valid) return SPD_OK;
+  // cycles already enqueued may still be running the old executables
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  HIPCHK(h, hipStreamSynchronize(h->ps));
   if (h->gx_stage) (void)hipGraphExecDestroy(h->gx_stage);
   if (h->gx_pdm) (void)hipGraphExecDestroy(h->gx_pdm);
   h->gx_stage = h->gx_pdm = nullptr;

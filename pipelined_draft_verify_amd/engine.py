@@ -93,11 +93,13 @@ class SPDEngine:
     # -- policy / inputs ---------------------------------------------------
     def set_uniforms(self, uni: np.ndarray) -> None:
         t = self.torch.from_numpy(np.ascontiguousarray(uni, dtype=np.float32)).to(self.device)
+        self.sync(raise_on_error=False)  # enqueued cycles may still read the old table
         self.uni = t
         A.spd_set_uniforms(self.h, t.data_ptr(), t.shape[0])
 
     def set_forced(self, ref_tokens, p_accept: float) -> None:
         t = self.torch.tensor(np.asarray(ref_tokens, dtype=np.int32), device=self.device)
+        self.sync(raise_on_error=False)  # enqueued cycles may still read the old reference
         self.ref = t
         A.spd_set_draft_policy(self.h, A.SPD_DRAFT_FORCED, float(p_accept), t.data_ptr(), t.numel())
 

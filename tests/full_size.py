@@ -16,10 +16,13 @@ plus floating-point state at two stopping points:
    (so that the forward's anchors are theirs): the oracle rebuilds the
    trailing rows' features at their depths, runs its layers over the
    committed prefix (one matrix pass over every position's full-depth
-   feature) plus those rows, and its head.  Under sampling, each checked
+   feature) plus those rows, and its head.  Under sampling, EVERY
    verification recomputes Q at the cycle that drafted the verified position
    and retakes the draw, the accept test and the residual redraw with the
-   same seeded uniforms.
+   same seeded uniforms.  Under top-k, the kept sets the GPU used (the top-k
+   ids of its own logits, read back in a second, cycle-by-cycle generation
+   that must reproduce the first bit for bit) must be valid top-k choices of
+   the oracle's logits, and the draws are retaken on those sets.
 
 The GPU side runs exactly as the benchmark times it: weights generated on the
 device, graph-launched cycles, the forced-acceptance reference from the
@@ -76,6 +79,10 @@ def gpu_run(name: str) -> dict:
     eng.set_uniforms(uni)
     prompt = si.make_prompt(w)
     first = int(eng.prefill(prompt))
+    first_set = None
+    if w.mode == "sample" and w.top_k:
+        from oracle.sampling import top_k_ids
+        first_set = top_k_ids(eng.logits(), w.top_k)  # the prefill's logits
     ref = None
     if w.mode == "greedy":
         ar = eng.generate_ar(w.G - 1)
@@ -94,13 +101,47 @@ def gpu_run(name: str) -> dict:
     toks = eng.tokens(0, w.P + w.G)
     end = _snapshot(eng, recs)
     end["kv"] = {l: (eng.kv(l, "k"), eng.kv(l, "v")) for l in sorted({0, w.L // 2, w.L - 1})}
+    sets = None
+    if first_set is not None:
+        sets = _topk_sets(eng, w, first, recs)
+        sets[("pset_first", 0)] = first_set
     eng.close()
     del eng
     flat = si.weights_numpy_f32(T)
     del T
     torch.cuda.empty_cache()
     return dict(w=w, W=si.nest_weights(flat, w), prompt=prompt, uni=uni, first=first, ref=ref,
-                recs=recs, toks=[int(x) for x in toks], mid=mid, end=end)
+                recs=recs, toks=[int(x) for x in toks], mid=mid, end=end, sets=sets)
+
+
+def _topk_sets(eng, w, first, recs):
+    """The generation again, one cycle at a time, reading the logits behind
+    every top-k truncation: the kept sets (top-k ids of the GPU's logits,
+    ties to the lower id).  Its records must equal the first run's."""
+    from oracle.sampling import top_k_ids
+
+    eng.rollback(w.P, first)
+    sets = {}
+    out = []
+    while True:
+        buf = eng.enqueue(1)
+        st = eng.sync()
+        r = eng.records_of(buf)
+        if r["flags"][0] & IDLE:
+            break
+        c = len(out)
+        sets[("qset", c)] = top_k_ids(eng.pdm_logits(), w.top_k)
+        if r["exit_pos"][0] >= 0:
+            sets[("pset", c)] = top_k_ids(eng.logits(), w.top_k)
+        out.append(r)
+        if st.done:
+            break
+    again = np.concatenate(out)
+    a, b = recs.copy(), again.copy()
+    a["cycle"] -= a["cycle"][0]
+    b["cycle"] -= b["cycle"][0]
+    assert a.tobytes() == b.tobytes(), "cycle-by-cycle generation differs from the graph-launched one"
+    return sets
 
 
 def replay(run: dict):
@@ -150,6 +191,17 @@ class OracleView:
 
     def pdm_logits(self, q: dict) -> np.ndarray:
         """Draft-module logits of the cycle of replay record q (rows row0..t)."""
+        return self.pdm.logits(self.pdm_last_row(q))
+
+    def pdm_head_rows(self, X: np.ndarray) -> np.ndarray:
+        """The draft head over many final rows at once: [M, V]."""
+        from oracle.layers import rmsnorm
+        W = self.pdm.W
+        U = np.stack([rmsnorm(x, W["pdm_final_norm"], self.w.eps) for x in X])
+        return (U @ W["pdm_lm_head"].T).astype(np.float32)
+
+    def pdm_last_row(self, q: dict) -> np.ndarray:
+        """Final draft-module row (before the head) of the cycle of replay record q."""
         w, pdm = self.w, self.pdm
         row0, t = q["row0"], q["t"]
         if w.schedule == "post":
@@ -167,7 +219,7 @@ class OracleView:
             for kv, (K, V) in zip(pdm.kv, saved):
                 kv.K[row0:t + 1] = K
                 kv.V[row0:t + 1] = V
-        return pdm.logits(X[-1])
+        return X[-1]
 
 
 def check_verifications(run: dict, view: OracleView, reps) -> Decisions:
@@ -205,37 +257,49 @@ def check_draft_module(run: dict, view: OracleView, reps, k: int = 32) -> Decisi
     return dec
 
 
-def check_sampling(run: dict, view: OracleView, reps, k: int = 32) -> Decisions:
-    """Sampling: the first token, and at sampled verifications the draft draw
-    from Q, the accept test u*Q(x) < P(x) and the residual redraw."""
+def check_sampling(run: dict, view: OracleView, reps, chunk: int = 32, progress=None) -> Decisions:
+    """Sampling: the first token, and at EVERY verification the draft draw
+    from Q (recomputed at the cycle that drafted the verified position), the
+    accept test u*Q(x) < P(x) and the residual redraw.  Under top-k the
+    GPU's kept sets come in as teacher decisions: each must be a valid top-k
+    choice of the oracle's logits, and the draws are retaken on it."""
     w, recs, uni = run["w"], run["recs"], run["uni"]
-    T = w.temperature
-    teacher = {("first", 0): run["first"]}
+    T, k = w.temperature, w.top_k
+    teacher = dict(run.get("sets") or {})
+    teacher[("first", 0)] = run["first"]
     dec = Decisions(teacher, TOL[w.dtype], STOL[w.dtype])
+
+    def keep(key, logits):
+        return dec.kept_set(key, logits, k) if 0 < k < w.V else None
+
     l0 = view.logits_at(w.P - 1)
-    pw0, _ = sampling.softmax_weights(l0, T, w.top_k)
-    dec.sample(("first", 0), pw0, float(uni[w.P, U_TARGET]), sampling.top_k_margin(l0, w.top_k))
+    pw0, _ = sampling.softmax_weights(l0, T, keep=keep(("pset_first", 0), l0))
+    dec.sample(("first", 0), pw0, float(uni[w.P, U_TARGET]))
     exits = [i for i, q in enumerate(reps) if q["exit_pos"] >= 0]
-    chosen = sample_indices(exits, k)
-    for i in chosen:
-        q = reps[i]
-        j, c2 = q["exit_pos"], q["drafted_at"]
-        qd = reps[c2]
-        assert qd["t"] == j and view.survived(qd)
-        ql = view.pdm_logits(qd)
-        qw, qZ = sampling.softmax_weights(ql, T, w.top_k)
-        qm = sampling.top_k_margin(ql, w.top_k)
-        teacher[("draft", c2)] = int(recs[c2]["pdm_argmax"])
-        dec.sample(("draft", c2), qw, float(uni[j + 1, U_DRAFT]), qm)
-        pl = view.logits_at(j)
-        pw, pZ = sampling.softmax_weights(pl, T, w.top_k)
-        sm = min(qm, sampling.top_k_margin(pl, w.top_k))
-        teacher[("accept", i)] = bool(recs[i]["accepted"])
-        ok = dec.accept(("accept", i), pw, pZ, qw, qZ, qd["draft"], float(uni[j + 1, U_ACCEPT]), sm)
-        if not ok:
-            teacher[("resample", i)] = int(recs[i]["target_token"])
-            dec.sample(("resample", i), sampling.residual(pw, pZ, qw, qZ), float(uni[j + 1, U_RESAMPLE]), sm)
-    dec.checked = len(chosen)
+    for b0 in range(0, len(exits), chunk):
+        batch = exits[b0:b0 + chunk]
+        rows = []
+        for i in batch:
+            qd = reps[reps[i]["drafted_at"]]
+            assert qd["t"] == reps[i]["exit_pos"] and view.survived(qd)
+            rows.append(view.pdm_last_row(qd))
+        QL = view.pdm_head_rows(np.stack(rows))
+        for i, ql in zip(batch, QL):
+            q = reps[i]
+            j, c2 = q["exit_pos"], q["drafted_at"]
+            qw, qZ = sampling.softmax_weights(ql, T, keep=keep(("qset", c2), ql))
+            teacher[("draft", c2)] = int(recs[c2]["pdm_argmax"])
+            dec.sample(("draft", c2), qw, float(uni[j + 1, U_DRAFT]))
+            pl = view.logits_at(j)
+            pw, pZ = sampling.softmax_weights(pl, T, keep=keep(("pset", i), pl))
+            teacher[("accept", i)] = bool(recs[i]["accepted"])
+            ok = dec.accept(("accept", i), pw, pZ, qw, qZ, reps[c2]["draft"], float(uni[j + 1, U_ACCEPT]))
+            if not ok:
+                teacher[("resample", i)] = int(recs[i]["target_token"])
+                dec.sample(("resample", i), sampling.residual(pw, pZ, qw, qZ), float(uni[j + 1, U_RESAMPLE]))
+        if progress:
+            progress(f"sampling check: {b0 + len(batch)} of {len(exits)} verifications")
+    dec.checked = len(exits)
     return dec
 
 

@@ -48,9 +48,49 @@ def run_gpu(w, T_cpu, prompt, uni=None, ref=None, p_accept=None, batch=64, per_c
     return eng, first, recs, toks
 
 
-def teacher_of(recs, first):
-    """Decisions the GPU took, keyed as the oracle's Decisions expects."""
-    t = {("first", 0): int(first)}
+def run_gpu_with_sets(w, T_cpu, prompt, uni):
+    """A sampling run, one cycle at a time, that also reads the logits behind
+    every top-k truncation the GPU made: the draft module's at every cycle,
+    the target's at every exit and after prefill.  The kept sets are the top-k
+    ids of those logits (ties to the lower id, as the kernels rank them)."""
+    from oracle.sampling import top_k_ids
+
+    sets = {}
+
+    def hook(eng, r):
+        c = int(r["cycle"])
+        sets[("qset", c)] = top_k_ids(eng.pdm_logits(), w.top_k)
+        if r["exit_pos"] >= 0:
+            sets[("pset", c)] = top_k_ids(eng.logits(), w.top_k)
+
+    import torch
+    from pipelined_draft_verify_amd import SPDEngine
+
+    eng = SPDEngine(w, {k: v.to("cuda:0") for k, v in T_cpu.items()})
+    eng.set_uniforms(uni)
+    first = eng.prefill(prompt)
+    sets[("pset_first", 0)] = top_k_ids(eng.logits(), w.top_k)
+    out = []
+    while True:
+        buf = eng.enqueue(1)
+        st = eng.sync()
+        r = eng.records_of(buf)
+        if r["flags"][0] & 8:
+            break
+        out.append(r)
+        hook(eng, r[0])
+        if st.done:
+            break
+    recs = np.concatenate(out)
+    toks = eng.tokens(0, w.P + w.G)
+    return eng, first, recs, toks, sets
+
+
+def teacher_of(recs, first, sets=None):
+    """Decisions the GPU took, keyed as the oracle's Decisions expects (with
+    `sets`: also the top-k kept sets behind them)."""
+    t = dict(sets or {})
+    t[("first", 0)] = int(first)
     for r in recs:
         c = int(r["cycle"])
         t[("pdm", c)] = int(r["pdm_argmax"])

@@ -84,12 +84,21 @@ def test_full_size(name, part):
             dec = fs.check_verifications(run, view, reps)
             _assert_decisions(dec, w.G, f"{name} target tokens")
         else:
-            dec = fs.check_sampling(run, view, reps)
+            dec = fs.check_sampling(run, view, reps, progress=lambda m: print(m, flush=True))
+            assert dec.checked == w.G - 1
             # Random-init T=1 distributions over 151936 ids are nearly uniform:
             # each id holds ~1/V of the mass, about the size of the bf16-vs-fp32
             # difference of the cumulative sums, so a draw often lands on the
-            # neighbouring id.  No count cap here; every differing draw must
-            # still lie within the sampling tolerance of its boundary.
+            # neighbouring id, and the 50th and 51st logits of a top-50 cut are
+            # ~0.007 apart.  No count cap on adoptions here: every differing
+            # draw must lie within the sampling tolerance of its boundary in
+            # the oracle's CDF, and every differing kept set within the argmax
+            # tolerance of a top-k set of the oracle's logits.
+            draws = [a for a in dec.adopted if a[1] != "set"]
+            sets = [a for a in dec.adopted if a[1] == "set"]
+            print(f"{name}: {len(draws)} draws and {len(sets)} kept sets adopted; largest draw gap "
+                  f"{max((a[3] for a in draws), default=0):.3g}, largest set gap "
+                  f"{max((a[3] for a in sets), default=0):.3g}")
             _assert_decisions(dec, dec.checked, f"{name} draws, accept tests and redraws", cap=False)
     else:
         reps = _reps(c)

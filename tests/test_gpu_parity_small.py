@@ -15,7 +15,7 @@ import pytest
 
 import seeded_inputs as si
 from oracle import ForcedPolicy, SPDOracle, ar_greedy
-from tests.gpu_common import compare_logs, gpu_workload_tiny, rel_l2, run_gpu, teacher_of
+from tests.gpu_common import compare_logs, gpu_workload_tiny, rel_l2, run_gpu, run_gpu_with_sets, teacher_of
 
 pytestmark = pytest.mark.gpu
 
@@ -132,9 +132,15 @@ def test_sampling_matches_oracle(name):
     need_accepts = kw.pop("need_accepts", True)
     w = gpu_workload_tiny(mode="sample", **kw)
     T, W, prompt, uni = _inputs(w)
-    eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni)
+    sets = None
+    if w.top_k:
+        # top-k: the GPU's kept sets (from its logits) must be valid top-k
+        # choices of the oracle's logits, and the draws are retaken on them
+        eng, first, recs, toks, sets = run_gpu_with_sets(w, T, prompt, uni)
+    else:
+        eng, first, recs, toks = run_gpu(w, T, prompt, uni=uni)
     eng.close()
-    o = SPDOracle(w, W, uniforms=uni, teacher=teacher_of(recs, first), tol=TOL[w.dtype],
+    o = SPDOracle(w, W, uniforms=uni, teacher=teacher_of(recs, first, sets), tol=TOL[w.dtype],
                   sample_tol=STOL[w.dtype])
     otoks, ologs = o.run(prompt, w.G)
     print(name, "adopted", o.dec.adopted)

@@ -80,3 +80,46 @@ def test_top_k_one_sampling_is_greedy_decoding(mi):
         assert x["pdm_raw"] == pdm_argmax[x["cycle"]]
         if x["exit_pos"] >= 0:
             assert x["accept"] == int(x["draft"] == ref[x["exit_pos"] + 1])
+
+
+def test_top_k_set_gap_brute_force():
+    """The gap of a candidate kept set is the smallest uniform logit
+    perturbation bound under which it becomes the top-k set: brute force over
+    every k-subset of a small vocabulary."""
+    import itertools
+    V, k = 7, 3
+    for _ in range(30):
+        l = rng.standard_normal(V).astype(np.float32)
+        for S in itertools.combinations(range(V), k):
+            out = [v for v in range(V) if v not in S]
+            want = max(0.0, max(float(l[v]) for v in out) - min(float(l[v]) for v in S))
+            assert sampling.top_k_set_gap(l, list(S)) == pytest.approx(want, abs=0)
+        assert sampling.top_k_set_gap(l, sampling.top_k_ids(l, k)) == 0.0
+
+
+def test_top_k_one_set_gap_is_the_argmax_rule():
+    l = rng.standard_normal(50).astype(np.float32)
+    for x in range(50):
+        assert sampling.top_k_set_gap(l, [x]) == float(l.max()) - float(l[x])
+
+
+def test_kept_set_teacher_validation():
+    """A teacher's kept set is adopted when it is a near-tie, and a set that
+    leaves out a clearly larger logit is a mismatch."""
+    from oracle.spd import Decisions
+    l = np.array([5.0, 4.0, 3.0, 2.99, 1.0, 0.0], np.float32)
+    d = Decisions({("qset", 0): [0, 1, 3], ("qset", 1): [0, 1, 4], ("qset", 2): [0, 1, 2]}, tol=0.05)
+    assert list(d.kept_set(("qset", 0), l, 3)) == [0, 1, 3] and len(d.adopted) == 1
+    d.kept_set(("qset", 1), l, 3)
+    assert len(d.mismatch) == 1
+    assert list(d.kept_set(("qset", 2), l, 3)) == [0, 1, 2] and len(d.adopted) == 1
+
+
+def test_softmax_weights_on_a_given_set():
+    l = rng.standard_normal(30).astype(np.float32)
+    keep = [1, 7, 8, 20]
+    w, Z = sampling.softmax_weights(l, 0.7, keep=keep)
+    wf, _ = sampling.softmax_weights(l, 0.7)
+    for v in range(30):
+        assert w[v] == (wf[v] if v in keep else 0.0)
+    assert Z == pytest.approx(float(wf[keep].astype(np.float64).sum()), rel=1e-12)
