@@ -69,6 +69,7 @@ extern "C" {
 #define SPD_ECTX (-3)    /* sequence would exceed max_ctx */
 #define SPD_EHIP (-4)    /* a HIP runtime call failed (see spd_sync status) */
 #define SPD_EDEVICE (-5) /* a device-side invariant check failed */
+#define SPD_ESCRATCH (-6) /* the configuration needs more scratch than the static scratch array holds */
 
 /* storage types of weights and KV cache */
 #define SPD_DTYPE_F32 0
@@ -234,6 +235,30 @@ SPD_API int spd_workspace_bytes(const spd_config *cfg, size_t *bytes);
  * streams equal), SPD_EHIP. */
 SPD_API int spd_init(const spd_config *cfg, const spd_weights *w, void *workspace, size_t ws_bytes,
              void *stage_stream, void *pdm_stream, spd_t **out);
+
+/* Allocation-free variant of spd_init, for callers that cannot allocate
+ * device memory around their decode calls (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The engine's
+ * per-cycle scratch (activation rows, attention and split-K partials,
+ * logits, argmax and sampling partials: everything spd_init carves after the
+ * persistent state) lives in a static device array of SPD_STATIC_SCRATCH_MB
+ * MiB that the library holds on every GPU it runs on until the process ends;
+ * the caller passes only the persistent state (KV caches, control block,
+ * rings, tables, in-flight slots) in `state`.
+ *   state == NULL: size query -- *state_bytes receives the state size (pure
+ *     host computation; the other pointers may be NULL).
+ *   state != NULL: *state_bytes is the size of `state` (device memory,
+ *     256-byte aligned, at least the queried size); otherwise as spd_init.
+ * Calls no hipMalloc / hipFree and allocates nothing on the device.  Every
+ * handle made by this call on one GPU shares that GPU's array, which keeps
+ * the last user's contents (this call clears it): work of two such handles
+ * that overlaps on one GPU races, so the caller must order it (one stream
+ * pair at a time).  Handles from spd_init are unaffected.  Errors:
+ * SPD_ESCRATCH (the configuration's scratch exceeds the array), SPD_EINVAL
+ * (as spd_init, or state_bytes too small), SPD_EHIP. */
+#define SPD_STATIC_SCRATCH_MB 64
+SPD_API int spd_init_static_scratch(const spd_config *cfg, const spd_weights *w, void *state, size_t *state_bytes,
+                                    void *stage_stream, void *pdm_stream, spd_t **out);
 
 /* Select the draft policy.  SPD_DRAFT_FORCED (greedy mode only): when
  * drafting position q < ref_len, if u[q][SPD_U_FORCE] < p_accept the draft is

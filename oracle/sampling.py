@@ -111,3 +111,34 @@ def emit_distribution(P: np.ndarray, Q: np.ndarray) -> np.ndarray:
     r = np.maximum(0.0, P - Q)
     r = r / r.sum() if r.sum() > 0 else np.zeros_like(P)
     return acc + rej_mass * r
+
+
+def cdf_shift_bound(eps: float, temperature: float = 1.0) -> float:
+    """Largest move of any point of a softmax CDF (as a fraction of the mass)
+    when every logit moves by at most eps: the mass below a boundary is
+    A / (A + B) with A, B scaled by at most exp(+-eps/T), so it moves by at
+    most tanh(eps / (2T))."""
+    return float(np.tanh(eps / (2.0 * temperature)))
+
+
+def accept_shift_bound(eps_p: float, eps_q: float, Px: float, Qx: float, u: float, temperature: float = 1.0) -> float:
+    """Largest move of the accept-test gap |u Q(x) - P(x)| / Q(x) when P's and
+    Q's logits move by at most eps_p, eps_q: each probability moves by a factor
+    within exp(+-2 eps / T)."""
+    rp = float(np.expm1(2.0 * eps_p / temperature))
+    rq = float(np.expm1(2.0 * eps_q / temperature))
+    return u * rq + (Px / Qx) * rp if Qx > 0 else float("inf")
+
+
+def residual_shift_bound(eps_p: float, eps_q: float, P: np.ndarray, Q: np.ndarray, temperature: float = 1.0) -> float:
+    """Largest move of a point of the residual max(0, P - Q)'s CDF (fraction of
+    its mass): each residual weight moves by at most |dP_v| + |dQ_v| <=
+    P_v rp + Q_v rq, so the mass below a boundary and the total move by at
+    most D = sum_v (P_v rp + Q_v rq) over the support, and the fraction by at
+    most 2 D / (total - D)."""
+    rp = float(np.expm1(2.0 * eps_p / temperature))
+    rq = float(np.expm1(2.0 * eps_q / temperature))
+    r = np.maximum(0.0, P - Q)
+    tot = float(r.sum())
+    D = float(np.sum((P * rp + Q * rq)[(P > 0) | (Q > 0)]))
+    return 2.0 * D / (tot - D) if tot > D else float("inf")

@@ -143,9 +143,9 @@ class Decisions:
         (self.adopted if gap <= self.tol else self.mismatch).append(rec)
         return theirs if ok_size else mine
 
-    def sample(self, key, weights: np.ndarray, u: float) -> int:
+    def sample(self, key, weights: np.ndarray, u: float, tol: Optional[float] = None) -> int:
         """A draw by inverse CDF; a differing teacher draw must lie within
-        `sample_tol` (fraction of the total mass) of its interval."""
+        `sample_tol` (or `tol`; fraction of the total mass) of its interval."""
         i, _ = sampling.inverse_cdf(weights, u)
         c = np.cumsum(weights.astype(np.float64))
         thr = np.float64(u) * c[-1]
@@ -155,11 +155,11 @@ class Decisions:
                 return float("inf")
             lo = c[t - 1] if t > 0 else 0.0
             return float(max(lo - thr, thr - c[t], 0.0) / c[-1])
-        return self._teach(key, i, gap, self.sample_tol)
+        return self._teach(key, i, gap, self.sample_tol if tol is None else tol)
 
-    def accept(self, key, p_w, p_Z, q_w, q_Z, x, u) -> bool:
+    def accept(self, key, p_w, p_Z, q_w, q_Z, x, u, tol: Optional[float] = None) -> bool:
         acc, g = sampling.accept_test(p_w, p_Z, q_w, q_Z, x, u)
-        return bool(self._teach(key, acc, lambda t: g, self.sample_tol))
+        return bool(self._teach(key, acc, lambda t: g, self.sample_tol if tol is None else tol))
 
 
 class SPDOracle:

@@ -20,7 +20,8 @@ SPD_MAX_STAGES = 16
 SPD_MAX_VOCAB = 1 << 20
 SPD_MAX_TOPK = 64
 
-SPD_OK, SPD_EINVAL, SPD_ESTATE, SPD_ECTX, SPD_EHIP, SPD_EDEVICE = 0, -1, -2, -3, -4, -5
+SPD_OK, SPD_EINVAL, SPD_ESTATE, SPD_ECTX, SPD_EHIP, SPD_EDEVICE, SPD_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
+SPD_STATIC_SCRATCH_MB = 64
 SPD_DTYPE_F32, SPD_DTYPE_BF16 = 0, 1
 SPD_MODE_GREEDY, SPD_MODE_SAMPLE = 0, 1
 SPD_SCHED_PRE, SPD_SCHED_POST = 0, 1
@@ -79,6 +80,8 @@ SIGNATURES = [
     ("spd_workspace_bytes", c_int32, [POINTER(spd_config), POINTER(c_size_t)]),
     ("spd_init", c_int32, [POINTER(spd_config), POINTER(spd_weights), c_void_p, c_size_t, c_void_p, c_void_p,
                            POINTER(c_void_p)]),
+    ("spd_init_static_scratch", c_int32, [POINTER(spd_config), POINTER(spd_weights), c_void_p, POINTER(c_size_t),
+                                          c_void_p, c_void_p, POINTER(c_void_p)]),
     ("spd_set_draft_policy", c_int32, [c_void_p, c_int32, c_float, c_void_p, c_int32]),
     ("spd_set_launch_mode", c_int32, [c_void_p, c_int32]),
     ("spd_set_uniforms", c_int32, [c_void_p, c_void_p, c_int32]),
@@ -143,6 +146,21 @@ def spd_init(cfg, weights, workspace_ptr, ws_bytes, stage_stream, pdm_stream):
     check("spd_init", lib().spd_init(ctypes.byref(cfg), ctypes.byref(weights), c_void_p(workspace_ptr),
                                       c_size_t(ws_bytes), c_void_p(stage_stream), c_void_p(pdm_stream),
                                       ctypes.byref(h)))
+    return h
+
+
+def spd_init_static_scratch(cfg, weights=None, state_ptr=None, state_bytes=0, stage_stream=None, pdm_stream=None):
+    """With state_ptr None: the size query, returns the state bytes.  Else
+    returns the handle."""
+    n = c_size_t(state_bytes)
+    if state_ptr is None:
+        check("spd_init_static_scratch", lib().spd_init_static_scratch(ctypes.byref(cfg), None, None,
+                                                                        ctypes.byref(n), None, None, None))
+        return n.value
+    h = c_void_p(0)
+    check("spd_init_static_scratch", lib().spd_init_static_scratch(
+        ctypes.byref(cfg), ctypes.byref(weights), c_void_p(state_ptr), ctypes.byref(n), c_void_p(stage_stream),
+        c_void_p(pdm_stream), ctypes.byref(h)))
     return h
 
 

@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -44,7 +45,9 @@ struct Layout {
   size_t lin_state, lin_ckpt;
   size_t bsq, bsp;
   size_t tkq, tkp;
-  size_t total;
+  size_t state_total;    // persistent state: KV caches, control block, rings, tables, in-flight slots
+  size_t scratch_total;  // per-cycle scratch (offsets of the scratch fields are relative to its base)
+  size_t total;          // one workspace holding both: state, then scratch
   int ctx_cap, nsplit, mr, log_cap, nparts_max;
 };
 
@@ -148,10 +151,15 @@ Layout make_layout(const spd_config* c) {
   L.log_cap = std::max(4096, n * c->max_new + 64);
   L.nparts_max = kCUs * kPersistPerCU;
   const int nslots = n + 1;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
+  size_t off = 0, soff = 0;
+  auto take = [&](size_t bytes) {  // persistent state
     size_t o = off;
     off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  auto scr = [&](size_t bytes) {  // scratch: rewritten before it is read within a cycle or a call
+    size_t o = soff;
+    soff = align_up(soff + bytes, kAlign);
     return o;
   };
   L.ctrl = take(sizeof(Ctrl));
@@ -172,29 +180,29 @@ Layout make_layout(const spd_config* c) {
   L.hslots = take(sizeof(float) * (size_t)nslots * d);
   L.anchors = take(sizeof(float) * (size_t)nslots * m * d);
   const size_t qd = (size_t)Hq * hd;
-  L.s_q = take(sizeof(float) * n * qd);
-  L.s_pacc = take(sizeof(float) * n * (size_t)Hq * L.nsplit * hd);
-  L.s_pml = take(sizeof(float) * n * (size_t)Hq * L.nsplit * 2);
-  L.s_o = take(sizeof(float) * n * qd);
-  L.s_act = take(sizeof(float) * n * (size_t)F);
-  L.Xt = take(sizeof(float) * L.mr * (size_t)d);
-  L.Xp = take(sizeof(float) * L.mr * (size_t)d);
-  L.r_q = take(sizeof(float) * L.mr * qd);
-  L.r_pacc = take(sizeof(float) * L.mr * (size_t)Hq * L.nsplit * hd);
-  L.r_pml = take(sizeof(float) * L.mr * (size_t)Hq * L.nsplit * 2);
-  L.r_o = take(sizeof(float) * L.mr * qd);
-  L.r_act = take(sizeof(float) * L.mr * (size_t)F);
-  L.taps = take(sizeof(float) * kRowsMR * (size_t)m * d);
-  L.logits = take(sizeof(float) * (size_t)V);
-  L.plogits = take(sizeof(float) * (size_t)V);
-  L.pw = take(sizeof(float) * (size_t)V);
-  L.parts = take(sizeof(ArgPair) * L.nparts_max);
-  L.pparts = take(sizeof(ArgPair) * L.nparts_max);
+  L.s_q = scr(sizeof(float) * n * qd);
+  L.s_pacc = scr(sizeof(float) * n * (size_t)Hq * L.nsplit * hd);
+  L.s_pml = scr(sizeof(float) * n * (size_t)Hq * L.nsplit * 2);
+  L.s_o = scr(sizeof(float) * n * qd);
+  L.s_act = scr(sizeof(float) * n * (size_t)F);
+  L.Xt = scr(sizeof(float) * L.mr * (size_t)d);
+  L.Xp = scr(sizeof(float) * L.mr * (size_t)d);
+  L.r_q = scr(sizeof(float) * L.mr * qd);
+  L.r_pacc = scr(sizeof(float) * L.mr * (size_t)Hq * L.nsplit * hd);
+  L.r_pml = scr(sizeof(float) * L.mr * (size_t)Hq * L.nsplit * 2);
+  L.r_o = scr(sizeof(float) * L.mr * qd);
+  L.r_act = scr(sizeof(float) * L.mr * (size_t)F);
+  L.taps = scr(sizeof(float) * kRowsMR * (size_t)m * d);
+  L.logits = scr(sizeof(float) * (size_t)V);
+  L.plogits = scr(sizeof(float) * (size_t)V);
+  L.pw = scr(sizeof(float) * (size_t)V);
+  L.parts = scr(sizeof(ArgPair) * L.nparts_max);
+  L.pparts = scr(sizeof(ArgPair) * L.nparts_max);
   L.ring = take(sizeof(spd_cycle_rec) * (size_t)L.log_cap);
   // matrix-core path (bf16): per-row partial sums of squares of the prefill
   // rows and the draft-module rows, and the split-K partial tiles
-  L.ssq_t = take(sizeof(float) * L.mr * (size_t)(d / kSsqCols));
-  L.ssq_p = take(sizeof(float) * L.mr * (size_t)(d / kSsqCols));
+  L.ssq_t = scr(sizeof(float) * L.mr * (size_t)(d / kSsqCols));
+  L.ssq_p = scr(sizeof(float) * L.mr * (size_t)(d / kSsqCols));
   size_t pf = 0;
   if (c->dtype == SPD_DTYPE_BF16) {
     const int rows = L.mr;  // 16 * MT of the largest pass
@@ -209,7 +217,7 @@ Layout make_layout(const spd_config* c) {
     const int full[1] = {m * d};
     pf = std::max(pf, mfma_part_floats(d, full, 1, rows));
   }
-  L.mpart = take(sizeof(float) * std::max<size_t>(pf, 1));
+  L.mpart = scr(sizeof(float) * std::max<size_t>(pf, 1));
   // hybrid target: linear-attention state ring [L][nslots][Hkv][hd*hd + hd]
   // and its copy at the end of prefill [L][Hkv][hd*hd + hd]
   const size_t lin_one = (size_t)Hkv * ((size_t)hd * hd + hd);
@@ -217,13 +225,15 @@ Layout make_layout(const spd_config* c) {
   L.lin_ckpt = take(c->attn_period > 0 ? sizeof(float) * (size_t)c->n_layers * lin_one : 0);
   // dense sampling: block sums of Q (draft) and P (target) from k_softmax_blocks
   const size_t nbs = smp && !c->top_k ? (size_t)(V + kCdfBlock - 1) / kCdfBlock : 0;
-  L.bsq = take(sizeof(double) * nbs);
-  L.bsp = take(sizeof(double) * nbs);
+  L.bsq = scr(sizeof(double) * nbs);
+  L.bsp = scr(sizeof(double) * nbs);
   // top-k sampling: candidate keys of Q and P from k_topk_blocks
   const size_t ntk = smp && c->top_k ? (size_t)topk_candidates(V) : 0;
-  L.tkq = take(sizeof(unsigned long long) * ntk);
-  L.tkp = take(sizeof(unsigned long long) * ntk);
-  L.total = off;
+  L.tkq = scr(sizeof(unsigned long long) * ntk);
+  L.tkp = scr(sizeof(unsigned long long) * ntk);
+  L.state_total = off;
+  L.scratch_total = std::max<size_t>(soff, kAlign);
+  L.total = L.state_total + L.scratch_total;
   return L;
 }
 
@@ -1230,27 +1240,32 @@ int spd_workspace_bytes(const spd_config* cfg, size_t* bytes) {
   return SPD_OK;
 }
 
-int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_t ws_bytes, void* stage_stream,
-             void* pdm_stream, spd_t** out) {
-  if (!out) return SPD_EINVAL;
-  *out = nullptr;
-  if (!valid_config(cfg) || !w || !workspace) return SPD_EINVAL;
-  if (stage_stream == pdm_stream) return SPD_EINVAL;
-  if (((uintptr_t)workspace) % kAlign) return SPD_EINVAL;
-  Layout L = make_layout(cfg);
-  if (ws_bytes < L.total) return SPD_EINVAL;
-  if (!w->embed || !w->final_norm || !w->lm_head || !w->pdm_final_norm || !w->pdm_lm_head) return SPD_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the init entry points (configuration, weights, streams).
+bool valid_init_args(const spd_config* cfg, const spd_weights* w, void* stage_stream, void* pdm_stream) {
+  if (!valid_config(cfg) || !w) return false;
+  if (stage_stream == pdm_stream) return false;
+  if (!w->embed || !w->final_norm || !w->lm_head || !w->pdm_final_norm || !w->pdm_lm_head) return false;
   for (int l = 0; l < cfg->n_layers; ++l) {
     const spd_layer_weights& x = w->layers[l];
-    if (!x.attn_norm || !x.w_qkv || !x.w_o || !x.ffn_norm || !x.w_gu || !x.w_down) return SPD_EINVAL;
+    if (!x.attn_norm || !x.w_qkv || !x.w_o || !x.ffn_norm || !x.w_gu || !x.w_down) return false;
   }
   for (int l = 0; l < cfg->pdm_layers; ++l) {
     const spd_layer_weights& x = w->pdm[l];
-    if (!x.attn_norm || !x.w_qkv || !x.w_o || !x.ffn_norm || !x.w_gu || !x.w_down) return SPD_EINVAL;
+    if (!x.attn_norm || !x.w_qkv || !x.w_o || !x.ffn_norm || !x.w_gu || !x.w_down) return false;
   }
   for (int f = 0; f < cfg->n_anchors; ++f)
-    if (!w->fc[f]) return SPD_EINVAL;
+    if (!w->fc[f]) return false;
+  return true;
+}
 
+// The handle over persistent state at `ws` (L.state_total bytes) and scratch
+// at `sc` (L.scratch_total bytes).  Allocates no device memory.
+int init_handle(const spd_config* cfg, const spd_weights* w, char* ws, char* sc, const Layout& L,
+                void* stage_stream, void* pdm_stream, spd_t** out) {
   spd_t* h = new (std::nothrow) spd_handle();
   if (!h) return SPD_EINVAL;
   h->cfg = *cfg;
@@ -1302,7 +1317,6 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
       if (cfg->anchors[i] <= lmax) f = i;
     g.fpat[k] = f;
   }
-  char* ws = (char*)workspace;
   h->ws = ws;
   h->ctrl = (Ctrl*)(ws + L.ctrl);
   h->kv_len = (int32_t*)(ws + L.kv_len);
@@ -1318,35 +1332,35 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   h->rsin = (float*)(ws + L.rsin);
   h->hslots = (float*)(ws + L.hslots);
   h->anchors = (float*)(ws + L.anchors);
-  h->s_q = (float*)(ws + L.s_q);
-  h->s_pacc = (float*)(ws + L.s_pacc);
-  h->s_pml = (float*)(ws + L.s_pml);
-  h->s_o = (float*)(ws + L.s_o);
-  h->s_act = (float*)(ws + L.s_act);
-  h->Xt = (float*)(ws + L.Xt);
-  h->Xp = (float*)(ws + L.Xp);
-  h->r_q = (float*)(ws + L.r_q);
-  h->r_pacc = (float*)(ws + L.r_pacc);
-  h->r_pml = (float*)(ws + L.r_pml);
-  h->r_o = (float*)(ws + L.r_o);
-  h->r_act = (float*)(ws + L.r_act);
-  h->taps = (float*)(ws + L.taps);
-  h->logits = (float*)(ws + L.logits);
-  h->plogits = (float*)(ws + L.plogits);
-  h->pw = (float*)(ws + L.pw);
-  h->parts = (ArgPair*)(ws + L.parts);
-  h->pparts = (ArgPair*)(ws + L.pparts);
+  h->s_q = (float*)(sc + L.s_q);
+  h->s_pacc = (float*)(sc + L.s_pacc);
+  h->s_pml = (float*)(sc + L.s_pml);
+  h->s_o = (float*)(sc + L.s_o);
+  h->s_act = (float*)(sc + L.s_act);
+  h->Xt = (float*)(sc + L.Xt);
+  h->Xp = (float*)(sc + L.Xp);
+  h->r_q = (float*)(sc + L.r_q);
+  h->r_pacc = (float*)(sc + L.r_pacc);
+  h->r_pml = (float*)(sc + L.r_pml);
+  h->r_o = (float*)(sc + L.r_o);
+  h->r_act = (float*)(sc + L.r_act);
+  h->taps = (float*)(sc + L.taps);
+  h->logits = (float*)(sc + L.logits);
+  h->plogits = (float*)(sc + L.plogits);
+  h->pw = (float*)(sc + L.pw);
+  h->parts = (ArgPair*)(sc + L.parts);
+  h->pparts = (ArgPair*)(sc + L.pparts);
   h->ring = (spd_cycle_rec*)(ws + L.ring);
-  h->ssq_t = (float*)(ws + L.ssq_t);
-  h->ssq_p = (float*)(ws + L.ssq_p);
-  h->mpart = (float*)(ws + L.mpart);
+  h->ssq_t = (float*)(sc + L.ssq_t);
+  h->ssq_p = (float*)(sc + L.ssq_p);
+  h->mpart = (float*)(sc + L.mpart);
   if (cfg->mode == SPD_MODE_SAMPLE && !cfg->top_k) {
-    h->bsq = (double*)(ws + L.bsq);
-    h->bsp = (double*)(ws + L.bsp);
+    h->bsq = (double*)(sc + L.bsq);
+    h->bsp = (double*)(sc + L.bsp);
   }
   if (cfg->mode == SPD_MODE_SAMPLE && cfg->top_k) {
-    h->tkq = (unsigned long long*)(ws + L.tkq);
-    h->tkp = (unsigned long long*)(ws + L.tkp);
+    h->tkq = (unsigned long long*)(sc + L.tkq);
+    h->tkp = (unsigned long long*)(sc + L.tkp);
   }
   if (cfg->attn_period > 0) {
     h->lin_state = (float*)(ws + L.lin_state);
@@ -1372,8 +1386,12 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   std::vector<int32_t> zl(SPD_MAX_LAYERS, 0);
   if ((e = hipMemcpy(h->kv_len, zl.data(), sizeof(int32_t) * SPD_MAX_LAYERS, hipMemcpyHostToDevice)) != hipSuccess)
     return fail(e);
-  // matrix-core scratch is cleared once so that nothing reads uninitialised memory
-  if ((e = hipMemset(ws + L.ssq_t, 0, L.total - L.ssq_t)) != hipSuccess) return fail(e);
+  // scratch (it may hold another handle's values) and the linear-attention
+  // state are cleared once, so that nothing reads uninitialised memory
+  if ((e = hipMemsetAsync(sc, 0, L.scratch_total, h->ss)) != hipSuccess) return fail(e);
+  if (L.lin_ckpt > L.lin_state &&
+      (e = hipMemsetAsync(ws + L.lin_state, 0, L.state_total - L.lin_state, h->ss)) != hipSuccess)
+    return fail(e);
   if ((e = attn_lds_limits()) != hipSuccess) return fail(e);
   hipLaunchKernelGGL(k_rope_table, dim3(512), dim3(256), 0, h->ss, h->rcos, h->rsin, L.ctx_cap, g.hd,
                      (double)cfg->rope_base);
@@ -1382,6 +1400,69 @@ int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_
   if ((e = hipStreamSynchronize(h->ss)) != hipSuccess) return fail(e);
   *out = h;
   return SPD_OK;
+}
+
+// The static scratch array of the allocation-free init: one per GPU the
+// library runs on, for the life of the process.  Host code never passes its
+// name to a kernel or a copy: it uses the device address looked up once per
+// device (scratch_ptr).
+constexpr size_t kStaticScratchBytes = (size_t)SPD_STATIC_SCRATCH_MB << 20;
+__device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's static scratch, looked up with that
+// device current on its first use.
+hipError_t scratch_ptr(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spd_init(const spd_config* cfg, const spd_weights* w, void* workspace, size_t ws_bytes, void* stage_stream,
+             void* pdm_stream, spd_t** out) {
+  if (!out) return SPD_EINVAL;
+  *out = nullptr;
+  if (!workspace || !valid_init_args(cfg, w, stage_stream, pdm_stream)) return SPD_EINVAL;
+  if (((uintptr_t)workspace) % kAlign) return SPD_EINVAL;
+  const Layout L = make_layout(cfg);
+  if (ws_bytes < L.total) return SPD_EINVAL;
+  char* ws = (char*)workspace;
+  return init_handle(cfg, w, ws, ws + L.state_total, L, stage_stream, pdm_stream, out);
+}
+
+int spd_init_static_scratch(const spd_config* cfg, const spd_weights* w, void* state, size_t* state_bytes,
+                            void* stage_stream, void* pdm_stream, spd_t** out) {
+  if (out) *out = nullptr;
+  if (!state_bytes || !valid_config(cfg)) return SPD_EINVAL;
+  const Layout L = make_layout(cfg);
+  if (L.scratch_total > kStaticScratchBytes) return SPD_ESCRATCH;
+  if (!state) {  // size query
+    *state_bytes = L.state_total;
+    return SPD_OK;
+  }
+  if (!out || !valid_init_args(cfg, w, stage_stream, pdm_stream)) return SPD_EINVAL;
+  if (((uintptr_t)state) % kAlign || *state_bytes < L.state_total) return SPD_EINVAL;
+  char* sc = nullptr;
+  const hipError_t e = scratch_ptr(&sc);
+  if (e != hipSuccess) return SPD_EHIP;
+  return init_handle(cfg, w, (char*)state, sc, L, stage_stream, pdm_stream, out);
 }
 
 int spd_set_draft_policy(spd_t* h, int32_t policy, float p_accept, const int32_t* ref_tokens_dev, int32_t ref_len) {
@@ -1700,6 +1781,7 @@ const char* spd_strerror(int code) {
     case SPD_ECTX: return "sequence would exceed max_ctx";
     case SPD_EHIP: return "HIP runtime error";
     case SPD_EDEVICE: return "device-side invariant check failed";
+    case SPD_ESCRATCH: return "the configuration needs more scratch than the static scratch array holds";
     default: return "unknown error";
   }
 }

@@ -64,7 +64,12 @@ def make_weights_struct(w, T: Dict[str, "object"]) -> A.spd_weights:
 class SPDEngine:
     """One libspd handle on one GPU, with torch-owned workspace and streams."""
 
-    def __init__(self, w, tensors: Dict[str, "object"], device: str = "cuda:0", max_ctx: Optional[int] = None):
+    def __init__(self, w, tensors: Dict[str, "object"], device: str = "cuda:0", max_ctx: Optional[int] = None,
+                 static_scratch: bool = False):
+        """static_scratch: initialise with spd_init_static_scratch -- the
+        workspace holds only the persistent state, the per-cycle scratch is
+        the library's static device array (shared by every such engine on the
+        GPU: their work must not overlap)."""
         import torch
 
         self.torch = torch
@@ -75,7 +80,9 @@ class SPDEngine:
                 raise ValueError(f"tensor {k} must be contiguous on {self.device}")
         self.tensors = tensors
         self.cfg = make_config(w, max_ctx)
-        self.ws_bytes = A.spd_workspace_bytes(self.cfg)
+        self.static_scratch = static_scratch
+        self.ws_bytes = (A.spd_init_static_scratch(self.cfg) if static_scratch
+                         else A.spd_workspace_bytes(self.cfg))
         self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
         base = self.ws.data_ptr()
         self.ws_ptr = (base + 255) // 256 * 256
@@ -83,8 +90,12 @@ class SPDEngine:
         self.s_pdm = torch.cuda.Stream(device=self.device)
         self.wstruct = make_weights_struct(w, tensors)
         torch.cuda.synchronize(self.device)
-        self.h = A.spd_init(self.cfg, self.wstruct, self.ws_ptr, self.ws_bytes,
-                            self.s_stage.cuda_stream, self.s_pdm.cuda_stream)
+        if static_scratch:
+            self.h = A.spd_init_static_scratch(self.cfg, self.wstruct, self.ws_ptr, self.ws_bytes,
+                                               self.s_stage.cuda_stream, self.s_pdm.cuda_stream)
+        else:
+            self.h = A.spd_init(self.cfg, self.wstruct, self.ws_ptr, self.ws_bytes,
+                                self.s_stage.cuda_stream, self.s_pdm.cuda_stream)
         self.uni = None
         self.ref = None
         self.P = 0

@@ -82,7 +82,9 @@ def gpu_run(name: str) -> dict:
     first_set = None
     if w.mode == "sample" and w.top_k:
         from oracle.sampling import top_k_ids
-        first_set = top_k_ids(eng.logits(), w.top_k)  # the prefill's logits
+        lg = eng.logits()  # the prefill's logits
+        first_set = top_k_ids(lg, w.top_k)
+        first_val = lg[first_set].copy()
     ref = None
     if w.mode == "greedy":
         ar = eng.generate_ar(w.G - 1)
@@ -105,6 +107,7 @@ def gpu_run(name: str) -> dict:
     if first_set is not None:
         sets = _topk_sets(eng, w, first, recs)
         sets[("pset_first", 0)] = first_set
+        sets[("pval_first", 0)] = first_val
     eng.close()
     del eng
     flat = si.weights_numpy_f32(T)
@@ -117,7 +120,8 @@ def gpu_run(name: str) -> dict:
 def _topk_sets(eng, w, first, recs):
     """The generation again, one cycle at a time, reading the logits behind
     every top-k truncation: the kept sets (top-k ids of the GPU's logits,
-    ties to the lower id).  Its records must equal the first run's."""
+    ties to the lower id) and the GPU's logits at those ids.  Its records
+    must equal the first run's."""
     from oracle.sampling import top_k_ids
 
     eng.rollback(w.P, first)
@@ -130,9 +134,13 @@ def _topk_sets(eng, w, first, recs):
         if r["flags"][0] & IDLE:
             break
         c = len(out)
-        sets[("qset", c)] = top_k_ids(eng.pdm_logits(), w.top_k)
+        ql = eng.pdm_logits()
+        sets[("qset", c)] = top_k_ids(ql, w.top_k)
+        sets[("qval", c)] = ql[sets[("qset", c)]].copy()
         if r["exit_pos"][0] >= 0:
-            sets[("pset", c)] = top_k_ids(eng.logits(), w.top_k)
+            pl = eng.logits()
+            sets[("pset", c)] = top_k_ids(pl, w.top_k)
+            sets[("pval", c)] = pl[sets[("pset", c)]].copy()
         out.append(r)
         if st.done:
             break
@@ -257,24 +265,59 @@ def check_draft_module(run: dict, view: OracleView, reps, k: int = 32) -> Decisi
     return dec
 
 
+def _on_set(V: int, ids, vals) -> np.ndarray:
+    """A logits vector holding `vals` at `ids` and -inf elsewhere."""
+    out = np.full(V, -np.inf, np.float32)
+    out[np.asarray(ids, np.int64)] = vals
+    return out
+
+
 def check_sampling(run: dict, view: OracleView, reps, chunk: int = 32, progress=None) -> Decisions:
     """Sampling: the first token, and at EVERY verification the draft draw
     from Q (recomputed at the cycle that drafted the verified position), the
-    accept test u*Q(x) < P(x) and the residual redraw.  Under top-k the
-    GPU's kept sets come in as teacher decisions: each must be a valid top-k
-    choice of the oracle's logits, and the draws are retaken on it."""
+    accept test u*Q(x) < P(x) and the residual redraw.
+
+    Dense (whole-vocabulary) distributions: a differing decision must lie
+    within STOL of its boundary in the oracle's arithmetic.
+
+    Top-k: the GPU's kept sets and its logits at them come in from the
+    cycle-by-cycle run.  Each set must be a valid top-k choice of the
+    oracle's logits (argmax tolerance), the GPU's logits at its set must be
+    within the argmax tolerance of the oracle's, every decision retaken on
+    the GPU's own logits must reproduce the GPU's decision (the sampler's
+    arithmetic; 1e-6 of the mass for rounding), and retaken on the oracle's
+    logits over the same set it may differ only within the shift that the
+    measured logit difference allows (oracle.sampling *_shift_bound)."""
     w, recs, uni = run["w"], run["recs"], run["uni"]
     T, k = w.temperature, w.top_k
+    topk = 0 < k < w.V
     teacher = dict(run.get("sets") or {})
     teacher[("first", 0)] = run["first"]
     dec = Decisions(teacher, TOL[w.dtype], STOL[w.dtype])
+    own = Decisions(teacher, TOL[w.dtype], 1e-6)  # decisions retaken on the GPU's own logits
+    dec.eps = 0.0
 
-    def keep(key, logits):
-        return dec.kept_set(key, logits, k) if 0 < k < w.V else None
+    def eps_of(sk, vk, logits):
+        """Largest difference of the GPU's and the oracle's logits on the GPU's set."""
+        e = float(np.max(np.abs(np.asarray(teacher[vk], np.float64) - logits[teacher[sk]])))
+        dec.eps = max(dec.eps, e)
+        if e > TOL[w.dtype]:
+            dec.mismatch.append((vk, "logits", e))
+        return e
 
     l0 = view.logits_at(w.P - 1)
-    pw0, _ = sampling.softmax_weights(l0, T, keep=keep(("pset_first", 0), l0))
-    dec.sample(("first", 0), pw0, float(uni[w.P, U_TARGET]))
+    if topk:
+        S0 = dec.kept_set(("pset_first", 0), l0, k)
+        e0 = eps_of(("pset_first", 0), ("pval_first", 0), l0)
+        gw0, _ = sampling.softmax_weights(_on_set(w.V, teacher[("pset_first", 0)], teacher[("pval_first", 0)]), T,
+                                          keep=teacher[("pset_first", 0)])
+        own.sample(("first", 0), gw0, float(uni[w.P, U_TARGET]))
+        pw0, _ = sampling.softmax_weights(l0, T, keep=S0)
+        dec.sample(("first", 0), pw0, float(uni[w.P, U_TARGET]),
+                   tol=max(STOL[w.dtype], sampling.cdf_shift_bound(e0, T)))
+    else:
+        pw0, _ = sampling.softmax_weights(l0, T)
+        dec.sample(("first", 0), pw0, float(uni[w.P, U_TARGET]))
     exits = [i for i, q in enumerate(reps) if q["exit_pos"] >= 0]
     for b0 in range(0, len(exits), chunk):
         batch = exits[b0:b0 + chunk]
@@ -287,19 +330,46 @@ def check_sampling(run: dict, view: OracleView, reps, chunk: int = 32, progress=
         for i, ql in zip(batch, QL):
             q = reps[i]
             j, c2 = q["exit_pos"], q["drafted_at"]
-            qw, qZ = sampling.softmax_weights(ql, T, keep=keep(("qset", c2), ql))
-            teacher[("draft", c2)] = int(recs[c2]["pdm_argmax"])
-            dec.sample(("draft", c2), qw, float(uni[j + 1, U_DRAFT]))
+            x = reps[c2]["draft"]
             pl = view.logits_at(j)
-            pw, pZ = sampling.softmax_weights(pl, T, keep=keep(("pset", i), pl))
+            teacher[("draft", c2)] = int(recs[c2]["pdm_argmax"])
             teacher[("accept", i)] = bool(recs[i]["accepted"])
-            ok = dec.accept(("accept", i), pw, pZ, qw, qZ, reps[c2]["draft"], float(uni[j + 1, U_ACCEPT]))
-            if not ok:
+            if not recs[i]["accepted"]:
                 teacher[("resample", i)] = int(recs[i]["target_token"])
-                dec.sample(("resample", i), sampling.residual(pw, pZ, qw, qZ), float(uni[j + 1, U_RESAMPLE]))
+            u_d, u_a, u_r = float(uni[j + 1, U_DRAFT]), float(uni[j + 1, U_ACCEPT]), float(uni[j + 1, U_RESAMPLE])
+            if not topk:
+                qw, qZ = sampling.softmax_weights(ql, T)
+                dec.sample(("draft", c2), qw, u_d)
+                pw, pZ = sampling.softmax_weights(pl, T)
+                if not dec.accept(("accept", i), pw, pZ, qw, qZ, x, u_a):
+                    dec.sample(("resample", i), sampling.residual(pw, pZ, qw, qZ), u_r)
+                continue
+            Sq = dec.kept_set(("qset", c2), ql, k)
+            Sp = dec.kept_set(("pset", i), pl, k)
+            eq = eps_of(("qset", c2), ("qval", c2), ql)
+            ep = eps_of(("pset", i), ("pval", i), pl)
+            # the GPU's own arithmetic on its own logits
+            gq_ids, gp_ids = teacher[("qset", c2)], teacher[("pset", i)]
+            gqw, gqZ = sampling.softmax_weights(_on_set(w.V, gq_ids, teacher[("qval", c2)]), T, keep=gq_ids)
+            gpw, gpZ = sampling.softmax_weights(_on_set(w.V, gp_ids, teacher[("pval", i)]), T, keep=gp_ids)
+            own.sample(("draft", c2), gqw, u_d)
+            if not own.accept(("accept", i), gpw, gpZ, gqw, gqZ, x, u_a):
+                own.sample(("resample", i), sampling.residual(gpw, gpZ, gqw, gqZ), u_r)
+            # the oracle's arithmetic on the same sets, within the shift the logit error allows
+            qw, qZ = sampling.softmax_weights(ql, T, keep=Sq)
+            pw, pZ = sampling.softmax_weights(pl, T, keep=Sp)
+            dec.sample(("draft", c2), qw, u_d, tol=max(STOL[w.dtype], sampling.cdf_shift_bound(eq, T)))
+            Px, Qx = float(pw[x]) / pZ, float(qw[x]) / qZ
+            ok = dec.accept(("accept", i), pw, pZ, qw, qZ, x, u_a,
+                            tol=max(STOL[w.dtype], sampling.accept_shift_bound(ep, eq, Px, Qx, u_a, T)))
+            if not ok:
+                P, Q = pw.astype(np.float64) / pZ, qw.astype(np.float64) / qZ
+                dec.sample(("resample", i), sampling.residual(pw, pZ, qw, qZ), u_r,
+                           tol=max(STOL[w.dtype], sampling.residual_shift_bound(ep, eq, P, Q, T)))
         if progress:
             progress(f"sampling check: {b0 + len(batch)} of {len(exits)} verifications")
     dec.checked = len(exits)
+    dec.own = own
     return dec
 
 

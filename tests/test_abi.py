@@ -154,3 +154,23 @@ def test_stage_split_constraints_are_checked():
         with pytest.raises(A.SPDError) as e:
             A.spd_workspace_bytes(make_config(w.replace(**kw)))
         assert e.value.code == A.SPD_EINVAL
+
+
+def test_static_scratch_state_query_on_host():
+    """The allocation-free init's size query: the state is the workspace less
+    the scratch, and every named workload's scratch fits the static array."""
+    for name in si.WORKLOADS:
+        c = make_config(si.workload(name))
+        total = A.spd_workspace_bytes(c)
+        state = A.spd_init_static_scratch(c)
+        assert 0 < state < total
+        assert total - state <= A.SPD_STATIC_SCRATCH_MB << 20, name
+
+
+def test_static_scratch_rejects_oversized_configs():
+    c = make_config(si.workload("9b_n8"), max_ctx=32768)
+    c.n_stages, c.pdm_layers = 16, 2
+    A.spd_workspace_bytes(c)  # a valid configuration ...
+    with pytest.raises(A.SPDError) as e:
+        A.spd_init_static_scratch(c)  # ... whose scratch exceeds the static array
+    assert e.value.code == A.SPD_ESCRATCH

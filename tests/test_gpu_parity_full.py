@@ -99,6 +99,11 @@ def test_full_size(name, part):
             print(f"{name}: {len(draws)} draws and {len(sets)} kept sets adopted; largest draw gap "
                   f"{max((a[3] for a in draws), default=0):.3g}, largest set gap "
                   f"{max((a[3] for a in sets), default=0):.3g}")
+            if w.top_k:
+                print(f"{name}: largest GPU-vs-oracle logit difference on the kept sets {dec.eps:.3g}; "
+                      f"decisions retaken on the GPU's own logits: {len(dec.own.adopted)} within 1e-6, "
+                      f"{len(dec.own.mismatch)} mismatches")
+                assert not dec.own.mismatch, dec.own.mismatch[:5]
             _assert_decisions(dec, dec.checked, f"{name} draws, accept tests and redraws", cap=False)
     else:
         reps = _reps(c)

@@ -131,3 +131,44 @@ def test_resampling_from_target_instead_of_residual_is_caught(monkeypatch):
                         lambda pw, pZ, qw, qZ: pw.astype(np.float64) / pZ)
     chi2, crit, _, _ = _first_two_tokens_chi2()
     assert chi2 > crit
+
+
+@pytest.mark.parametrize("T", [1.0, 0.5])
+def test_shift_bounds_hold_under_logit_perturbations(T):
+    """cdf_shift_bound, accept_shift_bound and residual_shift_bound bound the
+    movement of every inverse-CDF boundary, of the accept-test gap and of the
+    residual's CDF when each logit moves by at most eps (random and
+    worst-case-signed perturbations)."""
+    for trial in range(200):
+        V = int(rng.integers(2, 60))
+        eps = float(rng.choice([1e-4, 1e-3, 1e-2, 5e-2]))
+        lp = rng.standard_normal(V).astype(np.float32) * 2
+        lq = rng.standard_normal(V).astype(np.float32) * 2
+        if trial % 2:
+            dp = rng.uniform(-eps, eps, V)
+            dq = rng.uniform(-eps, eps, V)
+        else:  # all mass below one boundary up, all above it down
+            cut = int(rng.integers(0, V))
+            dp = np.where(np.arange(V) <= cut, eps, -eps)
+            dq = -dp
+        pw, pZ = sampling.softmax_weights(lp, T)
+        qw, qZ = sampling.softmax_weights(lq, T)
+        pw2, pZ2 = sampling.softmax_weights((lp + dp).astype(np.float32), T)
+        qw2, qZ2 = sampling.softmax_weights((lq + dq).astype(np.float32), T)
+        # every boundary of the inverse CDF
+        c1 = np.cumsum(qw.astype(np.float64)) / qZ
+        c2 = np.cumsum(qw2.astype(np.float64)) / qZ2
+        assert np.max(np.abs(c1 - c2)) <= sampling.cdf_shift_bound(eps * 1.0001, T) + 1e-7
+        # the accept test's gap
+        P, Q = pw.astype(np.float64) / pZ, qw.astype(np.float64) / qZ
+        P2, Q2 = pw2.astype(np.float64) / pZ2, qw2.astype(np.float64) / qZ2
+        x = int(rng.integers(0, V))
+        u = float(rng.random())
+        moved = abs((u * Q2[x] - P2[x]) - (u * Q[x] - P[x])) / Q[x]
+        assert moved <= sampling.accept_shift_bound(eps * 1.0001, eps * 1.0001, P[x], Q[x], u, T) + 1e-7
+        # the residual's CDF
+        r1, r2 = np.maximum(0, P - Q), np.maximum(0, P2 - Q2)
+        if r1.sum() > 0 and r2.sum() > 0:
+            b = sampling.residual_shift_bound(eps * 1.0001, eps * 1.0001, P, Q, T)
+            d = np.max(np.abs(np.cumsum(r1) / r1.sum() - np.cumsum(r2) / r2.sum()))
+            assert d <= b + 1e-7
