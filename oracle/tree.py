@@ -24,7 +24,9 @@ Reading taken here (greedy verification, pre-step drafting, n >= 2):
     rank, then lower token id);
   * drafting runs beside the stage step and verification prunes branches in
     the same cycle, so the next cycle enters the first W candidates whose leaf
-    survived, in rank order; they enter stage 0 together;
+    survived, in rank order; they enter stage 0 together, and every in-flight
+    node that is no longer on a path to one of them (a branch that got no
+    child) is dropped;
   * the stage step advances every node through its own stage; a node attends
     to the committed prefix, its ancestors and itself (per-branch KV);
   * the single node at the oldest position exits and verifies its children:
@@ -38,12 +40,13 @@ With W = 1 the tree is the single in-flight chain and the run is the
 pipeline of oracle.spd step for step (a pin in the CPU tests).
 
 Forced acceptance for trees (harness device, not on the pages): with the
-target's greedy continuation R and the on-path leaf (the leaf whose path
-tokens all equal R, if any), the draw u = U[q, FORCE] for position q places
-the pair (on-path leaf, R[q]) first in the ranking when u < p1, at rank W-1
-when p1 <= u < pW (only the tree catches it), and removes it when u >= pW
-(its token is replaced by the next id not already a candidate of that leaf).
-With W = 1 and p1 = pW this is the single-draft forced policy.
+target's greedy continuation R and the forced leaf (the on-path leaf, whose
+path tokens all equal R, if any, else the leaf of rank 0), the draw
+u = U[q, FORCE] for position q places the pair (forced leaf, R[q]) first in
+the ranking when u < p1, at rank W-1 when p1 <= u < pW and W >= 2 (only a
+tree catches it), and otherwise removes it (its token is replaced by the
+next id not already a candidate of that leaf).  With W = 1 this is the
+single-draft forced policy with p = p1.
 """
 from __future__ import annotations
 
@@ -183,7 +186,8 @@ class TreeSPDOracle:
         if self.reseed is not None:
             tok, t = self.reseed
             self.reseed = None
-            new = [Node(t, tok, None, 0.0)]
+            # parent: the exited token it follows (none right after prefill)
+            new = [Node(t, tok, self.pending, 0.0)]
             parents = [-1]
         else:
             t = max(self.levels) + 1
@@ -197,6 +201,12 @@ class TreeSPDOracle:
             nd.taps = [None] * len(self.w.anchors)
             nd.taps[0] = nd.h.copy()
         self.levels[t] = new
+        # branches that got no child are dead: only the paths to the new
+        # leaves stay in flight
+        live = {id(x) for nd in new for x in nd.path(-1)}
+        for p in self.levels:
+            if p < t:
+                self.levels[p] = [x for x in self.levels[p] if id(x) in live]
         if len(self.tokens) <= t:
             self.tokens.extend([-1] * (t + 1 - len(self.tokens)))
         self.tokens[t] = new[0].tok if len(new) == 1 else -1
@@ -252,10 +262,7 @@ class TreeSPDOracle:
             exit_pos = j
             if match:
                 accept, acc_rank = 1, match[0]
-                keep = children[acc_rank]
-                for p in sorted(self.levels):
-                    self.levels[p] = [nd for nd in self.levels[p] if keep in nd.path(j)]
-                    assert self.levels[p], "the kept child has a descendant at every in-flight position"
+                self._prune_to(children[acc_rank], j)
             else:
                 accept = 0
                 for l in range(self.L):
@@ -273,6 +280,12 @@ class TreeSPDOracle:
         self.logs.append(rec)
         self.ncycles += 1
         return rec
+
+    def _prune_to(self, keep: Node, j: int) -> None:
+        """After an accepted verification: only the kept child's subtree stays."""
+        for p in sorted(self.levels):
+            self.levels[p] = [nd for nd in self.levels[p] if keep in nd.path(j)]
+            assert self.levels[p], "the kept child has a descendant at every in-flight position"
 
     def _run_stage(self, nd: Node, k: int, F: int) -> None:
         s = self.s
@@ -334,6 +347,8 @@ class TreeSPDOracle:
         pdm = self.pdm
         G = np.stack([pdm.feature(nd.taps, k) for nd, k in rows])
         X = self._pdm_layers(G, rows)
+        if self.hook is not None:
+            self.hook("pdm_rows", dict(cycle=c, rows=rows, G=G, X=X, C=pdm.C))
         if commit:
             pdm.commit(1)
         leaves = self.levels[t]
@@ -362,21 +377,19 @@ class TreeSPDOracle:
         pol = self.policy
         if pol is None or q >= len(pol.ref):
             return cands
-        star = -1
+        star = 0
         oldest = min(self.levels)
         for r, leaf in enumerate(leaves):
             if all(x.tok == pol.ref[x.pos] for x in leaf.path(oldest - 1)):
                 star = r
                 break
-        if star < 0:
-            return cands
         leaf, R = leaves[star], pol.ref[q]
         u = pol.u[q, U_FORCE]
         cum = sum(x.logq for x in leaf.path(oldest)[1:])
         lq = lq_all[star]
         cands = [cd for cd in cands]
         at = [i for i, cd in enumerate(cands) if cd[0] is leaf and cd[1] == R]
-        if u < pol.pW:
+        if u < pol.p1 or (u < pol.pW and self.Wd >= 2):
             if at:
                 cands.pop(at[0])
             cands.insert(0 if u < pol.p1 else min(self.Wd - 1, len(cands)), (leaf, R, cum + float(lq[R]), float(lq[R])))
