@@ -55,11 +55,14 @@ def cycle_bytes(w, rec, es):
     P_attn = getattr(w, "attn_period", 0)
     lin_state = 2 * w.Hkv * (w.hd * w.hd + w.hd) * 4  # a linear layer reads and writes its fp32 state
     t, a = int(rec["t"]), int(rec["occupancy"])
+    # a draft tree's stage groups stream their weights once for all their
+    # nodes; each node reads its own KV (nodes per stage taken as the mean)
+    per_stage = (int(rec["nodes"]) / a) if getattr(w, "width", 1) > 1 and a > 0 else 1.0
     b = sum(len(stages[k]) for k in range(a)) * W_layer
     for k in range(a):
         for l in stages[k]:
             linear = P_attn > 0 and l % P_attn != P_attn - 1
-            b += lin_state if linear else (t - k + 1) * kv_pos
+            b += lin_state if linear else per_stage * (t - k + 1) * kv_pos
     if rec["exit_pos"] >= 0:
         b += V * d * es
     # draft module: FC patterns present, Ls layers, head, KV reads
@@ -106,6 +109,8 @@ def main():
                     help="run the draft module on the stage stream ahead of the stage step (no overlap)")
     ap.add_argument("--schedule", choices=["pre", "post"], default="pre",
                     help="draft-module features before (pre) or after (post) the stage step")
+    ap.add_argument("--dump-schedule", default="",
+                    help="write the step's per-cycle schedule (occupancy, exit) to this json file")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1"}))
@@ -141,13 +146,20 @@ def main():
         ar = eng.generate_ar(w.G - 1)
         log(f"reference AR decode of {w.G - 1} tokens in {time.time() - t0:.2f}s")
         eng.rollback(w.P, first)
-        eng.set_forced(list(prompt) + [first] + ar, w.p_accept)
+        if getattr(w, "width", 1) > 1:
+            eng.set_tree_forced(list(prompt) + [first] + ar, w.p_accept, w.p_tree)
+        else:
+            eng.set_forced(list(prompt) + [first] + ar, w.p_accept)
 
     # discover the step's cycle count (deterministic) with a logged run
     recs = eng.run(batch=128)
     K_c = len(recs)
     acc = recs[recs["exit_pos"] >= 0]
     log(f"one step = {K_c} cycles; {int((acc['accepted'] == 1).sum())}/{len(acc)} verifications accepted")
+    if args.dump_schedule:
+        json.dump({"workload": w.name, "cycles": [{"t": int(r["t"]), "occupancy": int(r["occupancy"]),
+                                                    "exit_pos": int(r["exit_pos"]), "nodes": int(r["nodes"])}
+                                                   for r in recs]}, open(args.dump_schedule, "w"))
 
     def step(log_buf=False):
         eng.rollback(w.P, first)
@@ -200,6 +212,7 @@ def main():
     cyc_end = cyc_arr[:, 2].reshape(reps, K_c).mean(axis=0)
     bubble = float(np.maximum(0.0, cyc_arr[:, 1] - cyc_arr[:, 0]).sum() / cyc_arr[:, 2].sum())
     hbm_frac = float(per_cycle_bytes.sum() / (cyc_end.sum() * 1e-3) / PEAK_HBM)
+    hbm_frac_wall = float(per_cycle_bytes.sum() * args.steps / elapsed / PEAK_HBM)
     per_cycle_frac = per_cycle_bytes / (cyc_end * 1e-3) / PEAK_HBM
     occ = recs["occupancy"]
     full = occ == w.n
@@ -240,6 +253,7 @@ def main():
                         f"Ls={w.Ls} anchors={w.anchors} prompt {w.P} gen {w.G} "
                         f"{w.mode}{' top-k ' + str(w.top_k) if w.top_k else ''} "
                         f"{w.policy}{' p=' + str(w.p_accept) if w.policy == 'forced' else ''}"
+                        f"{' draft tree W=' + str(w.width) + ' p_tree=' + str(w.p_tree) if w.width > 1 else ''}"
                         f" {w.schedule}-step drafting",
             "cycles_per_step": K_c,
             "parallelism": "single GPU, " + ("one stream (draft module serialized)" if args.serialized
@@ -248,6 +262,7 @@ def main():
         },
         "tokens_per_s": round(tokens_per_s, 3),
         "hbm_frac_per_cycle": round(hbm_frac, 4),
+        "hbm_frac_wall_clock": round(hbm_frac_wall, 4),
         "hbm_frac_full_cycles": round(hbm_full, 4) if hbm_full is not None else None,
         "hbm_frac_cycle_median": round(float(np.median(per_cycle_frac)), 4),
         "hbm_frac_cycle_p10": round(float(np.percentile(per_cycle_frac, 10)), 4),
@@ -282,17 +297,19 @@ def cpu_baseline(w, T, prompt, uni, n_cycles):
     import seeded_inputs as si
     from oracle import ForcedPolicy, SPDOracle
     from oracle.spd import ar_continue
+    from oracle.tree import TreeForcedPolicy, TreeSPDOracle
 
     t0 = time.time()
     W = si.nest_weights(si.weights_numpy_f32(T), w)
     log(f"cpu baseline: host fp32 weights in {time.time() - t0:.1f}s")
     t0 = time.time()
     pol = None
-    o = SPDOracle(w, W, uniforms=uni)
+    tree = getattr(w, "width", 1) > 1
+    o = TreeSPDOracle(w, W, w.width) if tree else SPDOracle(w, W, uniforms=uni)
     o.prefill(prompt, matrix=True)
     if w.policy == "forced":
         ref = ar_continue(o, n_cycles + w.n)
-        pol = ForcedPolicy(ref, w.p_accept, uni, w.V)
+        pol = TreeForcedPolicy(ref, w.p_accept, w.p_tree, uni, w.V) if tree else ForcedPolicy(ref, w.p_accept, uni, w.V)
         o.policy = pol
     log(f"cpu baseline: oracle prefill{' + reference decode' if pol else ''} in {time.time() - t0:.1f}s")
     t0 = time.perf_counter()
@@ -301,8 +318,10 @@ def cpu_baseline(w, T, prompt, uni, n_cycles):
     dt = time.perf_counter() - t0
     threads = _blas_threads()
     return {"value": round(n_cycles / dt, 4), "unit": "cycles/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(),
             "sample": f"first {n_cycles} SPD cycles after the {w.P}-token prefill of the same workload "
-                      f"(numpy fp32, {threads} BLAS threads); {dt:.1f}s of CPU work"}
+                      f"(numpy fp32, {threads} BLAS threads of {os.cpu_count()} host CPUs visible); "
+                      f"{dt:.1f}s of CPU work"}
 
 
 def _blas_threads():

@@ -61,6 +61,7 @@ extern "C" {
 #define SPD_MAX_STAGES 16
 #define SPD_MAX_VOCAB (1 << 20)
 #define SPD_MAX_TOPK 64
+#define SPD_MAX_WIDTH 4
 
 /* return codes */
 #define SPD_OK 0
@@ -166,6 +167,22 @@ typedef struct spd_config {
                          0..n_stages-1 are >= 1 and sum to n_layers, the rest are 0, and
                          pdm_layers is at most the longest stage (the cycle lasts as long as
                          its longest stage). */
+  int32_t draft_width; /* draft tree ([RB] prerequisites "draft tree": keep the top-W branches by
+                         cumulative probability; [PL] appendix B widens each SPD draft step into a
+                         width-4 tree).  0 or 1: one draft per cycle (a chain).  W in 2..
+                         SPD_MAX_WIDTH: the tokens in flight form a tree of at most W nodes per
+                         position (one at the oldest); every cycle the draft module runs on
+                         every node's pre-step features (each row attending to its own
+                         ancestors), scores each pair (leaf, token) among the leaves' W most
+                         likely tokens by cum(leaf) + log Q_leaf(token) -- cum summing log Q
+                         along the leaf's in-flight path -- and the next cycle enters the best W
+                         whose leaf survived verification; the exiting node keeps the child that
+                         matches the target's argmax and prunes the others, and the three-step
+                         rollback runs only when no child matches.  Each leaf owns a KV lane (a
+                         full cache copy): a node's key/values go to its descendants' lanes, so
+                         every node attends to committed prefix + ancestors + itself.  Needs
+                         greedy mode, the pre-step schedule, 2 <= n_stages, attn_period = 0,
+                         uniform stages, and 2 + (n_stages - 1) * W <= 32 draft rows. */
 } spd_config;
 
 /* Device pointers of one decoder layer.  Row-major, output features first:
@@ -190,7 +207,11 @@ typedef struct spd_weights {
 
 /* One record per enqueued cycle, written on the device and copied to the
  * caller's host buffer by spd_cycle.  kv_len[] holds every target layer's KV
- * length after the cycle (after any rollback truncation). */
+ * length after the cycle (after any rollback truncation); with a draft tree,
+ * the committed length (the tree's in-flight key/values live in its lanes),
+ * the same in every layer.  With a draft tree, draft / pdm_argmax are the
+ * best-ranked candidate's token and the draft module's top token of the
+ * rank-0 leaf. */
 typedef struct spd_cycle_rec {
   int32_t cycle;        /* engine cycle index */
   int32_t t;            /* position of the newest in-flight token (this cycle's seed) */
@@ -205,6 +226,12 @@ typedef struct spd_cycle_rec {
   int32_t emitted;      /* tokens emitted so far (including the prefill token) */
   uint32_t flags;       /* SPD_FLAG_* */
   int32_t kv_len[SPD_MAX_LAYERS];
+  /* draft tree (draft_width >= 2; a chain fills the first entries): */
+  int32_t nodes;        /* nodes in flight after entry */
+  int32_t n_new;        /* nodes that entered this cycle (at position t), in rank order: */
+  int32_t new_parent[SPD_MAX_WIDTH]; /* rank of each one's parent at t-1 (-1: re-seeded) */
+  int32_t new_token[SPD_MAX_WIDTH];
+  int32_t accepted_rank; /* rank of the kept child at exit_pos+1, or -1 */
 } spd_cycle_rec;
 
 typedef struct spd_status {
@@ -269,6 +296,18 @@ SPD_API int spd_init_static_scratch(const spd_config *cfg, const spd_weights *w,
  * policy.  Errors: SPD_EINVAL. */
 SPD_API int spd_set_draft_policy(spd_t *h, int32_t policy, float p_accept, const int32_t *ref_tokens_dev,
                          int32_t ref_len);
+
+/* Forced acceptance for draft trees (test harness device, greedy only; not
+ * on the pages): with ref_tokens the target's greedy continuation and the
+ * forced leaf (the leaf whose in-flight path matches ref_tokens, else the
+ * rank-0 leaf), u = u[q][SPD_U_FORCE] for position q puts the pair (forced
+ * leaf, ref[q]) first in the ranking when u < p_first, at rank W-1 when
+ * p_first <= u < p_tree (a second-ranked draft only a tree catches), and
+ * otherwise replaces it by the next id not already a candidate of that leaf.
+ * Positions >= ref_len are drafted naturally.  Needs draft_width >= 2 and the
+ * uniform table.  Errors: SPD_EINVAL. */
+SPD_API int spd_set_tree_policy(spd_t *h, float p_first, float p_tree, const int32_t *ref_tokens_dev,
+                                int32_t ref_len);
 
 /* How spd_cycle submits work.  SPD_LAUNCH_GRAPH (the default): each
  * stream's chain of one cycle is captured once as a HIP graph (on the first

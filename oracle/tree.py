@@ -362,7 +362,7 @@ class TreeSPDOracle:
                 self.hook("pdm", dict(cycle=c, rank=r, logits=lg))
             lq = log_softmax64(lg)
             lq_all.append(lq)
-            cum = sum(x.logq for x in leaf.path(min(p for p in self.levels))[1:])
+            cum = sum(x.logq for x in leaf.path(min(self.levels)))
             order = np.lexsort((np.arange(len(lg)), -lg.astype(np.float64)))[: self.Wd]
             if r == 0:
                 top_tok = int(order[0])
@@ -385,7 +385,7 @@ class TreeSPDOracle:
                 break
         leaf, R = leaves[star], pol.ref[q]
         u = pol.u[q, U_FORCE]
-        cum = sum(x.logq for x in leaf.path(oldest)[1:])
+        cum = sum(x.logq for x in leaf.path(oldest))
         lq = lq_all[star]
         cands = [cd for cd in cands]
         at = [i for i, cd in enumerate(cands) if cd[0] is leaf and cd[1] == R]

@@ -19,6 +19,7 @@ SPD_MAX_ANCHORS = 8
 SPD_MAX_STAGES = 16
 SPD_MAX_VOCAB = 1 << 20
 SPD_MAX_TOPK = 64
+SPD_MAX_WIDTH = 4
 
 SPD_OK, SPD_EINVAL, SPD_ESTATE, SPD_ECTX, SPD_EHIP, SPD_EDEVICE, SPD_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 SPD_STATIC_SCRATCH_MB = 64
@@ -41,6 +42,7 @@ class spd_config(Structure):
         ("rms_eps", c_float), ("rope_base", c_float), ("temperature", c_float),
         ("schedule", c_int32), ("attn_period", c_int32), ("top_k", c_int32),
         ("stage_layers", c_int32 * SPD_MAX_STAGES),
+        ("draft_width", c_int32),
     ]
 
 
@@ -65,6 +67,8 @@ class spd_cycle_rec(Structure):
         ("pdm_argmax", c_int32), ("draft", c_int32), ("exit_pos", c_int32), ("target_token", c_int32),
         ("accepted", c_int32), ("pdm_len", c_int32), ("emitted", c_int32), ("flags", c_uint32),
         ("kv_len", c_int32 * SPD_MAX_LAYERS),
+        ("nodes", c_int32), ("n_new", c_int32), ("new_parent", c_int32 * SPD_MAX_WIDTH),
+        ("new_token", c_int32 * SPD_MAX_WIDTH), ("accepted_rank", c_int32),
     ]
 
 
@@ -83,6 +87,7 @@ SIGNATURES = [
     ("spd_init_static_scratch", c_int32, [POINTER(spd_config), POINTER(spd_weights), c_void_p, POINTER(c_size_t),
                                           c_void_p, c_void_p, POINTER(c_void_p)]),
     ("spd_set_draft_policy", c_int32, [c_void_p, c_int32, c_float, c_void_p, c_int32]),
+    ("spd_set_tree_policy", c_int32, [c_void_p, c_float, c_float, c_void_p, c_int32]),
     ("spd_set_launch_mode", c_int32, [c_void_p, c_int32]),
     ("spd_set_uniforms", c_int32, [c_void_p, c_void_p, c_int32]),
     ("spd_prefill", c_int32, [c_void_p, POINTER(c_int32), c_int32, POINTER(c_int32)]),
@@ -166,6 +171,10 @@ def spd_init_static_scratch(cfg, weights=None, state_ptr=None, state_bytes=0, st
 
 def spd_set_draft_policy(h, policy, p_accept, ref_ptr, ref_len):
     return check("spd_set_draft_policy", lib().spd_set_draft_policy(h, policy, p_accept, c_void_p(ref_ptr), ref_len))
+
+
+def spd_set_tree_policy(h, p_first, p_tree, ref_ptr, ref_len):
+    return check("spd_set_tree_policy", lib().spd_set_tree_policy(h, p_first, p_tree, c_void_p(ref_ptr), ref_len))
 
 
 SPD_LAUNCH_EAGER, SPD_LAUNCH_GRAPH, SPD_LAUNCH_SERIALIZED = 0, 1, 2

@@ -51,29 +51,84 @@ struct Attn {
   int from_ctrl, pos0_arg, nrows_arg;
   int QB;          // rows per workgroup (rows mode)
   int qblocks;     // row blocks (rows mode)
+  long long lane_stride;  // draft tree: elements between the caches' KV lanes
   const Ctrl* ctrl;
   Geo g;
 };
 
-__device__ __forceinline__ bool attn_problem(const Attn& A, int z, int& pos0, int& nrows, int& layer) {
+// The problem of workgroup (z, row block qb): positions pos0 + r0 .. of its
+// rows (r0 = qb * QB), the row count, the layer, the KV lane offset and the
+// scratch row of its first query row.  A draft tree's stage groups hold one
+// node each (z = group * W + rank); its draft-module rows take one row per
+// workgroup (QB = 1), each at its own position and KV lane.
+__device__ __forceinline__ bool attn_problem(const Attn& A, int z, int qb, int& pos0, int& nrows, int& layer,
+                                             long long& kvoff, int& prow0) {
   const Ctrl* C = A.ctrl;
+  const Geo& g = A.g;
+  kvoff = 0;
   if (A.pmode == PM_STAGE) {
-    if (!C->active || A.stage[z] >= C->a) return false;
-    if (layer_is_linear(A.g, A.layer[z])) return false;  // the linear-attention kernel's group
-    pos0 = C->t - A.stage[z];
+    const int grp = z / g.W, r = z - grp * g.W;
+    if (!C->active || A.stage[grp] >= C->a) return false;
+    if (layer_is_linear(g, A.layer[grp])) return false;  // the linear-attention kernel's group
+    pos0 = C->t - A.stage[grp];
+    if (g.W > 1) {
+      const Tree* T = tree_of(C);
+      const int ps = pos0 % g.nslots;
+      if (r >= T->cnt[ps]) return false;
+      kvoff = T->lane[ps * g.W + T->rk[ps][r]] * A.lane_stride;
+    }
     nrows = 1;
-    layer = A.layer[z];
-  } else {
-    if (A.from_ctrl) {
-      if (!C->active) return false;
+    layer = A.layer[grp];
+    prow0 = z;
+    return qb == 0;
+  }
+  if (A.from_ctrl) {
+    if (!C->active) return false;
+    if (g.W > 1) {
+      const Tree* T = tree_of(C);
+      if (qb >= T->nrows) return false;
+      pos0 = T->row_pos[qb] - qb;
+      nrows = T->nrows;
+      kvoff = T->row_lane[qb] * A.lane_stride;
+    } else {
       pos0 = C->C;
       nrows = C->a + C->pending;
-    } else {
-      pos0 = A.pos0_arg;
-      nrows = A.nrows_arg;
     }
-    layer = A.layer[0];
+  } else {
+    pos0 = A.pos0_arg;
+    nrows = A.nrows_arg;
   }
+  layer = A.layer[0];
+  prow0 = qb * A.QB;
+  return true;
+}
+
+// Position of attention output row prow (merges).
+__device__ __forceinline__ bool attn_row_pos(const Attn& A, int prow, int& pos) {
+  const Ctrl* C = A.ctrl;
+  const Geo& g = A.g;
+  if (A.pmode == PM_STAGE) {
+    const int grp = prow / g.W, r = prow - grp * g.W;
+    if (!C->active || A.stage[grp] >= C->a) return false;
+    if (layer_is_linear(g, A.layer[grp])) return false;  // written by the linear-attention kernel
+    pos = C->t - A.stage[grp];
+    if (g.W > 1 && r >= tree_of(C)->cnt[pos % g.nslots]) return false;
+    return true;
+  }
+  if (A.from_ctrl) {
+    if (!C->active) return false;
+    if (g.W > 1) {
+      const Tree* T = tree_of(C);
+      if (prow >= T->nrows) return false;
+      pos = T->row_pos[prow];
+      return true;
+    }
+    if (prow >= C->a + C->pending) return false;
+    pos = C->C + prow;
+    return true;
+  }
+  if (prow >= A.nrows_arg) return false;
+  pos = A.pos0_arg + prow;
   return true;
 }
 
@@ -115,8 +170,9 @@ __global__ __launch_bounds__(kWG) void k_attn_valu(const Attn A) {
   __shared__ float rmax[kWG / kWave][kAttnQ];
   __shared__ float rsum[kWG / kWave][kAttnQ];
   __shared__ float racc[kWG / kWave][kAttnQ][HD];
-  int pos0, nrows, layer;
-  if (!attn_problem(A, blockIdx.z, pos0, nrows, layer)) return;
+  int pos0, nrows, layer, prow0;
+  long long kvoff;
+  if (!attn_problem(A, blockIdx.z, blockIdx.y / A.g.Hkv, pos0, nrows, layer, kvoff, prow0)) return;
   constexpr int NC = HD / 8;        // 8-element chunks per row
   constexpr int DL = HD / 8;        // lanes per value row
   constexpr int PG = kWave / DL;    // positions per wave instruction
@@ -135,13 +191,12 @@ __global__ __launch_bounds__(kWG) void k_attn_valu(const Attn A) {
   const int s0 = blockIdx.x * kSplit;
   const int maxpos = pos0 + r0 + nr - 1;
   if (s0 > maxpos) return;
-  const int prow0 = (A.pmode == PM_STAGE) ? blockIdx.z : r0;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int dl = lane % DL, pg = lane / DL;
   const int gp = wave * PG + pg;
-  const KT* K = reinterpret_cast<const KT*>(A.kc);
-  const KT* Vc = reinterpret_cast<const KT*>(A.vc);
+  const KT* K = reinterpret_cast<const KT*>(A.kc) + kvoff;
+  const KT* Vc = reinterpret_cast<const KT*>(A.vc) + kvoff;
 
   for (int idx = threadIdx.x; idx < nq * HD; idx += kWG) {
     const int qi = idx / HD, dim = idx - qi * HD;
@@ -298,8 +353,9 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(const Attn A) {
   uint16_t* pl = ph + NQ * PP;
   float* wmax = reinterpret_cast<float*>(pl + NQ * PP);  // [wave][NQ]
   float* wsum = wmax + (kWG / kWave) * NQ;
-  int pos0, nrows, layer;
-  if (!attn_problem(A, blockIdx.z, pos0, nrows, layer)) return;
+  int pos0, nrows, layer, prow0;
+  long long kvoff;
+  if (!attn_problem(A, blockIdx.z, blockIdx.y / A.g.Hkv, pos0, nrows, layer, kvoff, prow0)) return;
   const Geo& g = A.g;
   const int G = g.Hq / g.Hkv;
   const int kvh = blockIdx.y % g.Hkv;
@@ -312,11 +368,10 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(const Attn A) {
   const int s0 = blockIdx.x * kSplit;
   const int maxpos = pos0 + r0 + nr - 1;
   if (s0 > maxpos) return;
-  const int prow0 = (A.pmode == PM_STAGE) ? blockIdx.z : r0;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r = lane & 15, kq = lane >> 4;
-  const uint16_t* K = reinterpret_cast<const uint16_t*>(A.kc);
-  const uint16_t* Vc = reinterpret_cast<const uint16_t*>(A.vc);
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(A.kc) + kvoff;
+  const uint16_t* Vc = reinterpret_cast<const uint16_t*>(A.vc) + kvoff;
   const int pw0 = s0 + 64 * wave;  // this wave's 64 score positions
 
   // ---- loads: keys of the wave's positions, values of its head-dim tiles ----
@@ -483,26 +538,9 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(const Attn A) {
 template <int HD>
 __global__ __launch_bounds__(HD) void k_attn_merge(const Attn A) {
   const Geo& g = A.g;
-  const Ctrl* C = A.ctrl;
   const int prow = blockIdx.x, head = blockIdx.y;
   int pos;
-  if (A.pmode == PM_STAGE) {
-    if (!C->active || A.stage[prow] >= C->a) return;
-    if (layer_is_linear(g, A.layer[prow])) return;  // written by the linear-attention kernel
-    pos = C->t - A.stage[prow];
-  } else {
-    int pos0, nrows;
-    if (A.from_ctrl) {
-      if (!C->active) return;
-      pos0 = C->C;
-      nrows = C->a + C->pending;
-    } else {
-      pos0 = A.pos0_arg;
-      nrows = A.nrows_arg;
-    }
-    if (prow >= nrows) return;
-    pos = pos0 + prow;
-  }
+  if (!attn_row_pos(A, prow, pos)) return;
   const int ns = pos / kSplit + 1;
   const int dim = threadIdx.x;
   const size_t base = attn_part(g, prow, head, 0);

@@ -50,6 +50,43 @@ struct ArgPair {
   int32_t i;
 };
 
+// ---- draft trees ([RB] prerequisites "draft tree"; [PL] appendix B) --------
+// The tokens in flight form a tree: at most W nodes per in-flight position,
+// one at the oldest.  Node slot = (position mod nslots) * W + phys; the ranks
+// of the live nodes at a position map to phys indices through rk.  Every
+// node's target key/values go to the KV lanes of its descendant leaves (one
+// full cache copy per lane), so each node attends to committed prefix +
+// ancestors + itself in its own lane with the single-chain arithmetic.
+constexpr int kMaxW = 4;
+constexpr int kMaxTreeSlots = (SPD_MAX_STAGES + 1) * kMaxW;
+constexpr int kMaxTreeRows = 32;
+constexpr int kMaxCand = kMaxW * kMaxW + 1;
+
+struct Tree {
+  int32_t cnt[SPD_MAX_STAGES + 1];         // live nodes per position slot
+  int32_t rk[SPD_MAX_STAGES + 1][kMaxW];   // phys index of rank r at a position slot
+  int32_t tok[kMaxTreeSlots];
+  int32_t parent[kMaxTreeSlots];           // node slot of the parent, -1: none
+  int32_t lanes[kMaxTreeSlots];            // KV lanes (bitmask) its key/values go to
+  int32_t lane[kMaxTreeSlots];             // the lane its attention reads
+  double logq[kMaxTreeSlots];              // log Q of its token under its parent's draft
+  // candidates of the last draft step, ranked (leaf node slot, token, log Q)
+  int32_t ncand;
+  int32_t cand_leaf[kMaxCand];
+  int32_t cand_tok[kMaxCand];
+  double cand_lq[kMaxCand];
+  // lane copies the entry asked for: positions copy_lo..copy_hi of every layer
+  int32_t ncopy, copy_lo, copy_hi;
+  int32_t copy_src[kMaxW], copy_dst[kMaxW];
+  // draft-module rows of the cycle: the committed-next row, then the nodes
+  int32_t nrows, nleaves;
+  int32_t row_slot[kMaxTreeRows], row_pos[kMaxTreeRows], row_depth[kMaxTreeRows];
+  int32_t row_lanes[kMaxTreeRows], row_lane[kMaxTreeRows];
+  int32_t exit_slot;   // slot of the oldest node (exits when the pipeline is full)
+  int32_t pend_slot;   // slot of the exited node whose draft row is committed this cycle
+  int32_t last_exit;   // slot of the node that exited last (-1: none)
+};
+
 // A token id from an argmax/draw, forced into [0, V); flags non-finite input.
 __device__ __forceinline__ int valid_token(int y, int V, uint32_t* flags) {
   if (y < 0 || y >= V) {
@@ -218,6 +255,9 @@ struct Geo {
   int topk;      // sample mode: top-k truncation of P and Q (0: none)
   int attn_period;  // hybrid target: softmax attention iff layer % P == P - 1, else linear (0: all softmax)
   float eps;
+  int W;            // draft-tree width (1: a single chain of drafts)
+  long long lane_kv;   // elements between target KV lanes (tree mode)
+  long long lane_pkv;  // elements between draft-module KV lanes (tree mode)
   int anchor_of_layer[SPD_MAX_LAYERS + 1];  // anchor index of boundary b, or -1
   int fpat[SPD_MAX_STAGES + 1];             // f(k) for k = 0..n
   int sstart[SPD_MAX_STAGES + 1];           // first layer of stage k; sstart[n] = L
@@ -228,6 +268,19 @@ struct Geo {
 // unless attn_period is 0 or l is the last layer of its block.
 __device__ __host__ __forceinline__ bool layer_is_linear(const Geo& g, int layer) {
   return g.attn_period > 0 && (layer % g.attn_period) != g.attn_period - 1;
+}
+
+// The tree state sits right after the control block.
+__device__ __host__ __forceinline__ Tree* tree_of(Ctrl* C) {
+  return reinterpret_cast<Tree*>(reinterpret_cast<char*>(C) + sizeof(Ctrl));
+}
+__device__ __host__ __forceinline__ const Tree* tree_of(const Ctrl* C) {
+  return reinterpret_cast<const Tree*>(reinterpret_cast<const char*>(C) + sizeof(Ctrl));
+}
+// Node slot of rank r at position p.
+__device__ __forceinline__ int tree_slot(const Geo& g, const Tree* T, int p, int r) {
+  const int ps = p % g.nslots;
+  return ps * g.W + T->rk[ps][r];
 }
 
 // Depth (stages completed) of the feature of draft-module row i, position p.

@@ -618,6 +618,10 @@ __global__ __launch_bounds__(kWG) void k_entry(Ctrl* C, const Geo g, int32_t* to
     r->cycle = cyc;
     r->pdm_argmax = r->draft = r->exit_pos = r->target_token = -1;
     r->accepted = -1;
+    r->accepted_rank = -1;
+    r->nodes = 0;
+    r->n_new = 0;
+    for (int k = 0; k < SPD_MAX_WIDTH; ++k) r->new_parent[k] = r->new_token[k] = -1;
     s_ok = 0;
     if (C->done) {
       C->active = 0;
@@ -629,6 +633,7 @@ __global__ __launch_bounds__(kWG) void k_entry(Ctrl* C, const Geo g, int32_t* to
       r->flags = SPD_FLAG_IDLE;
     } else {
       int tok, pos, a;
+      r->new_parent[0] = C->reseed ? -1 : 0;
       if (C->reseed) {
         tok = C->seed_tok;
         pos = C->seed_pos;
@@ -651,6 +656,9 @@ __global__ __launch_bounds__(kWG) void k_entry(Ctrl* C, const Geo g, int32_t* to
       r->occupancy = a;
       r->pending_row = C->pending;
       r->flags = fl;
+      r->nodes = a;
+      r->n_new = 1;
+      r->new_token[0] = tok;
       if (fl) {
         C->active = 0;
         C->done = 1;
@@ -840,6 +848,7 @@ __global__ __launch_bounds__(kCtlThreads) void k_verify(const VerifyArgs A) {
     rec->exit_pos = j;
     rec->target_token = y;
     rec->accepted = acc;
+    rec->accepted_rank = acc ? 0 : -1;
     rec->emitted = C->emitted;
     rec->flags |= C->flags;
   }

@@ -25,6 +25,7 @@
 #include "gemv.h"
 #include "linattn.h"
 #include "mfma.h"
+#include "tree.h"
 
 using namespace spd;
 
@@ -43,6 +44,7 @@ struct Layout {
   size_t logits, plogits, pw, parts, pparts, ring;
   size_t ssq_t, ssq_p, mpart;
   size_t lin_state, lin_ckpt;
+  size_t zpart, tpart;
   size_t bsq, bsp;
   size_t tkq, tkp;
   size_t state_total;    // persistent state: KV caches, control block, rings, tables, in-flight slots
@@ -103,8 +105,19 @@ bool valid_config(const spd_config* c) {
   if (c->schedule == SPD_SCHED_POST && c->n_stages < 2) return false;
   if (c->top_k < 0 || c->top_k > SPD_MAX_TOPK || c->top_k > c->vocab) return false;
   if (c->attn_period < 0 || c->attn_period > c->n_layers) return false;
+  // draft trees: greedy, pre-step, n >= 2, softmax attention, uniform stages,
+  // and the draft module's rows (2 + (n - 1) W) within two row tiles
+  if (c->draft_width < 0 || c->draft_width > SPD_MAX_WIDTH) return false;
+  if (c->draft_width >= 2) {
+    if (c->mode != SPD_MODE_GREEDY || c->schedule != SPD_SCHED_PRE || c->n_stages < 2 || c->attn_period != 0 ||
+        has_split(c))
+      return false;
+    if (2 + (c->n_stages - 1) * c->draft_width > kMaxTreeRows) return false;
+  }
   return true;
 }
+
+int width_of(const spd_config* c) { return c->draft_width >= 2 ? c->draft_width : 1; }
 
 // Workgroups of k_topk_blocks over a vocabulary of V ids, and the candidate
 // keys they leave (64 each).
@@ -145,9 +158,11 @@ Layout make_layout(const spd_config* c) {
   const size_t es = c->dtype == SPD_DTYPE_BF16 ? 2 : 4;
   const int n = c->n_stages, d = c->d_model, Hq = c->n_heads, Hkv = c->n_kv_heads, hd = c->head_dim;
   const int F = c->d_ffn, V = c->vocab, m = c->n_anchors;
+  const int Wd = width_of(c);  // draft-tree width: KV lanes, nodes per position
   L.ctx_cap = (int)align_up((size_t)c->max_ctx, kSplit);
   L.nsplit = L.ctx_cap / kSplit;
-  L.mr = std::max(kRowsMR, (int)align_up((size_t)(n + 1), kRowsMR));
+  const int prow_max = Wd > 1 ? 2 + (n - 1) * Wd : n + 1;  // draft-module rows
+  L.mr = std::max(kRowsMR, (int)align_up((size_t)prow_max, kRowsMR));
   L.log_cap = std::max(4096, n * c->max_new + 64);
   L.nparts_max = kCUs * kPersistPerCU;
   const int nslots = n + 1;
@@ -162,7 +177,7 @@ Layout make_layout(const spd_config* c) {
     soff = align_up(soff + bytes, kAlign);
     return o;
   };
-  L.ctrl = take(sizeof(Ctrl));
+  L.ctrl = take(sizeof(Ctrl) + sizeof(Tree));
   L.kv_len = take(sizeof(int32_t) * SPD_MAX_LAYERS);
   L.tokens = take(sizeof(int32_t) * L.ctx_cap);
   L.dring = take(sizeof(int32_t) * nslots);
@@ -171,20 +186,21 @@ Layout make_layout(const spd_config* c) {
   L.qring = take(!smp ? 0 : c->top_k ? sizeof(SparseQ) * nslots : sizeof(float) * nslots * (size_t)V);
   L.qz = take(sizeof(double) * nslots);
   const size_t kvl = (size_t)Hkv * hd * L.ctx_cap * es;
-  L.kc = take(kvl * c->n_layers);
-  L.vc = take(kvl * c->n_layers);
-  L.pkc = take(kvl * c->pdm_layers);
-  L.pvc = take(kvl * c->pdm_layers);
+  L.kc = take(kvl * c->n_layers * Wd);
+  L.vc = take(kvl * c->n_layers * Wd);
+  L.pkc = take(kvl * c->pdm_layers * Wd);
+  L.pvc = take(kvl * c->pdm_layers * Wd);
   L.rcos = take(sizeof(float) * (size_t)L.ctx_cap * (hd / 2));
   L.rsin = take(sizeof(float) * (size_t)L.ctx_cap * (hd / 2));
-  L.hslots = take(sizeof(float) * (size_t)nslots * d);
-  L.anchors = take(sizeof(float) * (size_t)nslots * m * d);
+  L.hslots = take(sizeof(float) * (size_t)nslots * Wd * d);
+  L.anchors = take(sizeof(float) * (size_t)nslots * Wd * m * d);
   const size_t qd = (size_t)Hq * hd;
-  L.s_q = scr(sizeof(float) * n * qd);
-  L.s_pacc = scr(sizeof(float) * n * (size_t)Hq * L.nsplit * hd);
-  L.s_pml = scr(sizeof(float) * n * (size_t)Hq * L.nsplit * 2);
-  L.s_o = scr(sizeof(float) * n * qd);
-  L.s_act = scr(sizeof(float) * n * (size_t)F);
+  const int srows = n * Wd;  // stage-step rows: W nodes per stage group
+  L.s_q = scr(sizeof(float) * srows * qd);
+  L.s_pacc = scr(sizeof(float) * srows * (size_t)Hq * L.nsplit * hd);
+  L.s_pml = scr(sizeof(float) * srows * (size_t)Hq * L.nsplit * 2);
+  L.s_o = scr(sizeof(float) * srows * qd);
+  L.s_act = scr(sizeof(float) * srows * (size_t)F);
   L.Xt = scr(sizeof(float) * L.mr * (size_t)d);
   L.Xp = scr(sizeof(float) * L.mr * (size_t)d);
   L.r_q = scr(sizeof(float) * L.mr * qd);
@@ -194,10 +210,13 @@ Layout make_layout(const spd_config* c) {
   L.r_act = scr(sizeof(float) * L.mr * (size_t)F);
   L.taps = scr(sizeof(float) * kRowsMR * (size_t)m * d);
   L.logits = scr(sizeof(float) * (size_t)V);
-  L.plogits = scr(sizeof(float) * (size_t)V);
+  L.plogits = scr(sizeof(float) * (size_t)V * Wd);
   L.pw = scr(sizeof(float) * (size_t)V);
   L.parts = scr(sizeof(ArgPair) * L.nparts_max);
-  L.pparts = scr(sizeof(ArgPair) * L.nparts_max);
+  L.pparts = scr(sizeof(ArgPair) * L.nparts_max * Wd);
+  const int nblk = Wd > 1 ? tree_scan_blocks(V) : 0;
+  L.zpart = scr(sizeof(double) * Wd * nblk);
+  L.tpart = scr(sizeof(ArgPair) * Wd * nblk * Wd);
   L.ring = take(sizeof(spd_cycle_rec) * (size_t)L.log_cap);
   // matrix-core path (bf16): per-row partial sums of squares of the prefill
   // rows and the draft-module rows, and the split-K partial tiles
@@ -261,6 +280,9 @@ struct spd_handle {
   float *ssq_t, *ssq_p, *mpart;
   float *lin_state = nullptr, *lin_ckpt = nullptr;
   double *bsq = nullptr, *bsp = nullptr;  // dense sampling block sums (Q, P)
+  double* zpart = nullptr;                 // draft tree: per-leaf softmax partial sums
+  ArgPair* tpart = nullptr;                // draft tree: per-leaf partial top-W
+  float p_first = 0.f, p_tree = 0.f;       // draft tree forced policy
   unsigned long long *tkq = nullptr, *tkp = nullptr;  // top-k candidate keys (Q, P)
   int ckpt_len = 0;     // prefill length whose linear-attention states lin_ckpt holds
   int lin_newest = -1;  // newest position whose linear-attention state a row pass wrote
@@ -301,6 +323,10 @@ int hip_fail(spd_t* h, hipError_t e) {
   return SPD_EHIP;
 }
 
+// Most draft-module rows of one cycle: the committed-next row and the tokens
+// in flight (a draft tree: one oldest node, W per later position).
+int pdm_rows(const Geo& g) { return g.W > 1 ? 2 + (g.n - 1) * g.W : g.n + 1; }
+
 namespace {
 
 hipEvent_t pool_event(spd_t* h) {
@@ -322,18 +348,29 @@ int stage_grid(int units, int upt, int n_groups, int K) {
   return std::max(1, std::min(tiles, kCUs * occ));
 }
 
-template <typename WT, int EPI>
+template <typename WT, int EPI, int NR = 1>
 void launch_stage(spd_t* h, const StageGemv& a, int n_groups_max, hipStream_t s, int* grid_out = nullptr) {
   constexpr int upt = (epi_pairs(EPI) ? 2 : 4) * (kWG / kWave);
   // un-normalised long inputs (the down projection) are read from the cache
   // rather than staged: no LDS, so the draft stream's kernels fit beside it
   const bool xg = EPI == EPI_RESID && a.K > h->g.d;
-  const int grid = stage_grid(a.units, upt, n_groups_max, xg ? 0 : a.K);
+  const int grid = stage_grid(a.units, upt, n_groups_max, xg ? 0 : NR * a.K);
   if (grid_out) *grid_out = grid;
   if (xg)
-    hipLaunchKernelGGL((k_gemv_stage<WT, EPI, true>), dim3(grid), dim3(kWG), 0, s, a);
+    hipLaunchKernelGGL((k_gemv_stage<WT, EPI, true, NR>), dim3(grid), dim3(kWG), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemv_stage<WT, EPI>), dim3(grid), dim3(kWG), a.K * sizeof(float), s, a);
+    hipLaunchKernelGGL((k_gemv_stage<WT, EPI, false, NR>), dim3(grid), dim3(kWG), NR * a.K * sizeof(float), s, a);
+}
+
+// The stage GEMVs of a draft tree take the W nodes of a stage as rows.
+template <typename WT, int EPI>
+void launch_stage_w(spd_t* h, const StageGemv& a, int n_groups_max, hipStream_t s, int* grid_out = nullptr) {
+  switch (h->g.W) {
+    case 1: launch_stage<WT, EPI, 1>(h, a, n_groups_max, s, grid_out); break;
+    case 2: launch_stage<WT, EPI, 2>(h, a, n_groups_max, s, grid_out); break;
+    case 3: launch_stage<WT, EPI, 3>(h, a, n_groups_max, s, grid_out); break;
+    default: launch_stage<WT, EPI, 4>(h, a, n_groups_max, s, grid_out); break;
+  }
 }
 
 template <typename WT, int EPI>
@@ -460,7 +497,12 @@ void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, in
   t.pos0_arg = pos0;
   t.nrows_arg = M;
   int QT = 1;
-  if (sizeof(WT) == 2) {
+  if (from_ctrl && g.W > 1) {
+    // a draft tree's rows: one per workgroup, each at its own position and lane
+    t.QB = 1;
+    QT = (G + 15) / 16;
+    t.lane_stride = g.lane_pkv;
+  } else if (sizeof(WT) == 2) {
     // one query tile per workgroup: more workgroups, each streaming its KV
     // split once more from the cache
     t.QB = std::max(1, std::min(16 / G, max_rows));
@@ -482,7 +524,7 @@ void rows_layer(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, int l
                 int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s,
                 bool linear = false) {
   const Geo& g = h->g;
-  const int max_rows = from_ctrl ? g.n + 1 : M;
+  const int max_rows = from_ctrl ? pdm_rows(g) : M;
   const int qd = g.Hq * g.hd;
   RowsGemv a = rows_base(h);
   a.from_ctrl = from_ctrl;
@@ -594,7 +636,7 @@ void rows_layer_mfma(spd_t* h, const spd_layer_weights& lw, void* kc, void* vc, 
                      int M, int pos0, int from_ctrl, int* kv_len, float* taps, int anchor_idx, hipStream_t s,
                      bool linear = false) {
   const Geo& g = h->g;
-  const int max_rows = from_ctrl ? g.n + 1 : M;
+  const int max_rows = from_ctrl ? pdm_rows(g) : M;
   const int qd = g.Hq * g.hd;
   MfmaArgs a = mfma_base(h);
   a.M_arg = M;
@@ -724,7 +766,7 @@ int pdm_chain(spd_t* h, hipStream_t ps) {
       a.out = h->Xp;
       a.ldo = g.d;
       a.ssq_out = h->ssq_p;
-      launch_mfma<EPI_STORE>(h, a, g.m, g.n + 1, ps);
+      launch_mfma<EPI_STORE>(h, a, g.m, pdm_rows(g), ps);
     } else {
       RowsGemv a = rows_base(h);
       a.rmode = RM_FC;
@@ -739,7 +781,7 @@ int pdm_chain(spd_t* h, hipStream_t ps) {
       a.out = h->Xp;
       a.ldo = g.d;
       a.slot_anchors = h->anchors;
-      launch_rows<WT, EPI_STORE>(h, a, g.n + 1, ps);
+      launch_rows<WT, EPI_STORE>(h, a, pdm_rows(g), ps);
     }
     for (int l = 0; l < g.Ls; ++l)
       layer_rows_any<WT>(h, true, w.pdm[l], h->pkc, h->pvc, l, h->Xp, h->ssq_p, 0, 0, 1, nullptr, nullptr, -1, ps);
@@ -756,6 +798,41 @@ int pdm_chain(spd_t* h, hipStream_t ps) {
     hd.out = h->plogits;
     hd.parts = h->pparts;
     int grid = 0;
+    if (g.W > 1) {
+      // a draft tree: the leaves' heads in one weight stream, then their
+      // normalisers and best W tokens, the ranking and the forced policy
+      launch_stage_w<WT, EPI_ARGMAX>(h, hd, 1, ps, &grid);
+      TreeScanArgs sa;
+      memset(&sa, 0, sizeof(sa));
+      sa.logits = h->plogits;
+      sa.parts = h->pparts;
+      sa.nparts = grid;
+      sa.zpart = h->zpart;
+      sa.tpart = h->tpart;
+      sa.ctrl = h->ctrl;
+      sa.g = g;
+      const int nblk = tree_scan_blocks(g.V);
+      hipLaunchKernelGGL(k_tree_scan, dim3(nblk, g.W), dim3(kWG), 0, ps, sa);
+      TreeFinalizeArgs fa;
+      memset(&fa, 0, sizeof(fa));
+      fa.logits = h->plogits;
+      fa.parts = h->pparts;
+      fa.nparts = grid;
+      fa.zpart = h->zpart;
+      fa.tpart = h->tpart;
+      fa.nblk = nblk;
+      fa.uni = h->uni;
+      fa.policy = h->policy;
+      fa.p_first = h->p_first;
+      fa.p_tree = h->p_tree;
+      fa.ref = h->ref;
+      fa.ref_len = h->ref_len;
+      fa.ring = h->ring;
+      fa.ctrl = h->ctrl;
+      fa.g = g;
+      hipLaunchKernelGGL(k_tree_finalize, dim3(1), dim3(kWave), 0, ps, fa);
+      return hipGetLastError() == hipSuccess ? SPD_OK : SPD_EHIP;
+    }
     launch_stage<WT, EPI_ARGMAX>(h, hd, 1, ps, &grid);
     if (h->bsq) {
       SoftmaxArgs sm;
@@ -848,7 +925,7 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     a.kc = h->kc;
     a.vc = h->vc;
     a.kv_len = h->kv_len;
-    launch_stage<WT, EPI_QKV>(h, a, ng, ss);
+    launch_stage_w<WT, EPI_QKV>(h, a, ng, ss);
     // attention over each group's own layer cache
     Attn t;
     memset(&t, 0, sizeof(t));
@@ -863,13 +940,15 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     t.pacc = h->s_pacc;
     t.pml = h->s_pml;
     t.o = h->s_o;
+    t.lane_stride = g.lane_kv;
     t.ctrl = h->ctrl;
     t.g = g;
     // a hybrid target's sub-step may hold softmax and linear layers: each
-    // kernel takes its own groups (the layer types are fixed per sub-step)
+    // kernel takes its own groups (the layer types are fixed per sub-step);
+    // a draft tree's groups hold W nodes, one per workgroup
     bool any_soft = false, any_lin = false;
     for (int k = 0; k < ng; ++k) (layer_is_linear(g, a.layer[k]) ? any_lin : any_soft) = true;
-    if (any_soft) attention_any<WT>(t, dim3(g.nsplit, g.Hkv, ng), 1, ng, ss);
+    if (any_soft) attention_any<WT>(t, dim3(g.nsplit, g.Hkv, ng * g.W), 1, ng * g.W, ss);
     if (any_lin) {
       LinAttn la;
       memset(&la, 0, sizeof(la));
@@ -909,7 +988,7 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     o.out = h->hslots;
     o.out_stride = g.d;
     o.out_by_slot = 1;
-    launch_stage<WT, EPI_RESID>(h, o, ng, ss);
+    launch_stage_w<WT, EPI_RESID>(h, o, ng, ss);
     // norm + gate/up + SwiGLU
     StageGemv u = stage_base(h);
     u.n_groups = ng;
@@ -934,7 +1013,7 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
       g1 = pool_event(h);
       HIPCHK(h, hipEventRecord(g0, ss));
     }
-    launch_stage<WT, EPI_SWIGLU>(h, u, ng, ss);
+    launch_stage_w<WT, EPI_SWIGLU>(h, u, ng, ss);
     if (g1) {
       HIPCHK(h, hipEventRecord(g1, ss));
       h->gu_ev.push_back(g0);
@@ -959,7 +1038,7 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
     dn.out_stride = g.d;
     dn.out_by_slot = 1;
     dn.anchors = h->anchors;
-    launch_stage<WT, EPI_RESID>(h, dn, ng, ss);
+    launch_stage_w<WT, EPI_RESID>(h, dn, ng, ss);
   }
   // verification head on the exiting token, then verify / rollback
   StageGemv hd = stage_base(h);
@@ -977,6 +1056,22 @@ int stage_chain(spd_t* h, hipStream_t ss, bool timing_gu) {
   hd.parts = h->parts;
   int grid = 0;
   launch_stage<WT, EPI_ARGMAX>(h, hd, 1, ss, &grid);
+  if (g.W > 1) {
+    TreeVerifyArgs tv;
+    memset(&tv, 0, sizeof(tv));
+    tv.parts = h->parts;
+    tv.nparts = grid;
+    tv.tokens = h->tokens;
+    tv.kv_len = h->kv_len;
+    tv.kc = h->kc;
+    tv.vc = h->vc;
+    tv.kv_bytes = (int)sizeof(WT);
+    tv.ring = h->ring;
+    tv.ctrl = h->ctrl;
+    tv.g = g;
+    hipLaunchKernelGGL(k_tree_verify, dim3(1), dim3(kCtlThreads), 0, ss, tv);
+    return hipGetLastError() == hipSuccess ? SPD_OK : SPD_EHIP;
+  }
   if (h->bsp) {
     SoftmaxArgs sm;
     memset(&sm, 0, sizeof(sm));
@@ -1084,8 +1179,15 @@ int enqueue_cycle(spd_t* h) {
   // join: the previous cycle's draft is done
   HIPCHK(h, hipStreamWaitEvent(ss, h->ev_pdm, 0));
   if (e_start) HIPCHK(h, hipEventRecord(e_start, ss));
-  hipLaunchKernelGGL((k_entry<WT>), dim3(1), dim3(kWG), 0, ss, h->ctrl, g, h->tokens, (const WT*)h->w.embed,
-                     h->hslots, h->anchors, h->ring, h->lay.log_cap);
+  if (g.W > 1) {
+    hipLaunchKernelGGL((k_tree_entry<WT>), dim3(1), dim3(kWG), 0, ss, h->ctrl, g, h->tokens, (const WT*)h->w.embed,
+                       h->hslots, h->anchors, h->ring, h->lay.log_cap);
+    hipLaunchKernelGGL((k_tree_lane_copy<WT>), dim3(g.L, g.W), dim3(kWG), 0, ss, (const Ctrl*)h->ctrl, g, (WT*)h->kc,
+                       (WT*)h->vc);
+  } else {
+    hipLaunchKernelGGL((k_entry<WT>), dim3(1), dim3(kWG), 0, ss, h->ctrl, g, h->tokens, (const WT*)h->w.embed,
+                       h->hslots, h->anchors, h->ring, h->lay.log_cap);
+  }
   // fork
   if (ps != ss) {
     HIPCHK(h, hipEventRecord(h->ev_entry, ss));
@@ -1221,6 +1323,37 @@ int write_ctrl(spd_t* h, const Ctrl* c) {
   return SPD_OK;
 }
 
+// Every KV lane of a draft tree takes lane 0's contents: after prefill, a
+// host rollback or an autoregressive run, the positions before the seed are
+// common to every branch (and lane 0, which those passes write, holds them).
+int sync_lanes(spd_t* h) {
+  const Geo& g = h->g;
+  if (g.W <= 1) return SPD_OK;
+  const size_t es = h->cfg.dtype == SPD_DTYPE_BF16 ? 2 : 4;
+  for (int ln = 1; ln < g.W; ++ln) {
+    HIPCHK(h, hipMemcpyAsync((char*)h->kc + ln * g.lane_kv * es, h->kc, g.lane_kv * es, hipMemcpyDeviceToDevice,
+                             h->ss));
+    HIPCHK(h, hipMemcpyAsync((char*)h->vc + ln * g.lane_kv * es, h->vc, g.lane_kv * es, hipMemcpyDeviceToDevice,
+                             h->ss));
+    HIPCHK(h, hipMemcpyAsync((char*)h->pkc + ln * g.lane_pkv * es, h->pkc, g.lane_pkv * es,
+                             hipMemcpyDeviceToDevice, h->ss));
+    HIPCHK(h, hipMemcpyAsync((char*)h->pvc + ln * g.lane_pkv * es, h->pvc, g.lane_pkv * es,
+                             hipMemcpyDeviceToDevice, h->ss));
+  }
+  HIPCHK(h, hipStreamSynchronize(h->ss));
+  return SPD_OK;
+}
+
+// An empty draft tree (nothing in flight, no candidates, no exited node).
+int reset_tree(spd_t* h) {
+  Tree t0;
+  memset(&t0, 0, sizeof(t0));
+  t0.last_exit = -1;
+  t0.pend_slot = -1;
+  HIPCHK(h, hipMemcpy(tree_of(h->ctrl), &t0, sizeof(t0), hipMemcpyHostToDevice));
+  return SPD_OK;
+}
+
 int set_kv_len(spd_t* h, int len) {
   std::vector<int32_t> v(SPD_MAX_LAYERS, len);
   HIPCHK(h, hipMemcpy(h->kv_len, v.data(), sizeof(int32_t) * SPD_MAX_LAYERS, hipMemcpyHostToDevice));
@@ -1305,6 +1438,9 @@ int init_handle(const spd_config* cfg, const spd_weights* w, char* ws, char* sc,
   g.topk = cfg->mode == SPD_MODE_SAMPLE ? cfg->top_k : 0;
   g.attn_period = cfg->attn_period;
   g.eps = cfg->rms_eps;
+  g.W = width_of(cfg);
+  g.lane_kv = (long long)g.Hkv * g.hd * L.ctx_cap * g.L;
+  g.lane_pkv = (long long)g.Hkv * g.hd * L.ctx_cap * g.Ls;
   for (int b = 0; b <= SPD_MAX_LAYERS; ++b) g.anchor_of_layer[b] = -1;
   for (int i = 0; i < g.m; ++i) g.anchor_of_layer[cfg->anchors[i]] = i;
   g.anchor_of_layer[0] = -1;  // anchor 0 (embedding) is written at entry
@@ -1362,6 +1498,10 @@ int init_handle(const spd_config* cfg, const spd_weights* w, char* ws, char* sc,
     h->tkq = (unsigned long long*)(sc + L.tkq);
     h->tkp = (unsigned long long*)(sc + L.tkp);
   }
+  if (g.W > 1) {
+    h->zpart = (double*)(sc + L.zpart);
+    h->tpart = (ArgPair*)(sc + L.tpart);
+  }
   if (cfg->attn_period > 0) {
     h->lin_state = (float*)(ws + L.lin_state);
     h->lin_ckpt = (float*)(ws + L.lin_ckpt);
@@ -1383,6 +1523,13 @@ int init_handle(const spd_config* cfg, const spd_weights* w, char* ws, char* sc,
   c0.r_exit = -1;
   c0.done = 1;
   if ((e = hipMemcpy(h->ctrl, &c0, sizeof(c0), hipMemcpyHostToDevice)) != hipSuccess) return fail(e);
+  {
+    Tree t0;
+    memset(&t0, 0, sizeof(t0));
+    t0.last_exit = -1;
+    t0.pend_slot = -1;
+    if ((e = hipMemcpy(tree_of(h->ctrl), &t0, sizeof(t0), hipMemcpyHostToDevice)) != hipSuccess) return fail(e);
+  }
   std::vector<int32_t> zl(SPD_MAX_LAYERS, 0);
   if ((e = hipMemcpy(h->kv_len, zl.data(), sizeof(int32_t) * SPD_MAX_LAYERS, hipMemcpyHostToDevice)) != hipSuccess)
     return fail(e);
@@ -1472,10 +1619,23 @@ int spd_set_draft_policy(spd_t* h, int32_t policy, float p_accept, const int32_t
     h->policy = policy;
     return SPD_OK;
   }
-  if (policy != SPD_DRAFT_FORCED || h->cfg.mode != SPD_MODE_GREEDY) return SPD_EINVAL;
+  // a draft tree's forced policy is spd_set_tree_policy
+  if (policy != SPD_DRAFT_FORCED || h->cfg.mode != SPD_MODE_GREEDY || h->g.W > 1) return SPD_EINVAL;
   if (!ref_tokens_dev || ref_len < 0 || !(p_accept >= 0.f && p_accept <= 1.f) || !h->uni) return SPD_EINVAL;
   h->policy = policy;
   h->p_accept = p_accept;
+  h->ref = ref_tokens_dev;
+  h->ref_len = ref_len;
+  return SPD_OK;
+}
+
+int spd_set_tree_policy(spd_t* h, float p_first, float p_tree, const int32_t* ref_tokens_dev, int32_t ref_len) {
+  if (!h || h->g.W < 2 || !ref_tokens_dev || ref_len < 0 || !h->uni) return SPD_EINVAL;
+  if (!(p_first >= 0.f && p_first <= p_tree && p_tree <= 1.f)) return SPD_EINVAL;
+  h->graphs_valid = 0;
+  h->policy = SPD_DRAFT_FORCED;
+  h->p_first = p_first;
+  h->p_tree = p_tree;
   h->ref = ref_tokens_dev;
   h->ref_len = ref_len;
   return SPD_OK;
@@ -1526,9 +1686,11 @@ int spd_prefill(spd_t* h, const int32_t* prompt_host, int32_t len, int32_t* firs
   c.r_accept = -1;
   c.launches = (int32_t)(h->cyc % 0x40000000);
   if ((r = write_ctrl(h, &c))) return r;
+  if ((r = reset_tree(h))) return r;
   r = h->cfg.dtype == SPD_DTYPE_BF16 ? do_prefill<uint16_t>(h, len) : do_prefill<float>(h, len);
   if (r) return r;
   HIPCHK(h, hipStreamSynchronize(h->ss));
+  if ((r = sync_lanes(h))) return r;
   int32_t first = 0;
   HIPCHK(h, hipMemcpy(&first, h->tokens + len, sizeof(int32_t), hipMemcpyDeviceToHost));
   Ctrl cc;
@@ -1625,6 +1787,8 @@ int spd_rollback(spd_t* h, int32_t keep_len, int32_t reseed_token) {
   if ((r = set_kv_len(h, keep_len))) return r;
   HIPCHK(h, hipMemcpy(h->tokens + keep_len, &reseed_token, sizeof(int32_t), hipMemcpyHostToDevice));
   if ((r = write_ctrl(h, &n))) return r;
+  if ((r = reset_tree(h))) return r;
+  if ((r = sync_lanes(h))) return r;
   h->needs_rollback = 0;
   return SPD_OK;
 }

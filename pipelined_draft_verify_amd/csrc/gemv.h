@@ -76,7 +76,7 @@ struct StageGemv {
   int N, K, units, n_groups, gmode;
   const float* x;
   long long x_stride;
-  int x_by_slot;  // input row = x + (slot or group) * x_stride
+  int x_by_slot;  // input row = x + (slot or group row) * x_stride
   float* out;
   long long out_stride;
   int out_by_slot;
@@ -95,19 +95,27 @@ struct StageGemv {
 // instead of being staged in LDS -- for un-normalised long inputs (the down
 // projection), so that the kernel holds no LDS and the draft stream's kernels
 // can share its CUs.  The arithmetic is the same either way.
-// One k-step of four weight rows: fp32 FMAs in element order into acc[r].
-template <typename WT>
-__device__ __forceinline__ void gemv_step(const typename WVec<WT>::Raw* rw, const float* x, float* acc) {
+// One k-step of four weight rows against NR input rows (nr of them live):
+// the weights are converted once, then fp32 FMAs in element order into
+// acc[m][r] -- per input row exactly the single-row chain.
+template <typename WT, int NR>
+__device__ __forceinline__ void gemv_step(const typename WVec<WT>::Raw* rw, const float* const* xr, int k0, int nr,
+                                          float (&acc)[NR][4]) {
   constexpr int VEC = WVec<WT>::N;
-  float xv[VEC];
+  float w[4][VEC];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) xv[e] = x[e];
+  for (int r = 0; r < 4; ++r) WVec<WT>::cvt(rw[r], w[r]);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float w[VEC];
-    WVec<WT>::cvt(rw[r], w);
+  for (int m = 0; m < NR; ++m) {
+    if (NR == 1 || m < nr) {
+      float xv[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[r] = fmaf(w[e], xv[e], acc[r]);
+      for (int e = 0; e < VEC; ++e) xv[e] = xr[m][k0 + e];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[m][r] = fmaf(w[r][e], xv[e], acc[m][r]);
+    }
   }
 }
 
@@ -153,16 +161,36 @@ __device__ __forceinline__ void stage_input(const float* __restrict__ x, const f
   }
 }
 
-template <typename WT, int EPI, bool XG = false>
+// Rows of group `grp` (position pos): the live count and the node slot of
+// each (a single chain: one row, slot pos mod nslots; a draft tree: the live
+// nodes at that position in rank order).
+template <int NR>
+__device__ __forceinline__ int stage_rows(const Geo& g, const Ctrl* C, int pos, int* slot) {
+  const int ps = pos % g.nslots;
+  if (NR == 1 || g.W == 1) {
+    slot[0] = (g.W == 1) ? ps : ps * g.W + tree_of(C)->rk[ps][0];
+    return 1;
+  }
+  const Tree* T = tree_of(C);
+  const int nr = min(NR, (int)T->cnt[ps]);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) slot[r] = ps * g.W + T->rk[ps][r < nr ? r : 0];
+  return nr;
+}
+
+// NR: input rows per group (the nodes of a draft tree's stage; 1 for a chain
+// and the verification head; the leaves for the tree's draft head).
+template <typename WT, int EPI, bool XG = false, int NR = 1>
 __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
-  extern __shared__ float xs_lds[];  // [K] (unless XG)
+  extern __shared__ float xs_lds[];  // [NR][K] (unless XG)
   __shared__ float red[kWG / kWave];
-  __shared__ ArgPair wbest[kWG / kWave];
+  __shared__ ArgPair wbest[NR][kWG / kWave];
   constexpr int VEC = WVec<WT>::N;
   constexpr int UPW = epi_pairs(EPI) ? 2 : 4;  // units per wave
   constexpr int UPT = UPW * (kWG / kWave);     // units per tile
   const Ctrl* __restrict__ C = A.ctrl;
   const Geo& g = A.g;
+  const Tree* T = tree_of(C);
 
   int n_act, pos_base;
   if (A.gmode == GM_STAGE) {
@@ -183,10 +211,8 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
     n_act = 1;
     pos_base = 0;
   }
-  // GM_PDMLAST reads the newest draft-module row, index a + pending - 1
-  const float* xfix = (A.gmode == GM_PDMLAST) ? A.x + (size_t)(C->a + C->pending - 1) * A.x_stride : A.x;
   const int tpg = (A.units + UPT - 1) / UPT;
-  const long long T = (long long)n_act * tpg;
+  const long long Tt = (long long)n_act * tpg;
   // stage steps with few tokens in flight use a proportional share of the
   // grid (at least one workgroup per CU): the step takes about as long, and
   // the draft stream's latency-bound kernels find free CUs
@@ -194,22 +220,31 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
   if (A.gmode == GM_STAGE)
     nwg = max(min((int)gridDim.x, kStageMinWG), (int)((long long)gridDim.x * n_act / A.n_groups));
   if ((int)blockIdx.x >= nwg) return;
-  const long long t0 = T * blockIdx.x / nwg;
-  const long long t1 = T * (blockIdx.x + 1) / nwg;
+  const long long t0 = Tt * blockIdx.x / nwg;
+  const long long t1 = Tt * (blockIdx.x + 1) / nwg;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  float bv = -INFINITY;
-  int bi = 0x7FFFFFFF;
+  float bv[NR];
+  int bi[NR];
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    bv[m] = -INFINITY;
+    bi[m] = 0x7FFFFFFF;
+  }
 
-  int cur = -1, pos = 0, slot = 0;
-  const WT* W = nullptr;
-  const float* xs = xs_lds;
+  int cur = -1, pos = 0, nr = 1;
+  int slot[NR];
+  const float* xr[NR];
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    slot[m] = 0;
+    xr[m] = xs_lds;
+  }
   for (long long tile = t0; tile < t1; ++tile) {
     const int grp = (int)(tile / tpg);
     const int ut = (int)(tile - (long long)grp * tpg);
     // four rows of this wave
     int rows[4];
-    bool ok[4];
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
       const int u = ut * UPT + wave * UPW + j;
@@ -218,19 +253,17 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
       if (epi_pairs(EPI)) {
         rows[2 * j] = r0;
         rows[2 * j + 1] = r1;
-        ok[2 * j] = ok[2 * j + 1] = u < A.units;
       } else {
         rows[j] = r0;
-        ok[j] = u < A.units;
       }
     }
-    W = reinterpret_cast<const WT*>(A.W[grp]);
+    const WT* W = reinterpret_cast<const WT*>(A.W[grp]);
     const WT* p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = W + (size_t)rows[r] * A.K;
     // two k-steps per trip: the eight 16-byte weight loads are all issued
     // before the first is used; the odd last step (if any) likewise.  The
-    // first trip's loads go out before a new group's input row is staged,
+    // first trip's loads go out before a new group's input rows are staged,
     // so the staging overlaps their latency.
     constexpr int kStep = kWave * VEC;
     int k0 = lane * VEC;
@@ -248,26 +281,52 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
     if (grp != cur) {
       cur = grp;
       pos = pos_base - A.stage[grp];
-      const bool fixed = (A.gmode == GM_FIXED || A.gmode == GM_PDMLAST);
-      slot = fixed ? 0 : pos % g.nslots;
-      const float* x = fixed ? xfix : A.x + (A.x_by_slot ? slot : grp) * A.x_stride;
+      const float* xin[NR];
+      if (A.gmode == GM_STAGE) {
+        nr = stage_rows<NR>(g, C, pos, slot);
+#pragma unroll
+        for (int m = 0; m < NR; ++m) xin[m] = A.x + (A.x_by_slot ? slot[m] : grp * NR + m) * A.x_stride;
+      } else if (A.gmode == GM_EXIT) {
+        nr = 1;
+        slot[0] = (g.W == 1) ? pos % g.nslots : T->exit_slot;
+        xin[0] = A.x + slot[0] * A.x_stride;
+      } else if (A.gmode == GM_PDMLAST) {
+        // the newest draft-module rows: a chain's last row, or a tree's leaves
+        const int nrow = (g.W == 1) ? C->a + C->pending : T->nrows;
+        nr = (g.W == 1) ? 1 : min(NR, (int)T->nleaves);
+#pragma unroll
+        for (int m = 0; m < NR; ++m) xin[m] = A.x + (size_t)(nrow - nr + (m < nr ? m : 0)) * A.x_stride;
+      } else {
+        nr = 1;
+#pragma unroll
+        for (int m = 0; m < NR; ++m) xin[m] = A.x;
+      }
       if (XG) {
-        xs = x;
+#pragma unroll
+        for (int m = 0; m < NR; ++m) xr[m] = xin[m];
       } else {
         __syncthreads();
-        stage_input(x, A.gamma[grp], A.K, g.eps, red, xs_lds);
+#pragma unroll
+        for (int m = 0; m < NR; ++m)
+          if (m < nr) stage_input(xin[m], A.gamma[grp], A.K, g.eps, red, xs_lds + (size_t)m * A.K);
+#pragma unroll
+        for (int m = 0; m < NR; ++m) xr[m] = xs_lds + (size_t)m * A.K;
         __syncthreads();
       }
-      if (EPI == EPI_QKV && ut == 0 && threadIdx.x == 0 && A.kv_len) {
+      if (EPI == EPI_QKV && ut == 0 && threadIdx.x == 0 && A.kv_len && g.W == 1) {
         int* len = A.kv_len + A.layer[grp];
         if (*len != pos) atomicOr(&A.ctrl->flags, SPD_FLAG_KVLEN);
         *len = pos + 1;
       }
     }
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[NR][4];
+#pragma unroll
+    for (int m = 0; m < NR; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[m][r] = 0.f;
     if (pair0) {
-      gemv_step<WT>(ra, xs + k0, acc);
-      gemv_step<WT>(rb, xs + k0 + kStep, acc);
+      gemv_step<WT, NR>(ra, xr, k0, nr, acc);
+      gemv_step<WT, NR>(rb, xr, k0 + kStep, nr, acc);
       k0 += 2 * kStep;
       for (; k0 + kStep < A.K; k0 += 2 * kStep) {
 #pragma unroll
@@ -275,77 +334,90 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) rb[r] = WVec<WT>::ld(p[r] + k0 + kStep);
         __builtin_amdgcn_sched_barrier(0);
-        gemv_step<WT>(ra, xs + k0, acc);
-        gemv_step<WT>(rb, xs + k0 + kStep, acc);
+        gemv_step<WT, NR>(ra, xr, k0, nr, acc);
+        gemv_step<WT, NR>(rb, xr, k0 + kStep, nr, acc);
       }
       if (k0 < A.K) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) ra[r] = WVec<WT>::ld(p[r] + k0);
         __builtin_amdgcn_sched_barrier(0);
-        gemv_step<WT>(ra, xs + k0, acc);
+        gemv_step<WT, NR>(ra, xr, k0, nr, acc);
       }
     } else if (k0 < A.K) {
-      gemv_step<WT>(ra, xs + k0, acc);
+      gemv_step<WT, NR>(ra, xr, k0, nr, acc);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = wave_sum(acc[r]);
 
-    // epilogue: lane j handles unit j of the wave
-    if (lane < UPW) {
-      const int j = lane;
-      const int u = ut * UPT + wave * UPW + j;
-      if (u < A.units) {
-        if (EPI == EPI_QKV) {
-          float a = sel4(acc, 2 * j), b = sel4(acc, 2 * j + 1);
-          const int half = g.hd >> 1;
-          const int h = u / half, i = u - h * half;
-          if (h < g.Hq + g.Hkv) rope_pair(a, b, A.rcos[(size_t)pos * half + i], A.rsin[(size_t)pos * half + i]);
-          if (h < g.Hq) {
-            float* q = A.out + (size_t)grp * A.out_stride + (size_t)h * g.hd;
-            q[i] = a;
-            q[i + half] = b;
-          } else if (h < g.Hq + g.Hkv) {
-            auto* kc = reinterpret_cast<WT*>(A.kc);
-            const int kvh = h - g.Hq, ly = A.layer[grp];
-            kc[k_index(g, ly, kvh, pos, i)] = to_store<WT>(a);
-            kc[k_index(g, ly, kvh, pos, i + half)] = to_store<WT>(b);
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      if (NR > 1 && m >= nr) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[m][r] = wave_sum(acc[m][r]);
+
+      // epilogue: lane j handles unit j of the wave
+      if (lane < UPW) {
+        const int j = lane;
+        const int u = ut * UPT + wave * UPW + j;
+        if (u < A.units) {
+          if (EPI == EPI_QKV) {
+            float a = sel4(acc[m], 2 * j), b = sel4(acc[m], 2 * j + 1);
+            const int half = g.hd >> 1;
+            const int h = u / half, i = u - h * half;
+            if (h < g.Hq + g.Hkv) rope_pair(a, b, A.rcos[(size_t)pos * half + i], A.rsin[(size_t)pos * half + i]);
+            if (h < g.Hq) {
+              float* q = A.out + (size_t)(grp * NR + m) * A.out_stride + (size_t)h * g.hd;
+              q[i] = a;
+              q[i + half] = b;
+            } else {
+              // the node's key/values go to every KV lane of its descendants
+              const int lanes = (g.W == 1) ? 1 : T->lanes[slot[m]];
+              const bool isk = h < g.Hq + g.Hkv;
+              auto* cache = reinterpret_cast<WT*>(isk ? A.kc : A.vc);
+              const int kvh = isk ? h - g.Hq : h - g.Hq - g.Hkv, ly = A.layer[grp];
+              const size_t i0 = isk ? k_index(g, ly, kvh, pos, i) : v_index(g, ly, kvh, pos, i);
+              const size_t i1 = isk ? k_index(g, ly, kvh, pos, i + half) : v_index(g, ly, kvh, pos, i + half);
+              for (int ln = 0; ln < kMaxW; ++ln) {
+                if (!((lanes >> ln) & 1)) continue;
+                cache[ln * g.lane_kv + i0] = to_store<WT>(a);
+                cache[ln * g.lane_kv + i1] = to_store<WT>(b);
+              }
+            }
+          } else if (EPI == EPI_SWIGLU) {
+            A.out[(size_t)(grp * NR + m) * A.out_stride + u] = silu_mul(sel4(acc[m], 2 * j), sel4(acc[m], 2 * j + 1));
+          } else if (EPI == EPI_RESID) {
+            const int sl = slot[m];
+            float* o = A.out + (A.out_by_slot ? sl : grp * NR + m) * A.out_stride;
+            const float hn = o[u] + sel4(acc[m], j);
+            o[u] = hn;
+            const int ai = A.anchor_idx[grp];
+            if (ai >= 0) A.anchors[((size_t)sl * g.m + ai) * g.d + u] = hn;
+          } else if (EPI == EPI_ARGMAX) {
+            const float y = sel4(acc[m], j);
+            A.out[(size_t)m * A.N + u] = y;
+            if (better(y, u, bv[m], bi[m])) {
+              bv[m] = y;
+              bi[m] = u;
+            }
           } else {
-            auto* vc = reinterpret_cast<WT*>(A.vc);
-            const int kvh = h - g.Hq - g.Hkv, ly = A.layer[grp];
-            vc[v_index(g, ly, kvh, pos, i)] = to_store<WT>(a);
-            vc[v_index(g, ly, kvh, pos, i + half)] = to_store<WT>(b);
+            A.out[(size_t)(grp * NR + m) * A.out_stride + u] = sel4(acc[m], j);
           }
-        } else if (EPI == EPI_SWIGLU) {
-          A.out[(size_t)grp * A.out_stride + u] = silu_mul(sel4(acc, 2 * j), sel4(acc, 2 * j + 1));
-        } else if (EPI == EPI_RESID) {
-          float* o = A.out + (A.out_by_slot ? slot : grp) * A.out_stride;
-          const float hn = o[u] + sel4(acc, j);
-          o[u] = hn;
-          const int ai = A.anchor_idx[grp];
-          if (ai >= 0) A.anchors[((size_t)slot * g.m + ai) * g.d + u] = hn;
-        } else if (EPI == EPI_ARGMAX) {
-          const float y = sel4(acc, j);
-          A.out[u] = y;
-          if (better(y, u, bv, bi)) {
-            bv = y;
-            bi = u;
-          }
-        } else {
-          A.out[(size_t)grp * A.out_stride + u] = sel4(acc, j);
         }
       }
     }
   }
   if (EPI == EPI_ARGMAX) {
     // lanes 0..3 of each wave hold candidates; reduce in a fixed order
-    wave_argmax(bv, bi);
-    if (lane == 0) wbest[wave] = ArgPair{bv, bi};
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      wave_argmax(bv[m], bi[m]);
+      if (lane == 0) wbest[m][wave] = ArgPair{bv[m], bi[m]};
+    }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      ArgPair b = wbest[0];
+    if (threadIdx.x < NR) {
+      const int m = threadIdx.x;
+      ArgPair b = wbest[m][0];
       for (int w = 1; w < kWG / kWave; ++w)
-        if (better(wbest[w].v, wbest[w].i, b.v, b.i)) b = wbest[w];
-      A.parts[blockIdx.x] = b;
+        if (better(wbest[m][w].v, wbest[m][w].i, b.v, b.i)) b = wbest[m][w];
+      A.parts[(size_t)m * gridDim.x + blockIdx.x] = b;
     }
   }
 }
@@ -398,8 +470,10 @@ __global__ __launch_bounds__(kWG) void k_gemv_rows(const RowsGemv A) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
 
-  // rows of this pass
-  int Mtot = A.from_ctrl ? (C->a + C->pending) : A.M_arg;
+  // rows of this pass (a draft tree's rows come from its row table)
+  const bool tree = A.from_ctrl && g.W > 1;
+  const Tree* TR = tree_of(C);
+  int Mtot = tree ? TR->nrows : A.from_ctrl ? (C->a + C->pending) : A.M_arg;
   const int pos0 = A.from_ctrl ? C->C : A.pos0_arg;
   int M = Mtot - A.row_base;
   if (M > kRowsMR) M = kRowsMR;
@@ -410,8 +484,7 @@ __global__ __launch_bounds__(kWG) void k_gemv_rows(const RowsGemv A) {
       // pass `row_base / kRowsMR` takes the matching rows row_base .. row_base + kRowsMR - 1
       int cnt = 0, seen = 0;
       for (int i = 0; i < Mtot; ++i) {
-        const int p = pos0 + i;
-        const int dep = pdm_row_depth(g, C, i, p);
+        const int dep = tree ? TR->row_depth[i] : pdm_row_depth(g, C, i, pos0 + i);
         if (g.fpat[dep] == grp) {
           if (seen >= A.row_base && cnt < kRowsMR) rsrc[cnt++] = i;
           ++seen;
@@ -431,7 +504,7 @@ __global__ __launch_bounds__(kWG) void k_gemv_rows(const RowsGemv A) {
   auto in_row = [&](int r) -> const float* {
     if (A.rmode == RM_FC) {
       const int i = rsrc[r];
-      const int slot = (pos0 + i) % g.nslots;
+      const int slot = tree ? TR->row_slot[i] : (pos0 + i) % g.nslots;
       return A.slot_anchors + (size_t)slot * g.m * g.d;
     }
     return A.x + (size_t)(A.row_base + r) * A.ldx;
@@ -513,7 +586,7 @@ __global__ __launch_bounds__(kWG) void k_gemv_rows(const RowsGemv A) {
       const int u = ut * UPT + wave * UPW + j;
       if (u < A.units) {
         const int orow = (A.rmode == RM_FC) ? rsrc[m] : (A.row_base + m);
-        const int pos = pos0 + orow;
+        const int pos = tree ? TR->row_pos[orow] : pos0 + orow;
         if (EPI == EPI_QKV) {
           float a = sel4(v, 2 * j), b = sel4(v, 2 * j + 1);
           const int h = u / half, i = u - h * half;
@@ -522,16 +595,19 @@ __global__ __launch_bounds__(kWG) void k_gemv_rows(const RowsGemv A) {
             float* q = A.out + (size_t)orow * A.ldo + (size_t)h * g.hd;
             q[i] = a;
             q[i + half] = b;
-          } else if (h < g.Hq + g.Hkv) {
-            auto* kc = reinterpret_cast<WT*>(A.kc);
-            const int kvh = h - g.Hq;
-            kc[k_index(g, A.layer, kvh, pos, i)] = to_store<WT>(a);
-            kc[k_index(g, A.layer, kvh, pos, i + half)] = to_store<WT>(b);
           } else {
-            auto* vc = reinterpret_cast<WT*>(A.vc);
-            const int kvh = h - g.Hq - g.Hkv;
-            vc[v_index(g, A.layer, kvh, pos, i)] = to_store<WT>(a);
-            vc[v_index(g, A.layer, kvh, pos, i + half)] = to_store<WT>(b);
+            // a draft tree's row writes its key/values to every lane of its descendants
+            const int lanes = tree ? TR->row_lanes[orow] : 1;
+            const bool isk = h < g.Hq + g.Hkv;
+            auto* cache = reinterpret_cast<WT*>(isk ? A.kc : A.vc);
+            const int kvh = isk ? h - g.Hq : h - g.Hq - g.Hkv;
+            const size_t i0 = isk ? k_index(g, A.layer, kvh, pos, i) : v_index(g, A.layer, kvh, pos, i);
+            const size_t i1 = isk ? k_index(g, A.layer, kvh, pos, i + half) : v_index(g, A.layer, kvh, pos, i + half);
+            for (int ln = 0; ln < kMaxW; ++ln) {
+              if (!((lanes >> ln) & 1)) continue;
+              cache[ln * g.lane_pkv + i0] = to_store<WT>(a);
+              cache[ln * g.lane_pkv + i1] = to_store<WT>(b);
+            }
           }
         } else if (EPI == EPI_SWIGLU) {
           A.out[(size_t)orow * A.ldo + u] = silu_mul(sel4(v, 2 * j), sel4(v, 2 * j + 1));

@@ -104,15 +104,15 @@ __device__ __forceinline__ void mfma_select_rows(const MfmaArgs& A, int prob, in
                                                  int* rsrc) {
   if (threadIdx.x == 0) {
     const Ctrl* C = A.ctrl;
-    const int Mtot = A.from_ctrl ? (C->a + C->pending) : A.M_arg;
+    const Geo& g = A.g;
+    const bool tree = A.from_ctrl && g.W > 1;
+    const int Mtot = tree ? tree_of(C)->nrows : A.from_ctrl ? (C->a + C->pending) : A.M_arg;
     const int pos0 = A.from_ctrl ? C->C : A.pos0_arg;
     int M;
     if (A.rmode == RM_FC) {
-      const Geo& g = A.g;
       M = 0;
       for (int i = 0; i < Mtot; ++i) {
-        const int p = pos0 + i;
-        const int dep = pdm_row_depth(g, C, i, p);
+        const int dep = tree ? tree_of(C)->row_depth[i] : pdm_row_depth(g, C, i, pos0 + i);
         if (g.fpat[dep] == prob && M < cap) rsrc[M++] = i;
       }
     } else {
@@ -126,10 +126,15 @@ __device__ __forceinline__ void mfma_select_rows(const MfmaArgs& A, int prob, in
 
 __device__ __forceinline__ const float* mfma_in_row(const MfmaArgs& A, int orow, int pos0) {
   if (A.rmode == RM_FC) {
-    const int slot = (pos0 + orow) % A.g.nslots;
+    const int slot = (A.g.W > 1) ? tree_of(A.ctrl)->row_slot[orow] : (pos0 + orow) % A.g.nslots;
     return A.slot_anchors + (size_t)slot * A.g.m * A.g.d;
   }
   return A.x + (size_t)orow * A.ldx;
+}
+
+// Position of activation row orow (a draft tree's rows carry their own).
+__device__ __forceinline__ int mfma_row_pos(const MfmaArgs& A, int orow, int pos0) {
+  return (A.from_ctrl && A.g.W > 1) ? tree_of(A.ctrl)->row_pos[orow] : pos0 + orow;
 }
 
 // Epilogue of activation row m of one row group, run by one wave: lane c
@@ -151,22 +156,25 @@ __device__ __forceinline__ void mfma_epilogue_row(const MfmaArgs& A, int rg, int
     if (EPI == EPI_QKV) {
       const int half = g.hd >> 1;
       const int h = u / half, i = u - h * half;
-      const int pos = pos0 + orow;
+      const int pos = mfma_row_pos(A, orow, pos0);
       if (h < g.Hq + g.Hkv) rope_pair(a, b, A.rcos[(size_t)pos * half + i], A.rsin[(size_t)pos * half + i]);
       if (h < g.Hq) {
         float* q = A.out + (size_t)orow * A.ldo + (size_t)h * g.hd;
         q[i] = a;
         q[i + half] = b;
-      } else if (h < g.Hq + g.Hkv) {
-        uint16_t* kc = reinterpret_cast<uint16_t*>(A.kc);
-        const int kvh = h - g.Hq;
-        kc[k_index(g, A.layer, kvh, pos, i)] = f32_to_bf16_rne(a);
-        kc[k_index(g, A.layer, kvh, pos, i + half)] = f32_to_bf16_rne(b);
       } else {
-        uint16_t* vc = reinterpret_cast<uint16_t*>(A.vc);
-        const int kvh = h - g.Hq - g.Hkv;
-        vc[v_index(g, A.layer, kvh, pos, i)] = f32_to_bf16_rne(a);
-        vc[v_index(g, A.layer, kvh, pos, i + half)] = f32_to_bf16_rne(b);
+        // a draft tree's row writes its key/values to every lane of its descendants
+        const int lanes = (A.from_ctrl && g.W > 1) ? tree_of(A.ctrl)->row_lanes[orow] : 1;
+        const bool isk = h < g.Hq + g.Hkv;
+        uint16_t* cache = reinterpret_cast<uint16_t*>(isk ? A.kc : A.vc);
+        const int kvh = isk ? h - g.Hq : h - g.Hq - g.Hkv;
+        const size_t i0 = isk ? k_index(g, A.layer, kvh, pos, i) : v_index(g, A.layer, kvh, pos, i);
+        const size_t i1 = isk ? k_index(g, A.layer, kvh, pos, i + half) : v_index(g, A.layer, kvh, pos, i + half);
+        for (int ln = 0; ln < kMaxW; ++ln) {
+          if (!((lanes >> ln) & 1)) continue;
+          cache[ln * g.lane_pkv + i0] = f32_to_bf16_rne(a);
+          cache[ln * g.lane_pkv + i1] = f32_to_bf16_rne(b);
+        }
       }
     } else {
       A.out[(size_t)orow * A.ldo + u] = silu_mul(a, b);
@@ -286,7 +294,7 @@ __global__ __launch_bounds__(kWG) void k_mfma_gemv(const MfmaArgs A) {
         // the same arithmetic, in split order, as the split-merge kernel
         const Geo& g = A.g;
         const int orow = rsrc[m];
-        const int ns = (pos0 + orow) / kSplit + 1;
+        const int ns = mfma_row_pos(A, orow, pos0) / kSplit + 1;
         const int head = k / g.hd, d0 = k - head * g.hd;
         const size_t base = ((size_t)orow * g.Hq + head) * g.nsplit;
         float M = -INFINITY;

@@ -1,0 +1,639 @@
+// Draft trees in the SPD cycle: control kernels (gfx950).
+//
+// [RB] prerequisites ("draft tree": the draft module proposes several branch
+// candidates, keeping the top-W branches by cumulative probability) and [PL]
+// appendix B (each SPD draft step widened into a width-4 tree).  Reading:
+// the tokens in flight form a tree with at most W nodes per position and one
+// at the oldest; each cycle the draft module scores the pairs (leaf, token)
+// among every leaf's W most likely tokens by cum(leaf) + log Q_leaf(token)
+// (cum: log Q summed over the leaf's path above the oldest position), the
+// next cycle enters the best W whose leaf survived verification, the exiting
+// node keeps its child that matches the target's argmax and prunes the rest,
+// and the three-step rollback runs only when no child matches.
+//
+// Per-branch KV ([PL] §4 and [RB] limitations name branched KV caches as
+// what a wall-clock tree needs): the target and draft caches hold W lanes
+// (full copies).  A node's key/values go to the lanes of all its descendant
+// leaves and it reads any one of them, so it attends to committed prefix +
+// ancestors + itself with the arithmetic of the single chain.  A leaf that
+// inherits its parent's lane needs nothing; a second child gets a free lane
+// and a copy of the parent's in-flight window; an exiting node's key/values
+// are broadcast to every lane (everything up to the last exit is common).
+#pragma once
+
+#include "common.h"
+#include "control.h"
+
+namespace spd {
+
+// ---- entry (A0/A1 for a tree) --------------------------------------------
+template <typename WT>
+__global__ __launch_bounds__(kWG) void k_tree_entry(Ctrl* C, const Geo g, int32_t* tokens, const WT* embed,
+                                                    float* hslots, float* anchors, spd_cycle_rec* ring,
+                                                    int log_cap) {
+  __shared__ int s_n, s_slot[kMaxW], s_tok[kMaxW];
+  Tree* T = tree_of(C);
+  const int W = g.W, ns = g.nslots;
+  if (threadIdx.x == 0) {
+    const int cyc = C->launches;
+    C->launches = cyc + 1;
+    C->rec_slot = cyc % log_cap;
+    spd_cycle_rec* r = ring + C->rec_slot;
+    r->cycle = cyc;
+    r->pdm_argmax = r->draft = r->exit_pos = r->target_token = -1;
+    r->accepted = -1;
+    r->accepted_rank = -1;
+    r->nodes = 0;
+    r->n_new = 0;
+    for (int k = 0; k < SPD_MAX_WIDTH; ++k) r->new_parent[k] = r->new_token[k] = -1;
+    s_n = 0;
+    T->ncopy = 0;
+    if (C->done) {
+      C->active = 0;
+      r->t = -1;
+      r->occupancy = 0;
+      r->pending_row = 0;
+      r->pdm_len = C->C;
+      r->emitted = C->emitted;
+      r->flags = SPD_FLAG_IDLE;
+    } else {
+      int pos, a, n_new = 0;
+      int par[kMaxW], tk[kMaxW], prank[kMaxW];
+      double lq[kMaxW];
+      const bool reseed = C->reseed != 0;
+      if (reseed) {
+        pos = C->seed_pos;
+        a = 1;
+        n_new = 1;
+        par[0] = -1;
+        tk[0] = C->seed_tok;
+        lq[0] = 0.0;
+        prank[0] = -1;
+        C->reseed = 0;
+        for (int ps = 0; ps < ns; ++ps) T->cnt[ps] = 0;
+      } else {
+        pos = C->t + 1;
+        a = C->a - (C->r_exit >= 0 ? 1 : 0) + 1;
+        // the first W candidates whose leaf survived this cycle's verification
+        const int lps = C->t % ns, nl = T->cnt[lps];
+        for (int c = 0; c < T->ncand && n_new < W; ++c) {
+          const int leaf = T->cand_leaf[c];
+          int lr = -1;
+          for (int q = 0; q < nl; ++q)
+            if (lps * W + T->rk[lps][q] == leaf) lr = q;
+          if (lr < 0) continue;
+          par[n_new] = leaf;
+          tk[n_new] = T->cand_tok[c];
+          lq[n_new] = T->cand_lq[c];
+          prank[n_new] = lr;
+          ++n_new;
+        }
+      }
+      uint32_t fl = 0;
+      if (a < 1 || a > g.n) fl |= SPD_FLAG_OCCUPANCY;
+      if (pos + 1 >= g.max_ctx) fl |= SPD_FLAG_CTX;
+      if (n_new < 1) fl |= SPD_FLAG_NODRAFT;
+      C->flags |= fl;
+      r->t = pos;
+      r->occupancy = a;
+      r->flags = fl;
+      if (fl) {
+        C->active = 0;
+        C->done = 1;
+        r->pending_row = 0;
+      } else {
+        const int oldest = pos - a + 1;
+        const int pps = pos % ns;
+        T->cnt[pps] = n_new;
+        for (int k = 0; k < n_new; ++k) {
+          T->rk[pps][k] = k;
+          const int sl = pps * W + k;
+          T->tok[sl] = tk[k];
+          T->parent[sl] = par[k];
+          T->logq[sl] = lq[k];
+        }
+        // branches that got no child are dead: keep the new nodes' ancestors
+        int live[SPD_MAX_STAGES + 1];
+        for (int ps = 0; ps < ns; ++ps) live[ps] = 0;
+        for (int k = 0; k < n_new; ++k) {
+          int x = par[k];
+          for (int p = pos - 1; p >= oldest && x >= 0; --p) {
+            live[p % ns] |= 1 << (x % W);
+            if (p > oldest) x = T->parent[x];
+          }
+        }
+        for (int p = oldest; p < pos; ++p) {
+          const int ps = p % ns;
+          int c2 = 0;
+          for (int q = 0; q < T->cnt[ps]; ++q) {
+            const int ph = T->rk[ps][q];
+            if ((live[ps] >> ph) & 1) T->rk[ps][c2++] = ph;
+          }
+          T->cnt[ps] = c2;
+        }
+        // lanes: the first child of a leaf inherits its lane, the others take
+        // free lanes and a copy of the parent's in-flight window
+        int nlane[kMaxW];
+        int taken = 0;
+        if (reseed) {
+          nlane[0] = 0;
+          taken = 1;
+        } else {
+          for (int k = 0; k < n_new; ++k) {
+            bool first = true;
+            for (int k2 = 0; k2 < k; ++k2)
+              if (par[k2] == par[k]) first = false;
+            const int pl = T->lane[par[k]];
+            if (first && !((taken >> pl) & 1)) {
+              nlane[k] = pl;
+              taken |= 1 << pl;
+            } else {
+              nlane[k] = -1;
+            }
+          }
+          for (int k = 0; k < n_new; ++k) {
+            if (nlane[k] >= 0) continue;
+            int fr = 0;
+            while ((taken >> fr) & 1) ++fr;
+            nlane[k] = fr;
+            taken |= 1 << fr;
+            T->copy_src[T->ncopy] = T->lane[par[k]];
+            T->copy_dst[T->ncopy] = fr;
+            T->ncopy += 1;
+          }
+          T->copy_lo = oldest;
+          T->copy_hi = pos - 1;
+        }
+        // lane masks: every live node writes to the lanes of its descendant leaves
+        for (int p = oldest; p < pos; ++p) {
+          const int ps = p % ns;
+          for (int q = 0; q < T->cnt[ps]; ++q) T->lanes[ps * W + T->rk[ps][q]] = 0;
+        }
+        for (int k = 0; k < n_new; ++k) {
+          const int sl = pps * W + k;
+          T->lanes[sl] = 1 << nlane[k];
+          T->lane[sl] = nlane[k];
+          int x = par[k];
+          for (int p = pos - 1; p >= oldest && x >= 0; --p) {
+            T->lanes[x] |= 1 << nlane[k];
+            if (p > oldest) x = T->parent[x];
+          }
+        }
+        int nodes = n_new;
+        for (int p = oldest; p < pos; ++p) {
+          const int ps = p % ns;
+          nodes += T->cnt[ps];
+          for (int q = 0; q < T->cnt[ps]; ++q) {
+            const int sl = ps * W + T->rk[ps][q];
+            T->lane[sl] = __ffs(T->lanes[sl]) - 1;
+          }
+        }
+        T->exit_slot = (oldest % ns) * W + T->rk[oldest % ns][0];
+        // draft-module rows: the committed-next row (every lane), then the
+        // nodes by position and rank
+        int nr = 0;
+        if (C->pend_next) {
+          T->row_slot[nr] = T->last_exit;
+          T->row_pos[nr] = C->C;
+          T->row_depth[nr] = g.n;
+          T->row_lanes[nr] = (1 << W) - 1;
+          T->row_lane[nr] = 0;
+          ++nr;
+        }
+        for (int p = oldest; p <= pos; ++p) {
+          const int ps = p % ns;
+          for (int q = 0; q < T->cnt[ps]; ++q) {
+            if (nr >= kMaxTreeRows) break;  // cannot happen: 2 + (n - 1) W <= kMaxTreeRows
+            const int sl = ps * W + T->rk[ps][q];
+            T->row_slot[nr] = sl;
+            T->row_pos[nr] = p;
+            T->row_depth[nr] = pos - p;
+            T->row_lanes[nr] = T->lanes[sl];
+            T->row_lane[nr] = T->lane[sl];
+            ++nr;
+          }
+        }
+        T->nrows = nr;
+        T->nleaves = n_new;
+        T->pend_slot = C->pend_next ? T->last_exit : -1;
+        C->pending = C->pend_next;
+        C->t = pos;
+        C->a = a;
+        C->cycle += 1;
+        C->active = 1;
+        tokens[pos] = tk[0];
+        r->pending_row = C->pending;
+        r->nodes = nodes;
+        r->n_new = n_new;
+        for (int k = 0; k < n_new; ++k) {
+          r->new_parent[k] = prank[k];
+          r->new_token[k] = tk[k];
+          s_slot[k] = pps * W + k;
+          s_tok[k] = tk[k];
+        }
+        s_n = n_new;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    spd_cycle_rec* r = ring + C->rec_slot;
+    for (int l = threadIdx.x; l < SPD_MAX_LAYERS; l += kWG) r->kv_len[l] = 0;
+  }
+  for (int k = 0; k < s_n; ++k) {
+    const WT* e = embed + (size_t)s_tok[k] * g.d;
+    for (int i = threadIdx.x; i < g.d; i += kWG) {
+      const float v = from_store(e[i]);
+      hslots[(size_t)s_slot[k] * g.d + i] = v;
+      anchors[((size_t)s_slot[k] * g.m + 0) * g.d + i] = v;
+    }
+  }
+}
+
+// ---- lane copies asked for by the entry: grid (layers, W) ----------------
+template <typename WT>
+__global__ __launch_bounds__(kWG) void k_tree_lane_copy(const Ctrl* C, const Geo g, WT* kc, WT* vc) {
+  const Tree* T = tree_of(C);
+  if (!C->active || (int)blockIdx.y >= T->ncopy) return;
+  const int layer = blockIdx.x;
+  const long long src = T->copy_src[blockIdx.y] * g.lane_kv, dst = T->copy_dst[blockIdx.y] * g.lane_kv;
+  const int lo = T->copy_lo, np = T->copy_hi - T->copy_lo + 1;
+  if (np <= 0) return;
+  const int n = g.Hkv * g.hd * np;
+  for (int idx = threadIdx.x; idx < n; idx += kWG) {
+    const int p = lo + idx % np, rest = idx / np;
+    const int dim = rest % g.hd, kvh = rest / g.hd;
+    const size_t ik = k_index(g, layer, kvh, p, dim), iv = v_index(g, layer, kvh, p, dim);
+    kc[dst + ik] = kc[src + ik];
+    vc[dst + iv] = vc[src + iv];
+  }
+}
+
+// ---- verification of the exiting node's children + rollback (A5/A6) ------
+struct TreeVerifyArgs {
+  const ArgPair* parts;
+  int nparts;
+  int32_t* tokens;
+  int32_t* kv_len;
+  void* kc;
+  void* vc;
+  int kv_bytes;  // bytes per KV element
+  spd_cycle_rec* ring;
+  Ctrl* ctrl;
+  Geo g;
+};
+
+__global__ __launch_bounds__(kCtlThreads) void k_tree_verify(const TreeVerifyArgs A) {
+  __shared__ ArgPair sh_ap[kCtlThreads / kWave];
+  Ctrl* C = A.ctrl;
+  Tree* T = tree_of(C);
+  const Geo& g = A.g;
+  const int W = g.W, ns = g.nslots;
+  if (!C->active) return;
+  spd_cycle_rec* rec = A.ring + C->rec_slot;
+  if (C->a != g.n) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      C->r_exit = -1;
+      C->r_accept = -1;
+      C->pend_next = 0;
+      rec->emitted = C->emitted;
+      rec->flags |= C->flags;
+    }
+    for (int l = threadIdx.x; l < g.L; l += kCtlThreads) rec->kv_len[l] = A.kv_len[l];
+    return;
+  }
+  const int j = C->t - (g.n - 1);
+  const int ex = T->exit_slot;
+  const ArgPair best = block_argmax_parts(A.parts, A.nparts, sh_ap);
+  // the exiting node's key/values join every lane (its position is verified)
+  {
+    const int src = T->lane[ex];
+    const int n = g.L * g.Hkv * g.hd;
+    for (int idx = threadIdx.x; idx < n; idx += kCtlThreads) {
+      const int dim = idx % g.hd, rest = idx / g.hd;
+      const int kvh = rest % g.Hkv, layer = rest / g.Hkv;
+      const size_t ik = k_index(g, layer, kvh, j, dim), iv = v_index(g, layer, kvh, j, dim);
+      for (int ln = 0; ln < W; ++ln) {
+        if (ln == src) continue;
+        if (A.kv_bytes == 2) {
+          uint16_t* kc = reinterpret_cast<uint16_t*>(A.kc);
+          uint16_t* vc = reinterpret_cast<uint16_t*>(A.vc);
+          kc[ln * g.lane_kv + ik] = kc[src * g.lane_kv + ik];
+          vc[ln * g.lane_kv + iv] = vc[src * g.lane_kv + iv];
+        } else {
+          float* kc = reinterpret_cast<float*>(A.kc);
+          float* vc = reinterpret_cast<float*>(A.vc);
+          kc[ln * g.lane_kv + ik] = kc[src * g.lane_kv + ik];
+          vc[ln * g.lane_kv + iv] = vc[src * g.lane_kv + iv];
+        }
+      }
+    }
+  }
+  for (int l = threadIdx.x; l < g.L; l += kCtlThreads) A.kv_len[l] = j + 1;  // committed (and (i) on reject)
+  if (threadIdx.x == 0) {
+    const int y = valid_token(best.i, g.V, &C->flags);
+    const int ps1 = (j + 1) % ns;
+    int acc_rank = -1;
+    for (int q = 0; q < T->cnt[ps1]; ++q)
+      if (T->tok[ps1 * W + T->rk[ps1][q]] == y) {
+        acc_rank = q;
+        break;
+      }
+    if (acc_rank >= 0) {
+      // only the kept child's subtree stays
+      const int keep = ps1 * W + T->rk[ps1][acc_rank];
+      for (int p = j + 1; p <= C->t; ++p) {
+        const int ps = p % ns;
+        int c2 = 0;
+        for (int q = 0; q < T->cnt[ps]; ++q) {
+          const int sl = ps * W + T->rk[ps][q];
+          int x = sl;
+          for (int pp = p; pp > j + 1; --pp) x = T->parent[x];
+          if (x == keep) T->rk[ps][c2++] = T->rk[ps][q];
+        }
+        T->cnt[ps] = c2;
+      }
+    } else {
+      // (ii) flush the tree and (iii) re-seed stage 0
+      for (int ps = 0; ps < ns; ++ps) T->cnt[ps] = 0;
+      T->ncand = 0;
+      C->reseed = 1;
+      C->seed_tok = y;
+      C->seed_pos = j + 1;
+    }
+    const int acc = acc_rank >= 0 ? 1 : 0;
+    A.tokens[j + 1] = y;
+    C->emitted += 1;
+    C->done = (C->emitted >= g.max_new);
+    C->r_exit = j;
+    C->r_y = y;
+    C->r_accept = acc;
+    C->pend_next = 1;
+    T->last_exit = ex;
+    rec->exit_pos = j;
+    rec->target_token = y;
+    rec->accepted = acc;
+    rec->accepted_rank = acc_rank;
+    rec->emitted = C->emitted;
+    rec->flags |= C->flags;
+  }
+  __syncthreads();
+  for (int l = threadIdx.x; l < g.L; l += kCtlThreads) rec->kv_len[l] = A.kv_len[l];
+}
+
+// ---- draft step of a tree: per leaf, the softmax normaliser and the W most
+// likely tokens; then candidates, ranking and the forced policy -----------
+constexpr int kTreeScanIds = 16;  // ids per thread of k_tree_scan
+constexpr int kTreeScanBlk = kWG * kTreeScanIds;
+
+__host__ __device__ constexpr int tree_scan_blocks(int V) { return (V + kTreeScanBlk - 1) / kTreeScanBlk; }
+
+struct TreeScanArgs {
+  const float* logits;    // [W][V] draft logits of the leaves
+  const ArgPair* parts;   // [W][nparts] per-workgroup argmax of each leaf's logits
+  int nparts;
+  double* zpart;          // [W][nblk] partial sums of exp(l - max)
+  ArgPair* tpart;         // [W][nblk][W] partial top-W (value, id)
+  const Ctrl* ctrl;
+  Geo g;
+};
+
+__device__ __forceinline__ float parts_max(const ArgPair* p, int n) {
+  float m = -INFINITY;
+  for (int k = 0; k < n; ++k) m = fmaxf(m, p[k].v);
+  return m;
+}
+
+// grid (blocks, W): block b of leaf m takes ids [b * kTreeScanBlk, ...)
+__global__ __launch_bounds__(kWG) void k_tree_scan(const TreeScanArgs A) {
+  __shared__ double sz[kWG / kWave];
+  __shared__ ArgPair sh[kWG / kWave];
+  __shared__ float s_max;
+  const Ctrl* C = A.ctrl;
+  const Geo& g = A.g;
+  const int m = blockIdx.y, W = g.W;
+  if (!C->active || m >= tree_of(C)->nleaves) return;
+  const float* l = A.logits + (size_t)m * g.V;
+  if (threadIdx.x == 0) s_max = parts_max(A.parts + (size_t)m * A.nparts, A.nparts);
+  __syncthreads();
+  const double M = s_max;
+  // each thread: its ids' exp sum (fp64) and its own best W (value desc, id asc)
+  float tv[kMaxW];
+  int ti[kMaxW];
+  for (int k = 0; k < kMaxW; ++k) {
+    tv[k] = -INFINITY;
+    ti[k] = 0x7FFFFFFF;
+  }
+  double z = 0.0;
+  const int base = blockIdx.x * kTreeScanBlk;
+  for (int e = 0; e < kTreeScanIds; ++e) {
+    const int v = base + e * kWG + threadIdx.x;
+    if (v >= g.V) break;
+    const float x = l[v];
+    z += exp((double)x - M);
+    if (better(x, v, tv[W - 1], ti[W - 1])) {
+      int k = W - 1;
+      while (k > 0 && better(x, v, tv[k - 1], ti[k - 1])) {
+        tv[k] = tv[k - 1];
+        ti[k] = ti[k - 1];
+        --k;
+      }
+      tv[k] = x;
+      ti[k] = v;
+    }
+  }
+  // block sums in a fixed order
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  double zw = wave_sum_d(z);
+  if (lane == 0) sz[wave] = zw;
+  // block top-W: W rounds of a block argmax over each thread's next candidate
+  int head = 0;
+  for (int k = 0; k < W; ++k) {
+    float v = head < W ? tv[head] : -INFINITY;
+    int i = head < W ? ti[head] : 0x7FFFFFFF;
+    float bv = v;
+    int bi = i;
+    wave_argmax(bv, bi);
+    __syncthreads();
+    if (lane == 0) sh[wave] = ArgPair{bv, bi};
+    __syncthreads();
+    ArgPair b = sh[0];
+    for (int w = 1; w < kWG / kWave; ++w)
+      if (better(sh[w].v, sh[w].i, b.v, b.i)) b = sh[w];
+    if (head < W && i == b.i && v == b.v) ++head;  // ids are unique: only the owner advances
+    if (threadIdx.x == 0) A.tpart[((size_t)m * gridDim.x + blockIdx.x) * W + k] = b;
+  }
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+    for (int w = 0; w < kWG / kWave; ++w) s += sz[w];
+    A.zpart[(size_t)m * gridDim.x + blockIdx.x] = s;
+  }
+}
+
+struct TreeFinalizeArgs {
+  const float* logits;    // [W][V]
+  const ArgPair* parts;   // [W][nparts]
+  int nparts;
+  const double* zpart;
+  const ArgPair* tpart;
+  int nblk;
+  const float* uni;
+  int policy;             // SPD_DRAFT_NATURAL / SPD_DRAFT_FORCED (tree policy)
+  float p_first, p_tree;
+  const int32_t* ref;
+  int ref_len;
+  spd_cycle_rec* ring;
+  Ctrl* ctrl;
+  Geo g;
+};
+
+__global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs A) {
+  Ctrl* C = A.ctrl;
+  Tree* T = tree_of(C);
+  const Geo& g = A.g;
+  const int W = g.W, ns = g.nslots;
+  if (!C->active || threadIdx.x != 0) return;
+  const int t = C->t, oldest = t - C->a + 1, nl = T->nleaves;
+  // per leaf: max, log normaliser, path score, best W tokens
+  int cl[kMaxCand], ct[kMaxCand], crank[kMaxCand];
+  double cs[kMaxCand], clq[kMaxCand];
+  int nc = 0;
+  double lM[kMaxW], lZ[kMaxW], cum[kMaxW];
+  int lslot[kMaxW], top0 = -1;
+  for (int m = 0; m < nl; ++m) {
+    const ArgPair* pp = A.parts + (size_t)m * A.nparts;
+    lM[m] = parts_max(pp, A.nparts);
+    double Z = 0.0;
+    for (int b = 0; b < A.nblk; ++b) Z += A.zpart[(size_t)m * A.nblk + b];
+    lZ[m] = log(Z);
+    const int sl = T->row_slot[T->nrows - nl + m];
+    lslot[m] = sl;
+    // cum: log Q over the path above the oldest position, in position order
+    double lqs[SPD_MAX_STAGES + 1];
+    int np = 0, x = sl;
+    for (int p = t; p > oldest; --p) {
+      lqs[np++] = T->logq[x];
+      x = T->parent[x];
+    }
+    double s = 0.0;
+    for (int k = np - 1; k >= 0; --k) s += lqs[k];
+    cum[m] = s;
+    // merge the blocks' top-W lists
+    float bv[kMaxW];
+    int bi[kMaxW];
+    for (int k = 0; k < W; ++k) {
+      bv[k] = -INFINITY;
+      bi[k] = 0x7FFFFFFF;
+    }
+    for (int b = 0; b < A.nblk; ++b)
+      for (int k = 0; k < W; ++k) {
+        const ArgPair c = A.tpart[((size_t)m * A.nblk + b) * W + k];
+        if (!better(c.v, c.i, bv[W - 1], bi[W - 1])) continue;
+        int q = W - 1;
+        while (q > 0 && better(c.v, c.i, bv[q - 1], bi[q - 1])) {
+          bv[q] = bv[q - 1];
+          bi[q] = bi[q - 1];
+          --q;
+        }
+        bv[q] = c.v;
+        bi[q] = c.i;
+      }
+    if (m == 0) top0 = bi[0];
+    for (int k = 0; k < W; ++k) {
+      const double lq = (double)bv[k] - lM[m] - lZ[m];
+      cl[nc] = sl;
+      ct[nc] = bi[k];
+      crank[nc] = m;
+      clq[nc] = lq;
+      cs[nc] = cum[m] + lq;
+      ++nc;
+    }
+  }
+  // rank: score desc, then leaf rank, then token id (insertion sort, <= 16)
+  for (int i = 1; i < nc; ++i) {
+    int k = i;
+    while (k > 0 && (cs[k] > cs[k - 1] || (cs[k] == cs[k - 1] && (crank[k] < crank[k - 1] ||
+                                                                   (crank[k] == crank[k - 1] && ct[k] < ct[k - 1]))))) {
+      int ti;
+      double td;
+      ti = cl[k]; cl[k] = cl[k - 1]; cl[k - 1] = ti;
+      ti = ct[k]; ct[k] = ct[k - 1]; ct[k - 1] = ti;
+      ti = crank[k]; crank[k] = crank[k - 1]; crank[k - 1] = ti;
+      td = cs[k]; cs[k] = cs[k - 1]; cs[k - 1] = td;
+      td = clq[k]; clq[k] = clq[k - 1]; clq[k - 1] = td;
+      --k;
+    }
+  }
+  // forced policy (harness device): the pair (forced leaf, ref[q])
+  const int q = t + 1;
+  if (A.policy == SPD_DRAFT_FORCED && q < A.ref_len) {
+    int star = 0;
+    for (int m = 0; m < nl; ++m) {
+      bool on = true;
+      int x = lslot[m];
+      for (int p = t; p >= oldest; --p) {
+        if (T->tok[x] != A.ref[p]) on = false;
+        if (p > oldest) x = T->parent[x];
+      }
+      if (on) {
+        star = m;
+        break;
+      }
+    }
+    const int R = A.ref[q];
+    const float u = A.uni[(size_t)q * SPD_U_COUNT + SPD_U_FORCE];
+    const float* ls = A.logits + (size_t)star * g.V;
+    int at = -1;
+    for (int i = 0; i < nc; ++i)
+      if (crank[i] == star && ct[i] == R) at = i;
+    if (u < A.p_first || (u < A.p_tree && W >= 2)) {
+      if (at >= 0) {
+        for (int i = at; i + 1 < nc; ++i) {
+          cl[i] = cl[i + 1]; ct[i] = ct[i + 1]; crank[i] = crank[i + 1]; cs[i] = cs[i + 1]; clq[i] = clq[i + 1];
+        }
+        --nc;
+      }
+      const int ins = (u < A.p_first) ? 0 : min(W - 1, nc);
+      for (int i = nc; i > ins; --i) {
+        cl[i] = cl[i - 1]; ct[i] = ct[i - 1]; crank[i] = crank[i - 1]; cs[i] = cs[i - 1]; clq[i] = clq[i - 1];
+      }
+      const double lq = (double)ls[R] - lM[star] - lZ[star];
+      cl[ins] = lslot[star];
+      ct[ins] = R;
+      crank[ins] = star;
+      clq[ins] = lq;
+      cs[ins] = cum[star] + lq;
+      ++nc;
+    } else if (at >= 0) {
+      int x = (R + 1) % g.V;
+      for (;;) {
+        bool used = false;
+        for (int i = 0; i < nc; ++i)
+          if (crank[i] == star && ct[i] == x) used = true;
+        if (!used) break;
+        x = (x + 1) % g.V;
+      }
+      const double lq = (double)ls[x] - lM[star] - lZ[star];
+      ct[at] = x;
+      clq[at] = lq;
+      cs[at] = cum[star] + lq;
+    }
+  }
+  T->ncand = nc;
+  for (int i = 0; i < nc; ++i) {
+    T->cand_leaf[i] = cl[i];
+    T->cand_tok[i] = ct[i];
+    T->cand_lq[i] = clq[i];
+  }
+  C->r_draft = ct[0];
+  C->r_raw = top0;
+  C->C += C->pending;  // the just-verified row's key/values stay cached
+  spd_cycle_rec* rec = A.ring + C->rec_slot;
+  rec->pdm_argmax = top0;
+  rec->draft = ct[0];
+  rec->pdm_len = C->C;
+  (void)ns;
+}
+
+}  // namespace spd

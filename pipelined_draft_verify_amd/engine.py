@@ -18,6 +18,8 @@ REC_DTYPE = np.dtype([
     ("pdm_argmax", "<i4"), ("draft", "<i4"), ("exit_pos", "<i4"), ("target_token", "<i4"),
     ("accepted", "<i4"), ("pdm_len", "<i4"), ("emitted", "<i4"), ("flags", "<u4"),
     ("kv_len", "<i4", (A.SPD_MAX_LAYERS,)),
+    ("nodes", "<i4"), ("n_new", "<i4"), ("new_parent", "<i4", (A.SPD_MAX_WIDTH,)),
+    ("new_token", "<i4", (A.SPD_MAX_WIDTH,)), ("accepted_rank", "<i4"),
 ])
 assert REC_DTYPE.itemsize == ctypes.sizeof(A.spd_cycle_rec)
 
@@ -39,6 +41,7 @@ def make_config(w, max_ctx: Optional[int] = None) -> A.spd_config:
     c.attn_period = getattr(w, "attn_period", 0)
     for k, n_k in enumerate(getattr(w, "split", ()) or ()):
         c.stage_layers[k] = n_k
+    c.draft_width = getattr(w, "width", 1)
     return c
 
 
@@ -113,6 +116,12 @@ class SPDEngine:
         self.sync(raise_on_error=False)  # enqueued cycles may still read the old reference
         self.ref = t
         A.spd_set_draft_policy(self.h, A.SPD_DRAFT_FORCED, float(p_accept), t.data_ptr(), t.numel())
+
+    def set_tree_forced(self, ref_tokens, p_first: float, p_tree: float) -> None:
+        t = self.torch.tensor(np.asarray(ref_tokens, dtype=np.int32), device=self.device)
+        self.sync(raise_on_error=False)  # enqueued cycles may still read the old reference
+        self.ref = t
+        A.spd_set_tree_policy(self.h, float(p_first), float(p_tree), t.data_ptr(), t.numel())
 
     def set_launch_mode(self, graph: bool, serialized: bool = False) -> None:
         mode = A.SPD_LAUNCH_GRAPH if graph else A.SPD_LAUNCH_EAGER

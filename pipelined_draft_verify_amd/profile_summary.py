@@ -10,11 +10,16 @@ end (a cycle starts at each k_entry dispatch), and prints, per stream and per ke
 average duration and time per cycle, plus each stream's busy time and the
 device-idle time (no kernel on any stream).
 
-`traffic` reads two counter-collection runs (FETCH_SIZE, then WRITE_SIZE, KiB
-per dispatch), scales each by what the same counter read for a plain copy of
-known size (1 GiB read + 1 GiB written) and prints the HBM bytes per launch of
-the stage-grouped gate/up GEMV, with a hash of the kernel sources they were
-taken on; bench.py reports the traffic only while that hash still matches.
+`traffic` reads two counter-collection runs of one workload step -- reads:
+TCC_EA0_RDREQ_DRAM_32B_sum (32-byte units of L2-to-memory read requests bound
+for DRAM; a 64-byte request counts 2, a 128-byte one 4) with the 32/64/128-byte
+request counts TCC_EA0_RDREQ_{32B,64B,128B}_sum; writes: TCC_EA0_WRREQ_sum and
+TCC_EA0_WRREQ_64B_sum (32- or 64-byte requests) -- checks them on a plain copy
+of known size (1 GiB read + 1 GiB written), and prints, per cycle kernel, the
+counted bytes per dispatch against the algorithmic bytes per dispatch of the
+step's schedule (bench.py --dump-schedule).  The gate/up record (with a hash
+of the kernel sources) feeds bench.py's roofline `traffic`, reported only
+while that hash still matches.
 """
 from __future__ import annotations
 
@@ -128,23 +133,117 @@ def copy_reading(d: str, counter: str):
     return max(vals) if vals else None
 
 
-def traffic(fetch_dir: str, write_dir: str):
-    f_gu, n_gu = counter_avg(fetch_dir, "FETCH_SIZE", GU_REGEX)
-    f_cp = copy_reading(fetch_dir, "FETCH_SIZE")
-    w_gu, m_gu = counter_avg(write_dir, "WRITE_SIZE", GU_REGEX)
-    w_cp = copy_reading(write_dir, "WRITE_SIZE")
-    fs = COPY_BYTES / (f_cp * 1024.0)
-    ws = COPY_BYTES / (w_cp * 1024.0)
-    rec = {
-        "kernel": "k_gemv_stage<bf16,SWIGLU>",
-        "workload": "4b_n8",
-        "source_hash": kernel_source_hash(),
-        "fetch_kib_per_dispatch": f_gu, "write_kib_per_dispatch": w_gu,
-        "dispatches": [n_gu, m_gu],
-        "copy_fetch_kib": f_cp, "copy_write_kib": w_cp, "fetch_scale": fs, "write_scale": ws,
-        "traffic_bytes_per_launch": f_gu * 1024.0 * fs + w_gu * 1024.0 * ws,
-    }
-    return rec
+RD_COUNTERS = ("TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+               "TCC_EA0_RDREQ_128B_sum")
+WR_COUNTERS = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")
+
+
+def _per_dispatch(d: str):
+    """{dispatch id: {"name", "grid", counter: value}} of one counter run."""
+    per = {}
+    for r in _counter_rows(d):
+        e = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"])})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def _read_bytes(e):
+    return (e.get("TCC_EA0_RDREQ_DRAM_32B_sum", 0.0) * 32.0,
+            e.get("TCC_EA0_RDREQ_32B_sum", 0.0) * 32.0 + e.get("TCC_EA0_RDREQ_64B_sum", 0.0) * 64.0
+            + e.get("TCC_EA0_RDREQ_128B_sum", 0.0) * 128.0)
+
+
+def _write_bytes(e):
+    n, n64 = e.get("TCC_EA0_WRREQ_sum", 0.0), e.get("TCC_EA0_WRREQ_64B_sum", 0.0)
+    return (n - n64) * 32.0 + n64 * 64.0
+
+
+def cycle_kernels(w, sched):
+    """(label, kernel regex, grid or None, algorithmic bytes per dispatch) of
+    the cycle kernels of one step with the given schedule (per-cycle
+    occupancy and exit).  Stage kernels stream a * matrix per launch (one
+    launch per sub-step); the heads share one kernel instance (the draft head
+    every cycle, the verification head launched every cycle but streaming
+    only when a token exits); the draft module's products stream their matrix
+    once per launch."""
+    es = 2 if w.dtype == "bf16" else 4
+    d, F, V = w.d, w.F, w.V
+    qkv = (w.Hq + 2 * w.Hkv) * w.hd * d * es
+    wo = w.Hq * w.hd * d * es
+    wgu, wdn = 2 * F * d * es, d * F * es
+    K = len(sched)
+    occ = sum(c["occupancy"] for c in sched) / K
+    exits = sum(1 for c in sched if c["exit_pos"] >= 0)
+    head = V * d * es * (K + exits) / (2 * K)
+    ks = [
+        ("stage q/k/v", r"k_gemv_stage<[^,]+, 0, false", None, occ * qkv),
+        ("stage o-projection", r"k_gemv_stage<[^,]+, 1, false", None, occ * wo),
+        ("stage gate/up", r"k_gemv_stage<[^,]+, 2, false", None, occ * wgu),
+        ("stage down", r"k_gemv_stage<[^,]+, 1, true", None, occ * wdn),
+        ("LM heads (draft every cycle, target on exit)", r"k_gemv_stage<[^,]+, 3, false", None, head),
+        ("draft gate/up", r"k_mfma_gemv<2, ", None, wgu),
+        ("draft o-projection", r"k_mfma_gemv<1, ", None, wo),
+        ("draft down", r"k_mfma_gemv<1, ", None, wdn),
+        ("draft q/k/v", r"k_mfma_gemv<0, ", None, qkv),
+    ]
+    return ks
+
+
+def traffic(read_dir: str, write_dir: str, sched_json: str):
+    """Counted read/write bytes per dispatch of each cycle kernel (dispatches
+    after the first cycle entry), the copy's reading, and the ratios."""
+    import seeded_inputs as si
+
+    sc = json.load(open(sched_json))
+    w = si.workload(sc["workload"])
+    sched = sc["cycles"]
+    rd, wr = _per_dispatch(read_dir), _per_dispatch(write_dir)
+    out = {"workload": w.name, "source_hash": kernel_source_hash(), "kernels": []}
+    for name, per, fn in (("read", rd, _read_bytes), ("write", wr, _write_bytes)):
+        cps = [e for e in per.values() if re.search(COPY_REGEX, e["name"])]
+        if cps:
+            best = max(cps, key=lambda e: fn(e)[0] if name == "read" else fn(e))
+            out[f"copy_{name}"] = fn(best)
+    ids_r = sorted(rd)
+    first = next((i for i in ids_r if "k_entry" in rd[i]["name"]), 0)
+    # the mfma down projection and o-projection share an instance: the o-projection has the smaller grid
+    for label, rx, _, alg in cycle_kernels(w, sched):
+        sel = [i for i in ids_r if i >= first and re.search(rx, rd[i]["name"])]
+        if label in ("draft down", "draft o-projection"):
+            grids = sorted({rd[i]["grid"] for i in sel})
+            if grids:
+                g_ = grids[-1] if label == "draft down" else grids[0]
+                sel = [i for i in sel if rd[i]["grid"] == g_]
+        if not sel:
+            continue
+        r_dram = sum(_read_bytes(rd[i])[0] for i in sel) / len(sel)
+        r_all = sum(_read_bytes(rd[i])[1] for i in sel) / len(sel)
+        wsel = [i for i in sorted(wr) if re.search(rx, wr[i]["name"]) and i in rd and i >= first]
+        wb = sum(_write_bytes(wr[i]) for i in wsel) / len(wsel) if wsel else None
+        out["kernels"].append({"kernel": label, "dispatches": len(sel), "algorithmic_bytes": alg,
+                               "read_dram_bytes": r_dram, "read_all_bytes": r_all, "write_bytes": wb,
+                               "read_ratio": r_dram / alg if alg else None})
+    gu = next((k for k in out["kernels"] if k["kernel"] == "stage gate/up"), None)
+    if gu:
+        out["kernel"] = "k_gemv_stage<bf16,SWIGLU>"
+        out["traffic_bytes_per_launch"] = gu["read_dram_bytes"] + (gu["write_bytes"] or 0.0)
+    return out
+
+
+def traffic_table(rec) -> str:
+    lines = []
+    cr, cw = rec.get("copy_read"), rec.get("copy_write")
+    if cr:
+        lines.append(f"calibration copy (1 GiB read + 1 GiB written): DRAM reads {cr[0] / COPY_BYTES:.3f}x, "
+                     f"all reads {cr[1] / COPY_BYTES:.3f}x, writes "
+                     f"{(cw or 0) / COPY_BYTES:.3f}x of the known bytes")
+    lines.append(f"{'kernel':46s} {'dispatches':>10s} {'algorithmic MB':>15s} {'DRAM read MB':>13s} "
+                 f"{'all read MB':>12s} {'write MB':>9s} {'read/alg':>9s}")
+    for k in rec["kernels"]:
+        lines.append(f"{k['kernel'][:46]:46s} {k['dispatches']:10d} {k['algorithmic_bytes'] / 1e6:15.1f} "
+                     f"{k['read_dram_bytes'] / 1e6:13.1f} {k['read_all_bytes'] / 1e6:12.1f} "
+                     f"{(k['write_bytes'] or 0) / 1e6:9.2f} {k['read_ratio']:9.3f}")
+    return "\n".join(lines)
 
 
 MFMA_PEAK_BF16 = 2.5e15  # dense bf16 matrix-core peak of one MI355X, flop/s
@@ -195,8 +294,9 @@ def main(argv=None):
     t.add_argument("--skip", type=int, default=0)
     t.add_argument("--cmd", default="")
     b = sub.add_parser("traffic")
-    b.add_argument("fetch_dir")
+    b.add_argument("read_dir")
     b.add_argument("write_dir")
+    b.add_argument("schedule")
     b.add_argument("--cmd", default="")
     b.add_argument("--write-json", action="store_true")
     mf = sub.add_parser("mfma")
@@ -216,9 +316,9 @@ def main(argv=None):
             print(f"command: {args.cmd}")
         print(mfma(args.dir))
     else:
-        rec = traffic(args.fetch_dir, args.write_dir)
+        rec = traffic(args.read_dir, args.write_dir, args.schedule)
         rec["command"] = args.cmd
-        print(json.dumps(rec, indent=2))
+        print(traffic_table(rec))
         if args.write_json:
             json.dump(rec, open(TRAFFIC_JSON, "w"), indent=2)
 

@@ -61,6 +61,9 @@ class Workload:
     top_k: int = 0          # sample mode: keep the k largest logits (0: the whole vocabulary)
     attn_period: int = 0    # hybrid target: layer l is softmax attention iff l % P == P-1, else linear (0: all softmax)
     split: tuple = ()       # layers of stages 0..n-1 (empty: L/n each)
+    width: int = 1          # draft-tree width W (1: one draft per cycle)
+    p_tree: float = 0.0     # tree forced policy: the true token is among the W candidates w.p. p_tree
+                            # (first-ranked w.p. p_accept)
 
     @property
     def max_ctx(self) -> int:
@@ -102,6 +105,13 @@ WORKLOADS: Dict[str, Workload] = {
     "4b_n8_post": Workload("4b_n8_post", "bf16", 32, 2560, 20, 4, 128, 9728, 151936, 8, 4,
                            [0, 8, 16, 24, 31], P=512, G=256, policy="forced",
                            p_accept=0.8, seed=2, schedule="post"),
+    # 4b_n8 with a width-4 draft tree: the true token is the best-ranked
+    # candidate w.p. 0.8 (as in 4b_n8) and among the 4 w.p. 0.87 -- the tree
+    # acceptance the pages' width-4 results imply (n=8 theoretical speedup
+    # 3.05 -> 3.84, i.e. a reject rate ~0.67x that of one draft)
+    "4b_tree4_n8": Workload("4b_tree4_n8", "bf16", 32, 2560, 20, 4, 128, 9728, 151936, 8, 4,
+                            [0, 8, 16, 24, 31], P=512, G=256, policy="forced",
+                            p_accept=0.8, seed=2, width=4, p_tree=0.87),
     # 4B shapes on the pages' non-uniform 4-stage split 5+4;9;9;9 (a 5-layer
     # first stage, three 9-layer stages, a 4-layer draft module)
     "4b_split_n4": Workload("4b_split_n4", "bf16", 32, 2560, 20, 4, 128, 9728, 151936, 4, 4,

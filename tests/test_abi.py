@@ -35,9 +35,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    # spd_cycle_rec: 12 words + 64 KV lengths
-    assert ctypes.sizeof(A.spd_cycle_rec) == 4 * (12 + A.SPD_MAX_LAYERS) == REC_DTYPE.itemsize
-    assert ctypes.sizeof(A.spd_config) == 4 * (10 + A.SPD_MAX_ANCHORS + 4 + 3 + 3 + A.SPD_MAX_STAGES)
+    # spd_cycle_rec: 12 words + 64 KV lengths + the tree fields
+    assert ctypes.sizeof(A.spd_cycle_rec) == 4 * (12 + A.SPD_MAX_LAYERS + 3 + 2 * A.SPD_MAX_WIDTH) \
+        == REC_DTYPE.itemsize
+    assert ctypes.sizeof(A.spd_config) == 4 * (10 + A.SPD_MAX_ANCHORS + 4 + 3 + 3 + A.SPD_MAX_STAGES + 1)
     assert ctypes.sizeof(A.spd_weights) == 8 * (1 + 6 * A.SPD_MAX_LAYERS + 2 + A.SPD_MAX_ANCHORS
                                                 + 6 * A.SPD_MAX_PDM_LAYERS + 2)
 

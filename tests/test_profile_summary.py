@@ -58,34 +58,72 @@ def test_timeline_needs_enough_cycles(tmp_path):
         ps.timeline(str(p), cycles=2)
 
 
-def _write_counters(d, counter, rows):
+def _write_counters(d, rows):
+    """rows: (dispatch id, kernel, grid, {counter: value})."""
     os.makedirs(d, exist_ok=True)
     with open(os.path.join(d, "x_counter_collection.csv"), "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
         w.writeheader()
-        for name, v in rows:
-            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+        for i, name, grid, cs in rows:
+            for c, v in cs.items():
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Grid_Size": grid, "Counter_Name": c,
+                            "Counter_Value": v})
 
 
-def test_traffic_is_scaled_by_the_calibration_copy(tmp_path):
-    copy = "__amd_rocclr_copyBuffer"
-    # the copy reads 1 GiB but the counter shows half: fetch scale 2
-    _write_counters(tmp_path / "f", "FETCH_SIZE", [(GU, 100.0), (GU, 300.0), (copy, 4.0), (copy, 524288.0)])
-    _write_counters(tmp_path / "w", "WRITE_SIZE", [(GU, 10.0), (GU, 10.0), (copy, 1048576.0)])
-    rec = ps.traffic(str(tmp_path / "f"), str(tmp_path / "w"))
-    assert rec["dispatches"] == [2, 2]
-    assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
-    assert rec["traffic_bytes_per_launch"] == pytest.approx(200 * 1024 * 2.0 + 10 * 1024)
-    assert rec["source_hash"] == ps.kernel_source_hash()
-
-
-def test_committed_traffic_record_matches_the_kernel_sources():
-    """bench.py reports the counted traffic only while the record's source
-    hash matches the GEMV sources; the committed record must be current."""
+def test_traffic_per_kernel_and_copy_check(tmp_path):
+    """Read bytes = 32 x DRAM 32-byte units (and 32/64/128 x the request
+    counts), writes = 32/64 x the write requests; the copy's reading is shown
+    against its known bytes; dispatches before the first cycle entry (a
+    prefill) are left out; per-dispatch averages against the schedule's
+    algorithmic bytes."""
     import json
-    rec = json.load(open(ps.TRAFFIC_JSON))
+    import seeded_inputs as si
+    w = si.workload("4b_n8")
+    copy = "__amd_rocclr_copyBuffer"
+    GIB = 1 << 30
+    rd = [(1, copy, 100, {"TCC_EA0_RDREQ_DRAM_32B_sum": GIB / 32, "TCC_EA0_RDREQ_32B_sum": 0,
+                          "TCC_EA0_RDREQ_64B_sum": 0, "TCC_EA0_RDREQ_128B_sum": GIB / 128}),
+          (2, GU, 7, {"TCC_EA0_RDREQ_DRAM_32B_sum": 9e9, "TCC_EA0_RDREQ_32B_sum": 0,
+                      "TCC_EA0_RDREQ_64B_sum": 0, "TCC_EA0_RDREQ_128B_sum": 0}),       # before the cycles
+          (3, "void spd::k_entry<unsigned short>(spd::Ctrl*)", 256, {"TCC_EA0_RDREQ_DRAM_32B_sum": 1}),
+          (4, GU, 7, {"TCC_EA0_RDREQ_DRAM_32B_sum": 1e6, "TCC_EA0_RDREQ_32B_sum": 2e5,
+                      "TCC_EA0_RDREQ_64B_sum": 1e5, "TCC_EA0_RDREQ_128B_sum": 1e5}),
+          (5, GU, 7, {"TCC_EA0_RDREQ_DRAM_32B_sum": 3e6, "TCC_EA0_RDREQ_32B_sum": 0,
+                      "TCC_EA0_RDREQ_64B_sum": 0, "TCC_EA0_RDREQ_128B_sum": 0})]
+    wr = [(1, copy, 100, {"TCC_EA0_WRREQ_sum": GIB / 64, "TCC_EA0_WRREQ_64B_sum": GIB / 64}),
+          (4, GU, 7, {"TCC_EA0_WRREQ_sum": 10, "TCC_EA0_WRREQ_64B_sum": 4}),
+          (5, GU, 7, {"TCC_EA0_WRREQ_sum": 10, "TCC_EA0_WRREQ_64B_sum": 4})]
+    _write_counters(tmp_path / "r", rd)
+    _write_counters(tmp_path / "w", wr)
+    sched = {"workload": "4b_n8", "cycles": [{"occupancy": 4, "exit_pos": -1}, {"occupancy": 8, "exit_pos": 5}]}
+    json.dump(sched, open(tmp_path / "s.json", "w"))
+    rec = ps.traffic(str(tmp_path / "r"), str(tmp_path / "w"), str(tmp_path / "s.json"))
+    assert rec["copy_read"][0] == pytest.approx(GIB) and rec["copy_read"][1] == pytest.approx(GIB)
+    assert rec["copy_write"] == pytest.approx(GIB)
+    gu = next(k for k in rec["kernels"] if k["kernel"] == "stage gate/up")
+    assert gu["dispatches"] == 2
+    assert gu["read_dram_bytes"] == pytest.approx(2e6 * 32)
+    assert gu["read_all_bytes"] == pytest.approx((2e5 * 32 + 1e5 * 64 + 1e5 * 128) / 2)
+    assert gu["write_bytes"] == pytest.approx(6 * 32 + 4 * 64)
+    assert gu["algorithmic_bytes"] == pytest.approx(6 * 2 * w.F * w.d * 2)  # mean occupancy 6
+    assert rec["traffic_bytes_per_launch"] == pytest.approx(2e6 * 32 + 6 * 32 + 4 * 64)
     assert rec["source_hash"] == ps.kernel_source_hash()
-    assert rec["traffic_bytes_per_launch"] > 0
+    assert "stage gate/up" in ps.traffic_table(rec)
+
+
+def test_bench_reports_only_a_current_traffic_record():
+    """bench.py reports the counted traffic only while the record's source
+    hash matches the GEMV sources (a kernel change since the counters were
+    taken makes it report none)."""
+    import json
+    import bench
+    rec = json.load(open(ps.TRAFFIC_JSON))
+    got = bench.traffic_bytes(rec.get("workload"))
+    if rec.get("source_hash") == ps.kernel_source_hash():
+        assert got == int(rec["traffic_bytes_per_launch"]) and got > 0
+    else:
+        assert got is None
+    assert bench.traffic_bytes("another workload") is None
 
 
 def test_mfma_summary_counts_only_the_cycles(tmp_path):
