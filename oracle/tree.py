@@ -40,13 +40,17 @@ With W = 1 the tree is the single in-flight chain and the run is the
 pipeline of oracle.spd step for step (a pin in the CPU tests).
 
 Forced acceptance for trees (harness device, not on the pages): with the
-target's greedy continuation R and the forced leaf (the on-path leaf, whose
-path tokens all equal R, if any, else the leaf of rank 0), the draw
+target's greedy continuation R and the forced leaf (the leaf whose path,
+from the oldest in-flight position, matches R for the longest prefix; ties
+to the lower rank), the draw
 u = U[q, FORCE] for position q places the pair (forced leaf, R[q]) first in
 the ranking when u < p1, at rank W-1 when p1 <= u < pW and W >= 2 (only a
 tree catches it), and otherwise removes it (its token is replaced by the
-next id not already a candidate of that leaf).  With W = 1 this is the
-single-draft forced policy with p = p1.
+next id not already a candidate of that leaf) while keeping the forced
+leaf's branch alive: if none of its candidates is among the first W, such a
+wrong child is put at rank W-1 (a draft module that keeps the true branch
+but misses its next token, as one draft per cycle does).  With W = 1 this is
+the single-draft forced policy with p = p1.
 """
 from __future__ import annotations
 
@@ -377,12 +381,17 @@ class TreeSPDOracle:
         pol = self.policy
         if pol is None or q >= len(pol.ref):
             return cands
-        star = 0
         oldest = min(self.levels)
-        for r, leaf in enumerate(leaves):
-            if all(x.tok == pol.ref[x.pos] for x in leaf.path(oldest - 1)):
-                star = r
-                break
+
+        def matched(leaf):
+            k = 0
+            for x in leaf.path(oldest - 1):
+                if x.tok != pol.ref[x.pos]:
+                    break
+                k += 1
+            return k
+        m = [matched(lf) for lf in leaves]
+        star = m.index(max(m))
         leaf, R = leaves[star], pol.ref[q]
         u = pol.u[q, U_FORCE]
         cum = sum(x.logq for x in leaf.path(oldest))
@@ -393,12 +402,19 @@ class TreeSPDOracle:
             if at:
                 cands.pop(at[0])
             cands.insert(0 if u < pol.p1 else min(self.Wd - 1, len(cands)), (leaf, R, cum + float(lq[R]), float(lq[R])))
-        elif at:
-            used = {cd[1] for cd in cands if cd[0] is leaf}
-            x = (R + 1) % self.V
-            while x in used:
-                x = (x + 1) % self.V
-            cands[at[0]] = (leaf, x, cum + float(lq[x]), float(lq[x]))
+        else:
+            def next_free():
+                used = {cd[1] for cd in cands if cd[0] is leaf}
+                x = (R + 1) % self.V
+                while x in used:
+                    x = (x + 1) % self.V
+                return x
+            if at:
+                x = next_free()
+                cands[at[0]] = (leaf, x, cum + float(lq[x]), float(lq[x]))
+            if not any(cd[0] is leaf for cd in cands[: self.Wd]):
+                x = next_free()
+                cands.insert(min(self.Wd - 1, len(cands)), (leaf, x, cum + float(lq[x]), float(lq[x])))
         return cands
 
     def _teach_entry(self, c: int, chosen, leaves):

@@ -568,17 +568,21 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
   // forced policy (harness device): the pair (forced leaf, ref[q])
   const int q = t + 1;
   if (A.policy == SPD_DRAFT_FORCED && q < A.ref_len) {
-    int star = 0;
+    // the leaf whose path matches the reference for the longest prefix from
+    // the oldest position (ties: the lower rank)
+    int star = 0, best = -1;
     for (int m = 0; m < nl; ++m) {
-      bool on = true;
-      int x = lslot[m];
+      int match[SPD_MAX_STAGES + 1];
+      int x = lslot[m], np = 0;
       for (int p = t; p >= oldest; --p) {
-        if (T->tok[x] != A.ref[p]) on = false;
+        match[np++] = T->tok[x] == A.ref[p];
         if (p > oldest) x = T->parent[x];
       }
-      if (on) {
+      int k = 0;
+      while (k < np && match[np - 1 - k]) ++k;
+      if (k > best) {
+        best = k;
         star = m;
-        break;
       }
     }
     const int R = A.ref[q];
@@ -605,19 +609,43 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
       clq[ins] = lq;
       cs[ins] = cum[star] + lq;
       ++nc;
-    } else if (at >= 0) {
-      int x = (R + 1) % g.V;
-      for (;;) {
-        bool used = false;
-        for (int i = 0; i < nc; ++i)
-          if (crank[i] == star && ct[i] == x) used = true;
-        if (!used) break;
-        x = (x + 1) % g.V;
+    } else {
+      // a miss: the forced leaf's true token is replaced by the next id that
+      // is not already one of its candidates, and its branch stays alive
+      auto next_free = [&]() {
+        int x = (R + 1) % g.V;
+        for (;;) {
+          bool used = false;
+          for (int i = 0; i < nc; ++i)
+            if (crank[i] == star && ct[i] == x) used = true;
+          if (!used) return x;
+          x = (x + 1) % g.V;
+        }
+      };
+      if (at >= 0) {
+        const int x = next_free();
+        const double lq = (double)ls[x] - lM[star] - lZ[star];
+        ct[at] = x;
+        clq[at] = lq;
+        cs[at] = cum[star] + lq;
       }
-      const double lq = (double)ls[x] - lM[star] - lZ[star];
-      ct[at] = x;
-      clq[at] = lq;
-      cs[at] = cum[star] + lq;
+      bool alive = false;
+      for (int i = 0; i < nc && i < W; ++i)
+        if (crank[i] == star) alive = true;
+      if (!alive) {
+        const int x = next_free();
+        const int ins = min(W - 1, nc);
+        for (int i = nc; i > ins; --i) {
+          cl[i] = cl[i - 1]; ct[i] = ct[i - 1]; crank[i] = crank[i - 1]; cs[i] = cs[i - 1]; clq[i] = clq[i - 1];
+        }
+        const double lq = (double)ls[x] - lM[star] - lZ[star];
+        cl[ins] = lslot[star];
+        ct[ins] = x;
+        crank[ins] = star;
+        clq[ins] = lq;
+        cs[ins] = cum[star] + lq;
+        ++nc;
+      }
     }
   }
   T->ncand = nc;
