@@ -128,12 +128,15 @@ def main():
     T = si.make_weights(w, "cuda:0")
     torch.cuda.synchronize()
     log(f"weights generated on GPU in {time.time() - t0:.1f}s")
-    # a plain 1 GiB copy: the reference the HBM traffic counters are scaled by
+    # dispatches of known HBM traffic that the traffic counters are checked
+    # on: a 1 GiB fill (writes), a sum over it (reads) and a 1 GiB copy (both)
     calib_src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    calib_sum = calib_src.sum()
     calib_dst = torch.empty_like(calib_src)
     calib_dst.copy_(calib_src)
     torch.cuda.synchronize()
-    del calib_src, calib_dst
+    assert float(calib_sum) == float(1 << 28)
+    del calib_src, calib_dst, calib_sum
     eng = SPDEngine(w, T)
     uni = si.make_uniforms(w)
     eng.set_uniforms(uni)

@@ -333,7 +333,15 @@ SPD_API int spd_set_launch_mode(spd_t *h, int32_t mode);
  * cover max_ctx.  Errors: SPD_EINVAL. */
 SPD_API int spd_set_uniforms(spd_t *h, const float *uniforms_dev, int32_t n_positions);
 
-/* Prefill: full target pass over the prompt (host int32 ids in [0,V)),
+/* Prefill.  The pages describe decoding only and say nothing of how the
+ * prompt is processed; this library takes the plain reading that a prompt
+ * is an ordinary full target pass (the same per-token arithmetic as the
+ * pipeline's stages) whose anchor taps also build the draft module's
+ * committed state, so that the first cycle starts from the state the method
+ * assumes ([RB] method step 1: the pipeline starts from a committed
+ * prefix; [PL] section 3.3: the draft module's pre-step inputs).
+ *
+ * Full target pass over the prompt (host int32 ids in [0,V)),
  * writing every layer's KV and the PDM's committed state for all prompt
  * positions, then the first generated token (argmax, or drawn with
  * u[len][SPD_U_TARGET]).  Leaves the pipeline empty, seeded with that token
@@ -342,7 +350,19 @@ SPD_API int spd_set_uniforms(spd_t *h, const float *uniforms_dev, int32_t n_posi
  * max_ctx), SPD_EHIP. */
 SPD_API int spd_prefill(spd_t *h, const int32_t *prompt_host, int32_t len, int32_t *first_token);
 
-/* Enqueue n_cycles SPD cycles on the two streams and return without waiting.
+/* One SPD cycle carries out [RB] method steps 1-5: entry of the newest
+ * draft with its anchor 0, one stage sub-step of every in-flight token, the
+ * draft module on the pre-step anchors, verification of the token leaving
+ * the last stage and, on rejection, the three-step rollback; in [PL]'s
+ * terms sections 3.1-3.4 (stage-grouped decode, the fused anchor feature,
+ * the pre-step draft module, the verify/rollback rule).  With draft_width
+ * W >= 2 the in-flight tokens form a draft tree ([RB] prerequisites, draft
+ * tree; [PL] appendix B): the entry adds up to W nodes, every node takes
+ * the stage sub-step, and verification keeps the exiting node's matching
+ * child.  The stage sub-step runs on the stage stream and the draft module
+ * on the draft stream, joined by events at the cycle boundary.
+ *
+ * Enqueue n_cycles SPD cycles on the two streams and return without waiting.
  * Cycles enqueued after max_new tokens have been emitted do nothing (their
  * records carry SPD_FLAG_IDLE).  If log_host is not NULL it must be pinned
  * host memory for n_cycles records; they are valid once spd_sync returned.

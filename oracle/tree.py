@@ -363,7 +363,7 @@ class TreeSPDOracle:
         for r, leaf in enumerate(leaves):
             lg = pdm.logits(X[base + r])
             if self.hook is not None:
-                self.hook("pdm", dict(cycle=c, rank=r, logits=lg))
+                self.hook("pdm", dict(cycle=c, rank=r, leaf=leaf, logits=lg))
             lq = log_softmax64(lg)
             lq_all.append(lq)
             cum = sum(x.logq for x in leaf.path(min(self.levels)))

@@ -14,8 +14,9 @@ device-idle time (no kernel on any stream).
 TCC_EA0_RDREQ_DRAM_32B_sum (32-byte units of L2-to-memory read requests bound
 for DRAM; a 64-byte request counts 2, a 128-byte one 4) with the 32/64/128-byte
 request counts TCC_EA0_RDREQ_{32B,64B,128B}_sum; writes: TCC_EA0_WRREQ_sum and
-TCC_EA0_WRREQ_64B_sum (32- or 64-byte requests) -- checks them on a plain copy
-of known size (1 GiB read + 1 GiB written), and prints, per cycle kernel, the
+TCC_EA0_WRREQ_64B_sum (32- or 64-byte requests) -- checks them on plain
+dispatches of known size (a sum over 1 GiB reads it once, a fill of 1 GiB
+writes it once, a 1 GiB copy does both), and prints, per cycle kernel, the
 counted bytes per dispatch against the algorithmic bytes per dispatch of the
 step's schedule (bench.py --dump-schedule).  The gate/up record (with a hash
 of the kernel sources) feeds bench.py's roofline `traffic`, reported only
@@ -37,6 +38,8 @@ ROOT = os.path.dirname(HERE)
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_gate_up_4b_n8.json")
 GU_REGEX = r"k_gemv_stage<unsigned short, 2[,>]"
 COPY_REGEX = r"copy"
+SUM_REGEX = r"reduce_kernel"
+FILL_REGEX = r"FillFunctor"
 COPY_BYTES = 1 << 30
 
 
@@ -199,11 +202,12 @@ def traffic(read_dir: str, write_dir: str, sched_json: str):
     sched = sc["cycles"]
     rd, wr = _per_dispatch(read_dir), _per_dispatch(write_dir)
     out = {"workload": w.name, "source_hash": kernel_source_hash(), "kernels": []}
-    for name, per, fn in (("read", rd, _read_bytes), ("write", wr, _write_bytes)):
-        cps = [e for e in per.values() if re.search(COPY_REGEX, e["name"])]
+    # calibration dispatches (before the cycles): the largest one of each kind
+    for key, per, fn, rx in (("copy_read", rd, _read_bytes, COPY_REGEX), ("copy_write", wr, _write_bytes, COPY_REGEX),
+                             ("sum_read", rd, _read_bytes, SUM_REGEX), ("fill_write", wr, _write_bytes, FILL_REGEX)):
+        cps = [e for e in per.values() if re.search(rx, e["name"])]
         if cps:
-            best = max(cps, key=lambda e: fn(e)[0] if name == "read" else fn(e))
-            out[f"copy_{name}"] = fn(best)
+            out[key] = max((fn(e) for e in cps), key=lambda v: v[0] if isinstance(v, tuple) else v)
     ids_r = sorted(rd)
     first = next((i for i in ids_r if "k_entry" in rd[i]["name"]), 0)
     # the mfma down projection and o-projection share an instance: the o-projection has the smaller grid
@@ -232,6 +236,11 @@ def traffic(read_dir: str, write_dir: str, sched_json: str):
 
 def traffic_table(rec) -> str:
     lines = []
+    sr, fw = rec.get("sum_read"), rec.get("fill_write")
+    if sr or fw:
+        lines.append(f"calibration sum over 1 GiB: DRAM reads {sr[0] / COPY_BYTES:.3f}x, all reads "
+                     f"{sr[1] / COPY_BYTES:.3f}x; fill of 1 GiB: writes {(fw or 0) / COPY_BYTES:.3f}x of the known bytes"
+                     if sr else f"calibration fill of 1 GiB: writes {(fw or 0) / COPY_BYTES:.3f}x of the known bytes")
     cr, cw = rec.get("copy_read"), rec.get("copy_write")
     if cr:
         lines.append(f"calibration copy (1 GiB read + 1 GiB written): DRAM reads {cr[0] / COPY_BYTES:.3f}x, "

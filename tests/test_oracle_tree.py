@@ -15,10 +15,13 @@ module header.  Pinned by:
   * each node's state equals a plain forward of its own path: the exiting
     node's logits equal the AR target logits, and the draft module's row of
     every leaf equals the chain computation over that leaf's path alone;
+  * the entered nodes are the top-W pairs (surviving leaf, token) by the
+    product of draft probabilities along the path, by brute force over every
+    surviving leaf and every token with torch's float64 softmax;
   * the tree's shape: at most W nodes per position, one at the oldest, every
     node a child of the previous position, the accepted child kept;
-  * planted mistakes (no pruning, all-rows draft attention, a sibling's KV)
-    are caught.
+  * planted mistakes (no pruning, all-rows draft attention, a sibling's KV,
+    a ranking without the path probability) are caught.
 """
 import numpy as np
 import pytest
@@ -266,3 +269,87 @@ def test_sibling_kv_is_caught(monkeypatch):
     monkeypatch.setattr(TreeSPDOracle, "_run_stage", bad_run)
     with pytest.raises(AssertionError):
         test_node_states_follow_their_own_paths(2)
+
+
+# -- the ranking: top-W branches by cumulative probability -------------------
+def test_log_softmax64_matches_torch():
+    import torch
+    rng = np.random.default_rng(5)
+    for V in (7, 300, 4096):
+        l = (rng.standard_normal(V) * rng.uniform(0.1, 30)).astype(np.float32)
+        want = torch.log_softmax(torch.from_numpy(l.astype(np.float64)), 0).numpy()
+        assert np.allclose(TR.log_softmax64(l), want, rtol=0, atol=1e-12)
+
+
+def _entries_by_brute_force(mi, Wd, G=24):
+    """Run the tree with its own draft module (no forcing) and, at every
+    cycle that enters drafted nodes, compare the entered (parent, token)
+    pairs with the top-W pairs over ALL surviving leaves and ALL tokens by
+    the product of draft probabilities along the path, the probabilities
+    taken by torch's float64 softmax of the logits each parent leaf had
+    when it drafted.  Returns the number of cycles checked."""
+    import torch
+    w, W, prompt, u, ref, _ = _setup(G=G, **MODELS[mi])
+    o = TreeSPDOracle(w, W, Wd)
+    logits = {}  # id(leaf) -> draft logits of the cycle it was a leaf in
+
+    def hook(kind, info):
+        if kind == "pdm":
+            logits[id(info["leaf"])] = info["logits"]
+
+    o.hook = hook
+    o.prefill(prompt)
+
+    def prob(x):
+        if id(x.parent) not in logits:     # a re-seeded or verified root: common to every path
+            return 1.0
+        p = torch.softmax(torch.from_numpy(logits[id(x.parent)].astype(np.float64)), 0)
+        return float(p[x.tok])
+
+    checked = 0
+    while o.emitted < w.G:
+        # the leaves that survived the last verification: the next entry drafts from them
+        leaves = list(o.levels[max(o.levels)]) if o.levels and o.reseed is None else []
+        rec = o.cycle()
+        if not leaves:
+            continue
+        assert rec["new_parent"][0] >= 0
+        pool = []
+        for lf in leaves:
+            path_p = 1.0
+            x = lf
+            while x is not None:
+                path_p *= prob(x)
+                x = x.parent
+            q = torch.softmax(torch.from_numpy(logits[id(lf)].astype(np.float64)), 0).numpy()
+            for tok in range(w.V):
+                pool.append((path_p * q[tok], lf, tok))
+        pool.sort(key=lambda e: -e[0])
+        want = {(id(lf), tok) for _, lf, tok in pool[:Wd]}
+        got = {(id(leaves[pr]), tok) for pr, tok in zip(rec["new_parent"], rec["new_token"])}
+        assert got == want, (rec["cycle"], got, want)
+        checked += 1
+    return checked
+
+
+@pytest.mark.parametrize("mi,Wd", [(0, 2), (1, 4), (3, 3)])
+def test_entries_are_the_top_branches_by_cumulative_probability(mi, Wd):
+    assert _entries_by_brute_force(mi, Wd) >= 5
+
+
+def test_ranking_without_the_path_probability_is_caught(monkeypatch):
+    """Ranking every leaf's candidates by their own draft probability alone
+    (dropping the path's cumulative probability) picks other branches."""
+    orig = TR.Node.path
+
+    def short_path(self, stop):
+        out = orig(self, stop)
+        import inspect
+        if inspect.stack()[1].function == "_draft":
+            return out[-1:]            # cum = the leaf's own log probability only
+        return out
+
+    monkeypatch.setattr(TR.Node, "path", short_path)
+    with pytest.raises(AssertionError):
+        for mi, Wd in [(0, 2), (1, 4), (3, 3)]:
+            _entries_by_brute_force(mi, Wd)

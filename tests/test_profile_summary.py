@@ -90,7 +90,12 @@ def test_traffic_per_kernel_and_copy_check(tmp_path):
                       "TCC_EA0_RDREQ_64B_sum": 1e5, "TCC_EA0_RDREQ_128B_sum": 1e5}),
           (5, GU, 7, {"TCC_EA0_RDREQ_DRAM_32B_sum": 3e6, "TCC_EA0_RDREQ_32B_sum": 0,
                       "TCC_EA0_RDREQ_64B_sum": 0, "TCC_EA0_RDREQ_128B_sum": 0})]
-    wr = [(1, copy, 100, {"TCC_EA0_WRREQ_sum": GIB / 64, "TCC_EA0_WRREQ_64B_sum": GIB / 64}),
+    red = "void at::native::reduce_kernel<512, 1, at::native::ReduceOp<float, at::native::func_wrapper_t<float, at::native::sum_functor<float, float, float>::operator()(at::TensorIterator&)::{lambda(float, float)#1}>, unsigned int, float, 4, 4> >(at::native::ReduceOp<float, at::native::func_wrapper_t<float, at::native::sum_functor<float, float, float>::operator()(at::TensorIterator&)::{lambda(float, float)#1}>, unsigned int, float, 4, 4>)"
+    fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>, std::array<char*, 1ul> >(int, at::native::FillFunctor<float>, std::array<char*, 1ul>)"
+    rd.insert(0, (0, red, 100, {"TCC_EA0_RDREQ_DRAM_32B_sum": GIB / 32 * 1.01, "TCC_EA0_RDREQ_32B_sum": 0,
+                               "TCC_EA0_RDREQ_64B_sum": GIB / 64, "TCC_EA0_RDREQ_128B_sum": 0}))
+    wr = [(0, fill, 100, {"TCC_EA0_WRREQ_sum": GIB / 64, "TCC_EA0_WRREQ_64B_sum": GIB / 128}),
+          (1, copy, 100, {"TCC_EA0_WRREQ_sum": GIB / 64, "TCC_EA0_WRREQ_64B_sum": GIB / 64}),
           (4, GU, 7, {"TCC_EA0_WRREQ_sum": 10, "TCC_EA0_WRREQ_64B_sum": 4}),
           (5, GU, 7, {"TCC_EA0_WRREQ_sum": 10, "TCC_EA0_WRREQ_64B_sum": 4})]
     _write_counters(tmp_path / "r", rd)
@@ -100,6 +105,10 @@ def test_traffic_per_kernel_and_copy_check(tmp_path):
     rec = ps.traffic(str(tmp_path / "r"), str(tmp_path / "w"), str(tmp_path / "s.json"))
     assert rec["copy_read"][0] == pytest.approx(GIB) and rec["copy_read"][1] == pytest.approx(GIB)
     assert rec["copy_write"] == pytest.approx(GIB)
+    assert rec["sum_read"][0] == pytest.approx(1.01 * GIB) and rec["sum_read"][1] == pytest.approx(GIB)
+    assert rec["fill_write"] == pytest.approx(GIB * 0.75)  # half the requests 32-byte, half 64-byte
+    table = ps.traffic_table(rec)
+    assert "sum over 1 GiB: DRAM reads 1.010x" in table and "writes 0.750x" in table
     gu = next(k for k in rec["kernels"] if k["kernel"] == "stage gate/up")
     assert gu["dispatches"] == 2
     assert gu["read_dram_bytes"] == pytest.approx(2e6 * 32)
