@@ -31,7 +31,10 @@ def _run(w, T, static, uni, ref, p):
     out = dict(ws=eng.ws_bytes, recs=recs.tobytes(), toks=eng.tokens(0, w.P + w.G),
                logits=eng.logits().tobytes(), pdm_logits=eng.pdm_logits().tobytes(),
                anchors=[eng.anchors(q).tobytes() for q in range(t - a + 1, t + 1)],
-               kv=[(eng.kv(l, "k").tobytes(), eng.kv(l, "v").tobytes()) for l in sorted({0, w.L - 1})])
+               # committed positions only: the cache beyond a layer's length is never
+               # written and holds whatever the two engines' buffers held before
+               kv=[(eng.kv(l, "k")[: int(last["kv_len"][l])].tobytes(),
+                    eng.kv(l, "v")[: int(last["kv_len"][l])].tobytes()) for l in sorted({0, w.L - 1})])
     eng.close()
     return out
 
