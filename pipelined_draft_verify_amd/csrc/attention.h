@@ -48,6 +48,8 @@ struct Attn {
   float* pacc;     // [prow][Hq][nsplit][hd]
   float* pml;      // [prow][Hq][nsplit][2]
   float* o;        // merged output [prow][Hq*hd]
+  uint16_t* oh;    // or, if set, its split into bf16 hi + lo parts [prow][Hq*hd]
+  uint16_t* ol;
   int from_ctrl, pos0_arg, nrows_arg;
   int QB;          // rows per workgroup (rows mode)
   int qblocks;     // row blocks (rows mode)
@@ -572,7 +574,15 @@ __global__ __launch_bounds__(HD) void k_attn_merge(const Attn A) {
       }
     }
   }
-  A.o[(size_t)prow * g.Hq * HD + (size_t)head * HD + dim] = num / den;
+  const size_t oi = (size_t)prow * g.Hq * HD + (size_t)head * HD + dim;
+  if (A.oh) {
+    const float v = num / den;
+    const uint16_t hi = f32_to_bf16_rne(v);
+    A.oh[oi] = hi;
+    A.ol[oi] = f32_to_bf16_rne(v - bf16_bits_to_f32(hi));
+  } else {
+    A.o[oi] = num / den;
+  }
 }
 
 }  // namespace spd

@@ -25,6 +25,7 @@
 #include "gemv.h"
 #include "linattn.h"
 #include "mfma.h"
+#include "skinny.h"
 #include "tree.h"
 
 using namespace spd;
@@ -43,6 +44,8 @@ struct Layout {
   size_t Xt, Xp, r_q, r_pacc, r_pml, r_o, r_act, taps;
   size_t logits, plogits, pw, parts, pparts, ring;
   size_t ssq_t, ssq_p, mpart;
+  size_t wtile;                   // draft-module layer weights in matrix-core tile order (bf16)
+  size_t xs_h, xs_l, as_h, as_l, os_h, os_l;  // split (bf16 hi + lo) inputs of the draft module's products
   size_t lin_state, lin_ckpt;
   size_t zpart, tpart;
   size_t bsq, bsp;
@@ -221,7 +224,7 @@ Layout make_layout(const spd_config* c) {
   // matrix-core path (bf16): per-row partial sums of squares of the prefill
   // rows and the draft-module rows, and the split-K partial tiles
   L.ssq_t = scr(sizeof(float) * L.mr * (size_t)(d / kSsqCols));
-  L.ssq_p = scr(sizeof(float) * L.mr * (size_t)(d / kSsqCols));
+  L.ssq_p = scr(sizeof(float) * L.mr * (size_t)(d / kSkinnyCols));  // 64- or 16-column parts
   size_t pf = 0;
   if (c->dtype == SPD_DTYPE_BF16) {
     const int rows = L.mr;  // 16 * MT of the largest pass
@@ -237,6 +240,17 @@ Layout make_layout(const spd_config* c) {
     pf = std::max(pf, mfma_part_floats(d, full, 1, rows));
   }
   L.mpart = scr(sizeof(float) * std::max<size_t>(pf, 1));
+  // draft module in the cycle (bf16): its layer weights re-tiled once at init,
+  // and the split inputs its skinny products read
+  const bool bf = c->dtype == SPD_DTYPE_BF16;
+  const size_t qkv_rows = (size_t)(Hq + 2 * Hkv) * hd;
+  L.wtile = take(bf ? (size_t)c->pdm_layers * (qkv_rows * d + d * qd + 2 * (size_t)F * d + (size_t)d * F) * 2 : 0);
+  L.xs_h = scr(bf ? sizeof(uint16_t) * L.mr * (size_t)d : 0);
+  L.xs_l = scr(bf ? sizeof(uint16_t) * L.mr * (size_t)d : 0);
+  L.as_h = scr(bf ? sizeof(uint16_t) * L.mr * (size_t)F : 0);
+  L.as_l = scr(bf ? sizeof(uint16_t) * L.mr * (size_t)F : 0);
+  L.os_h = scr(bf ? sizeof(uint16_t) * L.mr * qd : 0);
+  L.os_l = scr(bf ? sizeof(uint16_t) * L.mr * qd : 0);
   // hybrid target: linear-attention state ring [L][nslots][Hkv][hd*hd + hd]
   // and its copy at the end of prefill [L][Hkv][hd*hd + hd]
   const size_t lin_one = (size_t)Hkv * ((size_t)hd * hd + hd);
@@ -278,6 +292,8 @@ struct spd_handle {
   ArgPair *parts, *pparts;
   spd_cycle_rec* ring;
   float *ssq_t, *ssq_p, *mpart;
+  uint16_t* wtile = nullptr;  // draft-module layer weights in tile order: per layer q/k/v, o, gate/up, down
+  uint16_t *xs_h = nullptr, *xs_l = nullptr, *as_h = nullptr, *as_l = nullptr, *os_h = nullptr, *os_l = nullptr;
   float *lin_state = nullptr, *lin_ckpt = nullptr;
   double *bsq = nullptr, *bsp = nullptr;  // dense sampling block sums (Q, P)
   double* zpart = nullptr;                 // draft tree: per-leaf softmax partial sums
@@ -480,7 +496,7 @@ void rows_linattn(spd_t* h, int layer, int M, int pos0, hipStream_t s) {
 // module's trailing rows); output fp32 rows r_o.
 template <typename WT>
 void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, int from_ctrl, int max_rows,
-                    bool merge, hipStream_t s) {
+                    bool merge, hipStream_t s, uint16_t* oh = nullptr, uint16_t* ol = nullptr) {
   const Geo& g = h->g;
   const int G = g.Hq / g.Hkv;
   Attn t;
@@ -493,6 +509,8 @@ void rows_attention(spd_t* h, void* kc, void* vc, int layer, int M, int pos0, in
   t.pacc = h->r_pacc;
   t.pml = h->r_pml;
   t.o = h->r_o;
+  t.oh = oh;
+  t.ol = ol;
   t.from_ctrl = from_ctrl;
   t.pos0_arg = pos0;
   t.nrows_arg = M;
@@ -743,6 +761,130 @@ int head_fixed(spd_t* h, const float* x, const void* W, const void* gamma, float
   return grid;
 }
 
+// ---- the draft module's products in the cycle on the skinny GEMV (bf16) ----
+// Tile-order copy of draft layer l's matrix `which` (0 q/k/v, 1 o, 2 gate/up,
+// 3 down) in the workspace, with its rows and inputs.
+uint16_t* pdm_wtile(spd_t* h, int l, int which, int* N, int* K) {
+  const Geo& g = h->g;
+  const size_t qd = (size_t)g.Hq * g.hd;
+  const size_t sz[4] = {(size_t)g.qkv_rows * g.d, (size_t)g.d * qd, 2 * (size_t)g.F * g.d, (size_t)g.d * g.F};
+  const int Ns[4] = {g.qkv_rows, g.d, 2 * g.F, g.d};
+  const int Ks[4] = {g.d, (int)qd, g.d, g.F};
+  size_t off = (size_t)l * (sz[0] + sz[1] + sz[2] + sz[3]);
+  for (int i = 0; i < which; ++i) off += sz[i];
+  *N = Ns[which];
+  *K = Ks[which];
+  return h->wtile + off;
+}
+
+// Re-tile every draft layer's matrices once (at init; the caller's draft-layer
+// buffers are not read by the cycle after this).
+void tile_pdm_weights(spd_t* h, hipStream_t s) {
+  const Geo& g = h->g;
+  for (int l = 0; l < g.Ls; ++l) {
+    const spd_layer_weights& lw = h->w.pdm[l];
+    const void* src[4] = {lw.w_qkv, lw.w_o, lw.w_gu, lw.w_down};
+    for (int i = 0; i < 4; ++i) {
+      int N, K;
+      uint16_t* dst = pdm_wtile(h, l, i, &N, &K);
+      const int NW = skinny_ways(N, K);
+      const uint16_t* w = (const uint16_t*)src[i];
+      const dim3 grid(1024), blk(kWG);
+      if (i == 0)
+        hipLaunchKernelGGL(k_tile_weights<EPI_QKV>, grid, blk, 0, s, w, dst, N, K, NW, g);
+      else if (i == 2)
+        hipLaunchKernelGGL(k_tile_weights<EPI_SWIGLU>, grid, blk, 0, s, w, dst, N, K, NW, g);
+      else
+        hipLaunchKernelGGL(k_tile_weights<EPI_RESID>, grid, blk, 0, s, w, dst, N, K, NW, g);
+    }
+  }
+}
+
+template <int EPI, int MT>
+void launch_skinny_mt(const SkinnyArgs& a, int NW, hipStream_t s) {
+  const dim3 grid(a.N / 16);
+  switch (NW) {
+    case 16: hipLaunchKernelGGL((k_skinny<EPI, MT, 16>), grid, dim3(16 * kWave), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_skinny<EPI, MT, 8>), grid, dim3(8 * kWave), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_skinny<EPI, MT, 4>), grid, dim3(4 * kWave), 0, s, a); break;
+  }
+}
+
+template <int EPI>
+void launch_skinny(spd_t* h, const SkinnyArgs& a, hipStream_t s) {
+  const int NW = skinny_ways(a.N, a.K);
+  if (pdm_rows(h->g) <= 16)
+    launch_skinny_mt<EPI, 1>(a, NW, s);
+  else
+    launch_skinny_mt<EPI, 2>(a, NW, s);
+}
+
+// One draft-module layer over the cycle's trailing rows (rows and positions
+// from the control block).  X = Xp in place; on entry xs holds the split of
+// attn_norm (.) X and ssq_p its partial sums of squares (ssq_parts per row).
+void pdm_layer_skinny(spd_t* h, int l, int ssq_parts, hipStream_t s) {
+  const Geo& g = h->g;
+  const spd_layer_weights& lw = h->w.pdm[l];
+  const int qd = g.Hq * g.hd;
+  SkinnyArgs a;
+  memset(&a, 0, sizeof(a));
+  a.layer = l;
+  a.kc = h->pkc;
+  a.vc = h->pvc;
+  a.rcos = h->rcos;
+  a.rsin = h->rsin;
+  a.anchor_idx = -1;
+  a.ctrl = h->ctrl;
+  a.g = g;
+  // norm + q/k/v + RoPE + cache append
+  a.Wt = pdm_wtile(h, l, 0, &a.N, &a.K);
+  a.xh = h->xs_h;
+  a.xl = h->xs_l;
+  a.ssq = h->ssq_p;
+  a.ssq_parts = ssq_parts;
+  a.out = h->r_q;
+  a.ldo = qd;
+  launch_skinny<EPI_QKV>(h, a, s);
+  // attention splits, merged into the split input of the o-projection
+  rows_attention<uint16_t>(h, h->pkc, h->pvc, l, 0, 0, 1, pdm_rows(g), true, s, h->os_h, h->os_l);
+  // o-projection + residual; hands over the split of ffn_norm (.) X
+  a.Wt = pdm_wtile(h, l, 1, &a.N, &a.K);
+  a.xh = h->os_h;
+  a.xl = h->os_l;
+  a.ssq = nullptr;
+  a.out = h->Xp;
+  a.ldo = g.d;
+  a.ssq_out = h->ssq_p;
+  a.yh = h->xs_h;
+  a.yl = h->xs_l;
+  a.ygamma = (const float*)lw.ffn_norm;
+  launch_skinny<EPI_RESID>(h, a, s);
+  // norm + gate/up + SwiGLU into the split input of the down projection
+  a.Wt = pdm_wtile(h, l, 2, &a.N, &a.K);
+  a.xh = h->xs_h;
+  a.xl = h->xs_l;
+  a.ssq = h->ssq_p;
+  a.ssq_parts = g.d / kSkinnyCols;
+  a.ssq_out = nullptr;
+  a.yh = h->as_h;
+  a.yl = h->as_l;
+  a.ygamma = nullptr;
+  launch_skinny<EPI_SWIGLU>(h, a, s);
+  // down + residual; hands over the split of the next layer's attn_norm (.) X
+  a.Wt = pdm_wtile(h, l, 3, &a.N, &a.K);
+  a.xh = h->as_h;
+  a.xl = h->as_l;
+  a.ssq = nullptr;
+  a.out = h->Xp;
+  a.ldo = g.d;
+  a.ssq_out = h->ssq_p;
+  const bool next = l + 1 < g.Ls;
+  a.yh = next ? h->xs_h : nullptr;
+  a.yl = next ? h->xs_l : nullptr;
+  a.ygamma = next ? (const float*)h->w.pdm[l + 1].attn_norm : nullptr;
+  launch_skinny<EPI_RESID>(h, a, s);
+}
+
 // Draft-module chain of one cycle (draft stream): anchor gather + FC, Ls
 // layers over the trailing rows, draft head, finalisation.
 template <typename WT>
@@ -766,6 +908,9 @@ int pdm_chain(spd_t* h, hipStream_t ps) {
       a.out = h->Xp;
       a.ldo = g.d;
       a.ssq_out = h->ssq_p;
+      a.yh = h->xs_h;
+      a.yl = h->xs_l;
+      a.ygamma = (const float*)w.pdm[0].attn_norm;
       launch_mfma<EPI_STORE>(h, a, g.m, pdm_rows(g), ps);
     } else {
       RowsGemv a = rows_base(h);
@@ -783,8 +928,12 @@ int pdm_chain(spd_t* h, hipStream_t ps) {
       a.slot_anchors = h->anchors;
       launch_rows<WT, EPI_STORE>(h, a, pdm_rows(g), ps);
     }
-    for (int l = 0; l < g.Ls; ++l)
-      layer_rows_any<WT>(h, true, w.pdm[l], h->pkc, h->pvc, l, h->Xp, h->ssq_p, 0, 0, 1, nullptr, nullptr, -1, ps);
+    for (int l = 0; l < g.Ls; ++l) {
+      if (sizeof(WT) == 2)
+        pdm_layer_skinny(h, l, l == 0 ? g.d / kSsqCols : g.d / kSkinnyCols, ps);
+      else
+        layer_rows_any<WT>(h, true, w.pdm[l], h->pkc, h->pvc, l, h->Xp, h->ssq_p, 0, 0, 1, nullptr, nullptr, -1, ps);
+    }
     StageGemv hd = stage_base(h);
     hd.W[0] = w.pdm_lm_head;
     hd.gamma[0] = (const float*)w.pdm_final_norm;
@@ -1490,6 +1639,15 @@ int init_handle(const spd_config* cfg, const spd_weights* w, char* ws, char* sc,
   h->ssq_t = (float*)(sc + L.ssq_t);
   h->ssq_p = (float*)(sc + L.ssq_p);
   h->mpart = (float*)(sc + L.mpart);
+  if (cfg->dtype == SPD_DTYPE_BF16) {
+    h->wtile = (uint16_t*)(ws + L.wtile);
+    h->xs_h = (uint16_t*)(sc + L.xs_h);
+    h->xs_l = (uint16_t*)(sc + L.xs_l);
+    h->as_h = (uint16_t*)(sc + L.as_h);
+    h->as_l = (uint16_t*)(sc + L.as_l);
+    h->os_h = (uint16_t*)(sc + L.os_h);
+    h->os_l = (uint16_t*)(sc + L.os_l);
+  }
   if (cfg->mode == SPD_MODE_SAMPLE && !cfg->top_k) {
     h->bsq = (double*)(sc + L.bsq);
     h->bsp = (double*)(sc + L.bsp);
@@ -1542,6 +1700,7 @@ int init_handle(const spd_config* cfg, const spd_weights* w, char* ws, char* sc,
   if ((e = attn_lds_limits()) != hipSuccess) return fail(e);
   hipLaunchKernelGGL(k_rope_table, dim3(512), dim3(256), 0, h->ss, h->rcos, h->rsin, L.ctx_cap, g.hd,
                      (double)cfg->rope_base);
+  if (h->wtile) tile_pdm_weights(h, h->ss);
   if ((e = hipGetLastError()) != hipSuccess) return fail(e);
   if ((e = hipEventRecord(h->ev_pdm, h->ps)) != hipSuccess) return fail(e);
   if ((e = hipStreamSynchronize(h->ss)) != hipSuccess) return fail(e);

@@ -69,6 +69,9 @@ struct MfmaArgs {
   float* out;                   // QKV: q rows; SWIGLU: activation rows; RESID/STORE: X rows
   int ldo;
   float* ssq_out;               // RESID/STORE: [row][N / kSsqCols] partial sums of squares of the result
+  uint16_t* yh;                 // RESID/STORE: split (bf16 hi + lo) of ygamma (.) result [row][N], or nullptr
+  uint16_t* yl;
+  const float* ygamma;          //   gain of the next consumer's norm (nullptr: the result itself)
   int layer;
   void* kc;
   void* vc;
@@ -190,6 +193,12 @@ __device__ __forceinline__ void mfma_epilogue_row(const MfmaArgs& A, int rg, int
       hn = v;
     }
     o[n] = hn;
+    if (A.yh) {
+      uint16_t hi, lo;
+      split_bf16(A.ygamma ? A.ygamma[n] * hn : hn, hi, lo);
+      A.yh[(size_t)orow * A.N + n] = hi;
+      A.yl[(size_t)orow * A.N + n] = lo;
+    }
     if (A.ssq_out) {
       const float sq = wave_sum(hn * hn);
       if (lane == 0) A.ssq_out[(size_t)orow * (A.N / kSsqCols) + rg] = sq;

@@ -48,9 +48,11 @@ def test_strerror_and_workspace_sizing_on_host():
     assert "state" in A.spd_strerror(A.SPD_ESTATE)
     w = si.workload("4b_n8")
     n = A.spd_workspace_bytes(make_config(w))
-    # KV caches (target + draft) dominate: (L + Ls) * 2 * Hkv * hd * ctx * 2 bytes
+    # KV caches (target + draft): (L + Ls) * 2 * Hkv * hd * ctx * 2 bytes, and the
+    # draft module's layer matrices in matrix-core tile order (Ls layers, bf16)
     kv = (w.L + w.Ls) * 2 * w.Hkv * w.hd * 1024 * 2
-    assert kv < n < kv * 3
+    tiles = w.Ls * ((w.Hq + 2 * w.Hkv) * w.hd * w.d + w.d * w.Hq * w.hd + 3 * w.F * w.d) * 2
+    assert kv + tiles < n < (kv + tiles) * 1.5
 
 
 @pytest.mark.parametrize("field,value", [
