@@ -108,6 +108,8 @@ def gpu_run(name: str) -> dict:
         sets = _topk_sets(eng, w, first, recs)
         sets[("pset_first", 0)] = first_set
         sets[("pval_first", 0)] = first_val
+    elif w.mode == "sample":
+        sets = _dense_logs(eng, w, first, recs)
     eng.close()
     del eng
     flat = si.weights_numpy_f32(T)
@@ -150,6 +152,43 @@ def _topk_sets(eng, w, first, recs):
     b["cycle"] -= b["cycle"][0]
     assert a.tobytes() == b.tobytes(), "cycle-by-cycle generation differs from the graph-launched one"
     return sets
+
+
+def _log_softmax64(l: np.ndarray, T: float) -> np.ndarray:
+    x = l.astype(np.float64) / T
+    m = x.max()
+    return x - m - np.log(np.sum(np.exp(x - m)))
+
+
+def _dense_logs(eng, w, first, recs):
+    """Dense sampling: the generation again, one cycle at a time, reading the
+    GPU's own log Q(x) of every cycle's draft x (from its draft logits) and
+    the log-softmax of its target logits at every exit (kept as the logits),
+    for the accept tests.  Its records must equal the first run's."""
+    eng.rollback(w.P, first)
+    logs = {}
+    out = []
+    while True:
+        buf = eng.enqueue(1)
+        st = eng.sync()
+        r = eng.records_of(buf)
+        if r["flags"][0] & IDLE:
+            break
+        c = len(out)
+        x = int(r["draft"][0])
+        if x >= 0:
+            logs[("qlog", c)] = float(_log_softmax64(eng.pdm_logits(), w.temperature)[x])
+        if r["exit_pos"][0] >= 0:
+            logs[("plogits", c)] = eng.logits().copy()
+        out.append(r)
+        if st.done:
+            break
+    again = np.concatenate(out)
+    a, b = recs.copy(), again.copy()
+    a["cycle"] -= a["cycle"][0]
+    b["cycle"] -= b["cycle"][0]
+    assert a.tobytes() == b.tobytes(), "cycle-by-cycle generation differs from the graph-launched one"
+    return logs
 
 
 def replay(run: dict):
@@ -341,7 +380,20 @@ def check_sampling(run: dict, view: OracleView, reps, chunk: int = 32, progress=
                 qw, qZ = sampling.softmax_weights(ql, T)
                 dec.sample(("draft", c2), qw, u_d)
                 pw, pZ = sampling.softmax_weights(pl, T)
-                if not dec.accept(("accept", i), pw, pZ, qw, qZ, x, u_a):
+                # the accept test u Q(x) < P(x) rests on two single probabilities, so
+                # the logit error at x does not average out as in a CDF: the GPU's
+                # decision must hold on its own log P(x) - log Q(x) (1e-6), and a
+                # differing oracle decision is adopted only if u lies between the
+                # oracle's ratio and the GPU's ([YB] 2.1)
+                lr_gpu = _log_softmax64(teacher[("plogits", i)], T)[x] - teacher[("qlog", c2)]
+                acc_g = u_a < np.exp(lr_gpu)
+                if acc_g != bool(recs[i]["accepted"]) and abs(u_a - np.exp(lr_gpu)) > 1e-6:
+                    own.mismatch.append((("accept", i), bool(recs[i]["accepted"]), bool(acc_g),
+                                         float(abs(u_a - np.exp(lr_gpu)))))
+                Px, Qx = float(pw[x]) / pZ, float(qw[x]) / qZ
+                shift = abs(np.exp(lr_gpu) - Px / Qx) if Qx > 0 else float("inf")
+                dec.lr_err = max(getattr(dec, "lr_err", 0.0), abs(lr_gpu - np.log(Px / Qx)) if Qx > 0 else 0.0)
+                if not dec.accept(("accept", i), pw, pZ, qw, qZ, x, u_a, tol=max(STOL[w.dtype], shift)):
                     dec.sample(("resample", i), sampling.residual(pw, pZ, qw, qZ), u_r)
                 continue
             Sq = dec.kept_set(("qset", c2), ql, k)

@@ -99,6 +99,11 @@ def test_full_size(name, part):
             print(f"{name}: {len(draws)} draws and {len(sets)} kept sets adopted; largest draw gap "
                   f"{max((a[3] for a in draws), default=0):.3g}, largest set gap "
                   f"{max((a[3] for a in sets), default=0):.3g}")
+            if not w.top_k:
+                print(f"{name}: largest GPU-vs-oracle difference of log P(x)/Q(x) at the accept tests "
+                      f"{getattr(dec, 'lr_err', 0.0):.3g}; {len(dec.own.mismatch)} accept tests that the GPU's "
+                      f"own ratio does not reproduce")
+                assert not dec.own.mismatch, dec.own.mismatch[:5]
             if w.top_k:
                 print(f"{name}: largest GPU-vs-oracle logit difference on the kept sets {dec.eps:.3g}; "
                       f"decisions retaken on the GPU's own logits: {len(dec.own.adopted)} within 1e-6, "
