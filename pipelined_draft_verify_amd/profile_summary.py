@@ -6,7 +6,7 @@
   python -m pipelined_draft_verify_amd.profile_summary mfma <counter_dir> [--cmd "..."]
 
 `timeline` takes K cycles of a kernel trace, ending --skip cycles before its
-end (a cycle starts at each k_entry dispatch), and prints, per stream and per kernel/grid, the launches,
+end (a cycle starts at each k_entry or k_tree_entry dispatch), and prints, per stream and per kernel/grid, the launches,
 average duration and time per cycle, plus each stream's busy time and the
 device-idle time (no kernel on any stream).
 
@@ -37,6 +37,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_gate_up_4b_n8.json")
 GU_REGEX = r"k_gemv_stage<unsigned short, 2[,>]"
+ENTRY_REGEX = r"k_(tree_)?entry<"  # the first kernel of every cycle (single chain or draft tree)
 COPY_REGEX = r"copy"
 SUM_REGEX = r"reduce_kernel"
 FILL_REGEX = r"FillFunctor"
@@ -74,7 +75,7 @@ def stats(path: str, top: int = 16) -> str:
 
 def timeline(path: str, cycles: int, skip: int = 0, top: int = 30) -> str:
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
-    ent = [i for i, r in enumerate(rows) if "k_entry" in r["Kernel_Name"]]
+    ent = [i for i, r in enumerate(rows) if re.search(ENTRY_REGEX, r["Kernel_Name"])]
     if len(ent) < cycles + skip:
         raise ValueError(f"trace has {len(ent)} cycles, fewer than {cycles + skip}")
     # cycles [-(cycles + skip), -skip) of the trace; host-side copies between
@@ -162,13 +163,15 @@ def _write_bytes(e):
 
 
 def cycle_kernels(w, sched):
-    """(label, kernel regex, grid or None, algorithmic bytes per dispatch) of
-    the cycle kernels of one step with the given schedule (per-cycle
-    occupancy and exit).  Stage kernels stream a * matrix per launch (one
-    launch per sub-step); the heads share one kernel instance (the draft head
-    every cycle, the verification head launched every cycle but streaming
-    only when a token exits); the draft module's products stream their matrix
-    once per launch."""
+    """(label, kernel regex, which, algorithmic bytes per dispatch) of the
+    cycle kernels of one step with the given schedule (per-cycle occupancy
+    and exit).  Stage kernels stream a * matrix per launch (one launch per
+    sub-step); the heads share one kernel instance (the draft head every
+    cycle, the verification head launched every cycle but streaming only when
+    a token exits); the draft module's products stream their matrix once per
+    launch -- its o-projection and down projection share one kernel instance
+    and grid and alternate within each layer (which = 0 / 1: the even / odd
+    dispatches of that instance)."""
     es = 2 if w.dtype == "bf16" else 4
     d, F, V = w.d, w.F, w.V
     qkv = (w.Hq + 2 * w.Hkv) * w.hd * d * es
@@ -184,10 +187,10 @@ def cycle_kernels(w, sched):
         ("stage gate/up", r"k_gemv_stage<[^,]+, 2, false", None, occ * wgu),
         ("stage down", r"k_gemv_stage<[^,]+, 1, true", None, occ * wdn),
         ("LM heads (draft every cycle, target on exit)", r"k_gemv_stage<[^,]+, 3, false", None, head),
-        ("draft gate/up", r"k_mfma_gemv<2, ", None, wgu),
-        ("draft o-projection", r"k_mfma_gemv<1, ", None, wo),
-        ("draft down", r"k_mfma_gemv<1, ", None, wdn),
-        ("draft q/k/v", r"k_mfma_gemv<0, ", None, qkv),
+        ("draft gate/up", r"k_skinny<2, ", None, wgu),
+        ("draft o-projection", r"k_skinny<1, ", 0, wo),
+        ("draft down", r"k_skinny<1, ", 1, wdn),
+        ("draft q/k/v", r"k_skinny<0, ", None, qkv),
     ]
     return ks
 
@@ -209,15 +212,11 @@ def traffic(read_dir: str, write_dir: str, sched_json: str):
         if cps:
             out[key] = max((fn(e) for e in cps), key=lambda v: v[0] if isinstance(v, tuple) else v)
     ids_r = sorted(rd)
-    first = next((i for i in ids_r if "k_entry" in rd[i]["name"]), 0)
-    # the mfma down projection and o-projection share an instance: the o-projection has the smaller grid
-    for label, rx, _, alg in cycle_kernels(w, sched):
+    first = next((i for i in ids_r if re.search(ENTRY_REGEX, rd[i]["name"])), 0)
+    for label, rx, which, alg in cycle_kernels(w, sched):
         sel = [i for i in ids_r if i >= first and re.search(rx, rd[i]["name"])]
-        if label in ("draft down", "draft o-projection"):
-            grids = sorted({rd[i]["grid"] for i in sel})
-            if grids:
-                g_ = grids[-1] if label == "draft down" else grids[0]
-                sel = [i for i in sel if rd[i]["grid"] == g_]
+        if which is not None:
+            sel = sel[which::2]
         if not sel:
             continue
         r_dram = sum(_read_bytes(rd[i])[0] for i in sel) / len(sel)

@@ -80,6 +80,7 @@ def test_traffic_per_kernel_and_copy_check(tmp_path):
     import seeded_inputs as si
     w = si.workload("4b_n8")
     copy = "__amd_rocclr_copyBuffer"
+    SK1 = "void spd::k_skinny<1, 1, 16>(spd::SkinnyArgs)"
     GIB = 1 << 30
     rd = [(1, copy, 100, {"TCC_EA0_RDREQ_DRAM_32B_sum": GIB / 32, "TCC_EA0_RDREQ_32B_sum": 0,
                           "TCC_EA0_RDREQ_64B_sum": 0, "TCC_EA0_RDREQ_128B_sum": GIB / 128}),
@@ -89,7 +90,12 @@ def test_traffic_per_kernel_and_copy_check(tmp_path):
           (4, GU, 7, {"TCC_EA0_RDREQ_DRAM_32B_sum": 1e6, "TCC_EA0_RDREQ_32B_sum": 2e5,
                       "TCC_EA0_RDREQ_64B_sum": 1e5, "TCC_EA0_RDREQ_128B_sum": 1e5}),
           (5, GU, 7, {"TCC_EA0_RDREQ_DRAM_32B_sum": 3e6, "TCC_EA0_RDREQ_32B_sum": 0,
-                      "TCC_EA0_RDREQ_64B_sum": 0, "TCC_EA0_RDREQ_128B_sum": 0})]
+                      "TCC_EA0_RDREQ_64B_sum": 0, "TCC_EA0_RDREQ_128B_sum": 0}),
+          # the draft o-projection and down projection: one instance, alternating
+          (6, SK1, 160, {"TCC_EA0_RDREQ_DRAM_32B_sum": 1e5}),
+          (7, SK1, 160, {"TCC_EA0_RDREQ_DRAM_32B_sum": 4e5}),
+          (8, SK1, 160, {"TCC_EA0_RDREQ_DRAM_32B_sum": 3e5}),
+          (9, SK1, 160, {"TCC_EA0_RDREQ_DRAM_32B_sum": 6e5})]
     red = "void at::native::reduce_kernel<512, 1, at::native::ReduceOp<float, at::native::func_wrapper_t<float, at::native::sum_functor<float, float, float>::operator()(at::TensorIterator&)::{lambda(float, float)#1}>, unsigned int, float, 4, 4> >(at::native::ReduceOp<float, at::native::func_wrapper_t<float, at::native::sum_functor<float, float, float>::operator()(at::TensorIterator&)::{lambda(float, float)#1}>, unsigned int, float, 4, 4>)"
     fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>, std::array<char*, 1ul> >(int, at::native::FillFunctor<float>, std::array<char*, 1ul>)"
     rd.insert(0, (0, red, 100, {"TCC_EA0_RDREQ_DRAM_32B_sum": GIB / 32 * 1.01, "TCC_EA0_RDREQ_32B_sum": 0,
@@ -117,6 +123,12 @@ def test_traffic_per_kernel_and_copy_check(tmp_path):
     assert gu["algorithmic_bytes"] == pytest.approx(6 * 2 * w.F * w.d * 2)  # mean occupancy 6
     assert rec["traffic_bytes_per_launch"] == pytest.approx(2e6 * 32 + 6 * 32 + 4 * 64)
     assert rec["source_hash"] == ps.kernel_source_hash()
+    o = next(k for k in rec["kernels"] if k["kernel"] == "draft o-projection")
+    dn = next(k for k in rec["kernels"] if k["kernel"] == "draft down")
+    assert o["dispatches"] == dn["dispatches"] == 2
+    assert o["read_dram_bytes"] == pytest.approx(2e5 * 32) and dn["read_dram_bytes"] == pytest.approx(5e5 * 32)
+    assert o["algorithmic_bytes"] == pytest.approx(w.Hq * w.hd * w.d * 2)
+    assert dn["algorithmic_bytes"] == pytest.approx(w.d * w.F * 2)
     assert "stage gate/up" in ps.traffic_table(rec)
 
 
