@@ -215,9 +215,11 @@ __global__ __launch_bounds__(kWG) void k_gemv_stage(const StageGemv A) {
   const long long Tt = (long long)n_act * tpg;
   // stage steps with few tokens in flight use a proportional share of the
   // grid (at least one workgroup per CU): the step takes about as long, and
-  // the draft stream's latency-bound kernels find free CUs
+  // the draft stream's latency-bound kernels find free CUs.  A draft tree's
+  // stage groups hold several rows (NR > 1): their GEMV is bound by its FMA
+  // issue rate, not by HBM, and takes the whole grid.
   int nwg = gridDim.x;
-  if (A.gmode == GM_STAGE)
+  if (A.gmode == GM_STAGE && NR == 1)
     nwg = max(min((int)gridDim.x, kStageMinWG), (int)((long long)gridDim.x * n_act / A.n_groups));
   if ((int)blockIdx.x >= nwg) return;
   const long long t0 = Tt * blockIdx.x / nwg;

@@ -27,12 +27,28 @@
 namespace spd {
 
 // ---- entry (A0/A1 for a tree) --------------------------------------------
+// The tree block staged in LDS for a kernel's serial bookkeeping: one
+// thread's chains of dependent reads (parent walks, rank tables) then pay LDS
+// latency instead of L2 latency.  Copied word by word by the workgroup.
+static_assert(sizeof(Tree) % 4 == 0, "the tree block is copied in 4-byte words");
+__device__ __forceinline__ void tree_copy(Tree* dst, const Tree* src) {
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+  for (int i = threadIdx.x; i < (int)(sizeof(Tree) / 4); i += blockDim.x) d[i] = s[i];
+}
+
 template <typename WT>
 __global__ __launch_bounds__(kWG) void k_tree_entry(Ctrl* C, const Geo g, int32_t* tokens, const WT* embed,
                                                     float* hslots, float* anchors, spd_cycle_rec* ring,
                                                     int log_cap) {
   __shared__ int s_n, s_slot[kMaxW], s_tok[kMaxW];
-  Tree* T = tree_of(C);
+  // the entry is the only kernel on the tree block while it runs (the previous
+  // cycle's streams are joined): it works on an LDS copy and writes it back
+  __shared__ Tree sT;
+  Tree* TG = tree_of(C);
+  tree_copy(&sT, TG);
+  __syncthreads();
+  Tree* T = &sT;
   const int W = g.W, ns = g.nslots;
   if (threadIdx.x == 0) {
     const int cyc = C->launches;
@@ -236,6 +252,7 @@ __global__ __launch_bounds__(kWG) void k_tree_entry(Ctrl* C, const Geo g, int32_
     }
   }
   __syncthreads();
+  tree_copy(TG, &sT);
   {
     spd_cycle_rec* r = ring + C->rec_slot;
     for (int l = threadIdx.x; l < SPD_MAX_LAYERS; l += kWG) r->kv_len[l] = 0;
@@ -303,6 +320,14 @@ __global__ __launch_bounds__(kCtlThreads) void k_tree_verify(const TreeVerifyArg
     for (int l = threadIdx.x; l < g.L; l += kCtlThreads) rec->kv_len[l] = A.kv_len[l];
     return;
   }
+  // the draft stream's finalisation may write the candidate fields meanwhile:
+  // work on an LDS copy and write back only the counts, the rank tables and
+  // the last exit
+  __shared__ Tree sT;
+  Tree* TG = T;
+  tree_copy(&sT, TG);
+  __syncthreads();
+  T = &sT;
   const int j = C->t - (g.n - 1);
   const int ex = T->exit_slot;
   const ArgPair best = block_argmax_parts(A.parts, A.nparts, sh_ap);
@@ -357,7 +382,7 @@ __global__ __launch_bounds__(kCtlThreads) void k_tree_verify(const TreeVerifyArg
     } else {
       // (ii) flush the tree and (iii) re-seed stage 0
       for (int ps = 0; ps < ns; ++ps) T->cnt[ps] = 0;
-      T->ncand = 0;
+      TG->ncand = 0;
       C->reseed = 1;
       C->seed_tok = y;
       C->seed_pos = j + 1;
@@ -379,6 +404,12 @@ __global__ __launch_bounds__(kCtlThreads) void k_tree_verify(const TreeVerifyArg
     rec->flags |= C->flags;
   }
   __syncthreads();
+  for (int i = threadIdx.x; i < ns; i += kCtlThreads) {
+    TG->cnt[i] = sT.cnt[i];
+#pragma unroll
+    for (int k = 0; k < kMaxW; ++k) TG->rk[i][k] = sT.rk[i][k];
+  }
+  if (threadIdx.x == 0) TG->last_exit = sT.last_exit;
   for (int l = threadIdx.x; l < g.L; l += kCtlThreads) rec->kv_len[l] = A.kv_len[l];
 }
 
@@ -399,10 +430,12 @@ struct TreeScanArgs {
   Geo g;
 };
 
-__device__ __forceinline__ float parts_max(const ArgPair* p, int n) {
+// Largest value among n per-workgroup partials, by the 64 lanes of one wave
+// (every lane returns it).
+__device__ __forceinline__ float parts_max_wave(const ArgPair* p, int n) {
   float m = -INFINITY;
-  for (int k = 0; k < n; ++k) m = fmaxf(m, p[k].v);
-  return m;
+  for (int k = threadIdx.x & (kWave - 1); k < n; k += kWave) m = fmaxf(m, p[k].v);
+  return wave_max(m);
 }
 
 // grid (blocks, W): block b of leaf m takes ids [b * kTreeScanBlk, ...)
@@ -415,7 +448,10 @@ __global__ __launch_bounds__(kWG) void k_tree_scan(const TreeScanArgs A) {
   const int m = blockIdx.y, W = g.W;
   if (!C->active || m >= tree_of(C)->nleaves) return;
   const float* l = A.logits + (size_t)m * g.V;
-  if (threadIdx.x == 0) s_max = parts_max(A.parts + (size_t)m * A.nparts, A.nparts);
+  if (threadIdx.x < kWave) {
+    const float mx = parts_max_wave(A.parts + (size_t)m * A.nparts, A.nparts);
+    if (threadIdx.x == 0) s_max = mx;
+  }
   __syncthreads();
   const double M = s_max;
   // each thread: its ids' exp sum (fp64) and its own best W (value desc, id asc)
@@ -490,23 +526,78 @@ struct TreeFinalizeArgs {
 
 __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs A) {
   Ctrl* C = A.ctrl;
-  Tree* T = tree_of(C);
+  Tree* TG = tree_of(C);
   const Geo& g = A.g;
   const int W = g.W, ns = g.nslots;
-  if (!C->active || threadIdx.x != 0) return;
+  if (!C->active) return;
+  // reads from an LDS copy (the stage stream's verification may update the
+  // counts and rank tables meanwhile; nothing read here changes); the
+  // candidates are written to the tree block itself
+  __shared__ Tree sT;
+  tree_copy(&sT, TG);
+  __syncthreads();
+  const Tree* T = &sT;
   const int t = C->t, oldest = t - C->a + 1, nl = T->nleaves;
-  // per leaf: max, log normaliser, path score, best W tokens
+  // per leaf, by the whole wave: the max logit (over the head's per-workgroup
+  // partials), the normaliser (the scan blocks' sums; lane-strided, then a
+  // fixed butterfly) and the best W tokens (each lane's best W of its share of
+  // the blocks' lists, then W rounds of a wave argmax)
+  const int lane = threadIdx.x;
+  __shared__ double s_lM[kMaxW], s_lZ[kMaxW];
+  __shared__ float s_bv[kMaxW][kMaxW];
+  __shared__ int s_bi[kMaxW][kMaxW];
+  for (int m = 0; m < nl; ++m) {
+    const float mx = parts_max_wave(A.parts + (size_t)m * A.nparts, A.nparts);
+    double z = 0.0;
+    for (int b = lane; b < A.nblk; b += kWave) z += A.zpart[(size_t)m * A.nblk + b];
+    z = wave_sum_d(z);
+    float tv[kMaxW];
+    int ti[kMaxW];
+    for (int k = 0; k < kMaxW; ++k) {
+      tv[k] = -INFINITY;
+      ti[k] = 0x7FFFFFFF;
+    }
+    for (int e = lane; e < A.nblk * W; e += kWave) {
+      const ArgPair c = A.tpart[(size_t)m * A.nblk * W + e];
+      if (!better(c.v, c.i, tv[W - 1], ti[W - 1])) continue;
+      int q = W - 1;
+      while (q > 0 && better(c.v, c.i, tv[q - 1], ti[q - 1])) {
+        tv[q] = tv[q - 1];
+        ti[q] = ti[q - 1];
+        --q;
+      }
+      tv[q] = c.v;
+      ti[q] = c.i;
+    }
+    int head = 0;
+    for (int k = 0; k < W; ++k) {
+      const float v = head < W ? tv[head] : -INFINITY;
+      const int i = head < W ? ti[head] : 0x7FFFFFFF;
+      float bv = v;
+      int bi = i;
+      wave_argmax(bv, bi);
+      if (lane == 0) {
+        s_bv[m][k] = bv;
+        s_bi[m][k] = bi;
+      }
+      if (head < W && i == bi && v == bv) ++head;  // ids are unique: only the owner advances
+    }
+    if (lane == 0) {
+      s_lM[m] = mx;
+      s_lZ[m] = log(z);
+    }
+  }
+  __syncthreads();
+  if (lane != 0) return;
+  // candidates, ranking and the forced policy: one thread
   int cl[kMaxCand], ct[kMaxCand], crank[kMaxCand];
   double cs[kMaxCand], clq[kMaxCand];
   int nc = 0;
   double lM[kMaxW], lZ[kMaxW], cum[kMaxW];
   int lslot[kMaxW], top0 = -1;
   for (int m = 0; m < nl; ++m) {
-    const ArgPair* pp = A.parts + (size_t)m * A.nparts;
-    lM[m] = parts_max(pp, A.nparts);
-    double Z = 0.0;
-    for (int b = 0; b < A.nblk; ++b) Z += A.zpart[(size_t)m * A.nblk + b];
-    lZ[m] = log(Z);
+    lM[m] = s_lM[m];
+    lZ[m] = s_lZ[m];
     const int sl = T->row_slot[T->nrows - nl + m];
     lslot[m] = sl;
     // cum: log Q over the path above the oldest position, in position order
@@ -519,31 +610,11 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
     double s = 0.0;
     for (int k = np - 1; k >= 0; --k) s += lqs[k];
     cum[m] = s;
-    // merge the blocks' top-W lists
-    float bv[kMaxW];
-    int bi[kMaxW];
+    if (m == 0) top0 = s_bi[0][0];
     for (int k = 0; k < W; ++k) {
-      bv[k] = -INFINITY;
-      bi[k] = 0x7FFFFFFF;
-    }
-    for (int b = 0; b < A.nblk; ++b)
-      for (int k = 0; k < W; ++k) {
-        const ArgPair c = A.tpart[((size_t)m * A.nblk + b) * W + k];
-        if (!better(c.v, c.i, bv[W - 1], bi[W - 1])) continue;
-        int q = W - 1;
-        while (q > 0 && better(c.v, c.i, bv[q - 1], bi[q - 1])) {
-          bv[q] = bv[q - 1];
-          bi[q] = bi[q - 1];
-          --q;
-        }
-        bv[q] = c.v;
-        bi[q] = c.i;
-      }
-    if (m == 0) top0 = bi[0];
-    for (int k = 0; k < W; ++k) {
-      const double lq = (double)bv[k] - lM[m] - lZ[m];
+      const double lq = (double)s_bv[m][k] - lM[m] - lZ[m];
       cl[nc] = sl;
-      ct[nc] = bi[k];
+      ct[nc] = s_bi[m][k];
       crank[nc] = m;
       clq[nc] = lq;
       cs[nc] = cum[m] + lq;
@@ -648,11 +719,11 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
       }
     }
   }
-  T->ncand = nc;
+  TG->ncand = nc;
   for (int i = 0; i < nc; ++i) {
-    T->cand_leaf[i] = cl[i];
-    T->cand_tok[i] = ct[i];
-    T->cand_lq[i] = clq[i];
+    TG->cand_leaf[i] = cl[i];
+    TG->cand_tok[i] = ct[i];
+    TG->cand_lq[i] = clq[i];
   }
   C->r_draft = ct[0];
   C->r_raw = top0;

@@ -10,10 +10,12 @@
   * a generation of one token (prefill only: the cycles that follow are
     idle) and of two (one verification);
   * an empty prompt is refused;
-  * the longest context (max_ctx = 32768: 128 attention splits): the oracle
-    cannot attend over 32k positions in seconds, so the check is a property
-    that holds at any size -- natural and forced drafts emit exactly the
-    GPU's own autoregressive greedy decode;
+  * the longest context (max_ctx = 32768: 128 attention splits): natural and
+    forced drafts emit exactly the GPU's own autoregressive greedy decode (a
+    property that holds at any size), and the oracle's forward over the
+    final ~32k-token sequence (matrix form, about a minute on the host) checks
+    the first token and every verification's target token, and the last
+    verification's logits;
   * the largest vocabulary (SPD_MAX_VOCAB = 2^20 ids) in sample mode, dense
     and with top-64 truncation, and the smallest (2 and 3 ids).
 Every run through the oracle must agree cycle by cycle as in the other
@@ -120,7 +122,30 @@ def test_longest_context_is_lossless():
         ex = recs[recs["exit_pos"] >= 0]
         assert len(ex) == G - 1 and int(ex["exit_pos"][-1]) == P + G - 2
         assert int(recs["t"].max()) < w.max_ctx
+    toks = [int(x) for x in eng.tokens(0, P + G)]
+    last_logits = eng.logits()
     eng.close()
+    # the oracle's target forward over the final sequence (positions 0 .. P+G-2)
+    from oracle.model import Target
+    from oracle.spd import Decisions
+    from tests.full_size import rel_l2
+
+    W = si.nest_weights(si.weights_numpy_f32(T), w)
+    del T
+    tgt = Target(w, W)
+    H, _ = tgt.prefill_matrix(toks[: P + G - 1], all_rows=True)
+    LG = tgt.logits_rows(H[P - 1:])
+    del H
+    teacher = {("y", j): toks[j + 1] for j in range(P - 1, P + G - 1)}
+    dec = Decisions(teacher, 0.05)
+    for j in range(P - 1, P + G - 1):
+        dec.argmax(("y", j), LG[j - (P - 1)])
+    print(f"longest context: {G} target tokens checked against the oracle, {len(dec.adopted)} near-ties adopted")
+    assert not dec.mismatch, dec.mismatch[:5]
+    assert len(dec.adopted) <= 2
+    err = rel_l2(last_logits, LG[-1])
+    print(f"longest context: last verification logits rel-L2 {err:.3g}")
+    assert err <= 2e-2
 
 
 @pytest.mark.parametrize("top_k", [0, 64])

@@ -8,7 +8,9 @@ event edge, or a kernel that reads state the other stream is writing, makes
 the overlapped run differ from the one where the draft chain runs alone on
 the stage stream ahead of the stage step (SPD_LAUNCH_SERIALIZED).  Both runs
 use graph launch and enqueue a whole generation before the first wait, so
-nothing but the event edges orders the two streams.  Compared: every cycle
+nothing but the event edges orders the two streams.  Draft trees are
+included: there the draft stream's finalisation writes the next entry's
+candidates while the stage stream's verification prunes the tree.  Compared: every cycle
 record, the token sequence, the last verification's logits, the last draft
 logits, the anchors of the last in-flight tokens and every target layer's
 KV cache.
@@ -43,13 +45,15 @@ def _generation(eng, w, first):
     return state, len(recs)
 
 
-def _compare(w, T, uni=None, ref=None, p=None):
+def _compare(w, T, uni=None, ref=None, p=None, tree=None):
     from pipelined_draft_verify_amd import SPDEngine
 
     eng = SPDEngine(w, T)
     if uni is not None:
         eng.set_uniforms(uni)
-    if ref is not None:
+    if ref is not None and tree is not None:
+        eng.set_tree_forced(ref, *tree)
+    elif ref is not None:
         eng.set_forced(ref, p)
     first = int(eng.prefill(si.make_prompt(w)))
     # cycle count of this generation, from a first (overlapped) run
@@ -79,6 +83,11 @@ SMALL = {
     "f32_sample_topk12": dict(dtype="f32", mode="sample", top_k=12, V=40, G=30, seed=74),
     "bf16_hybrid_forced": dict(dtype="bf16", L=8, n=4, Ls=2, anchors=[0, 2, 4, 8], attn_period=4, G=30,
                                seed=75),
+    # draft trees: the draft stream's finalisation writes the candidates while
+    # the stage stream's verification prunes the tree
+    "bf16_tree_w4_forced": dict(dtype="bf16", L=8, n=4, Hq=8, Hkv=2, F=768, V=500, anchors=[0, 2, 4, 8], Ls=2,
+                                width=4, G=30, seed=76),
+    "f32_tree_w3_natural": dict(dtype="f32", L=4, n=4, anchors=[0, 1, 2, 3, 4], width=3, G=30, seed=77),
 }
 
 
@@ -88,12 +97,13 @@ def test_overlapped_equals_serialized_small(name):
     w = si.workload("tiny_fp32", G=40) if kw is None else gpu_workload_tiny(**kw)
     T = si.make_weights(w, "cpu")
     uni = si.make_uniforms(w)
-    ref = p = None
-    if kw is not None and w.mode == "greedy":
+    ref = p = tree = None
+    if kw is not None and w.mode == "greedy" and not name.endswith("natural"):
         W = si.nest_weights(si.weights_numpy_f32(T), w)
         ref, _ = ar_greedy(w, W, si.make_prompt(w), w.G)
         p = 0.6
-    ncyc = _compare(w, {k: v.to("cuda:0") for k, v in T.items()}, uni=uni, ref=ref, p=p)
+        tree = (0.3, 0.8) if w.width > 1 else None
+    ncyc = _compare(w, {k: v.to("cuda:0") for k, v in T.items()}, uni=uni, ref=ref, p=p, tree=tree)
     print(f"{name}: {ncyc} cycles bit-identical overlapped and serialized")
 
 
@@ -115,5 +125,27 @@ def test_overlapped_equals_serialized_full_size_4b_n8():
     del eng
     ncyc = _compare(w, T, uni=uni, ref=ref, p=w.p_accept)
     print(f"4b_n8: {ncyc} cycles bit-identical overlapped and serialized")
+    del T
+    torch.cuda.empty_cache()
+
+
+def test_overlapped_equals_serialized_full_size_tree():
+    """The width-4 draft tree on the 4B-class shapes (n = 8, forced tree policy)."""
+    import torch
+    from pipelined_draft_verify_amd import SPDEngine
+
+    w = si.workload("4b_tree4_n8")
+    T = si.make_weights(w, "cuda:0")
+    uni = si.make_uniforms(w)
+    eng = SPDEngine(w, T)
+    eng.set_uniforms(uni)
+    prompt = si.make_prompt(w)
+    first = int(eng.prefill(prompt))
+    ar = eng.generate_ar(w.G - 1)
+    ref = [int(x) for x in prompt] + [first] + [int(x) for x in ar]
+    eng.close()
+    del eng
+    ncyc = _compare(w, T, uni=uni, ref=ref, tree=(w.p_accept, w.p_tree))
+    print(f"4b_tree4_n8: {ncyc} cycles bit-identical overlapped and serialized")
     del T
     torch.cuda.empty_cache()
