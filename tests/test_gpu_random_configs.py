@@ -5,7 +5,10 @@ uniform or uneven stage split, draft-module depth, anchor set, head layout,
 vocabulary, greedy with forced drafts or temperature sampling (optionally
 top-k), pre- or post-step drafting, hybrid linear-attention layers -- and must
 agree with the oracle cycle by cycle as in the hand-picked small variants.
-The point is the combinations no single variant covers.  Three medium cases
+Sixteen more cases draw draft-tree configurations (width 2-4, up to eight
+stages, forced tree policies or the draft module's own drafts) and follow
+the tree oracle cycle by cycle.  The point is the combinations no single
+variant covers.  Three medium cases
 (widths 1024-2048, prompts of 260-620 tokens, vocabularies up to 32000) add
 several tiles per stage group and multi-split attention.
 """
@@ -106,3 +109,44 @@ def test_random_configuration_matches_oracle(kind, i):
     assert len(o.dec.adopted) <= 2, o.dec.adopted
     assert toks == otoks
     compare_logs(recs, ologs, w.L)
+
+
+# ---- draft trees ----------------------------------------------------------
+N_TREE_CASES = 16
+
+
+def _draw_tree(i):
+    """A random draft-tree configuration (greedy, pre-step, uniform stages,
+    2 + (n - 1) W <= 32 draft-module rows), with a forced tree policy or the
+    draft module's own drafts."""
+    rng = np.random.default_rng(7000 + i)
+    while True:
+        n = int(rng.choice([2, 3, 4, 6, 8]))
+        Wd = int(rng.choice([2, 3, 4]))
+        if 2 + (n - 1) * Wd <= 32:
+            break
+    L = n * int(rng.integers(1, 3))
+    Ls = int(rng.integers(1, L // n + 1))
+    inner = sorted(set(int(b) for b in rng.integers(1, L + 1, size=int(rng.integers(0, 4)))))
+    Hq, Hkv, hd = [(4, 2, 64), (4, 4, 64), (8, 2, 64), (2, 1, 128), (4, 1, 128)][int(rng.integers(0, 5))]
+    kw = dict(dtype=str(rng.choice(["f32", "bf16"])), L=L, n=n, Ls=Ls, anchors=[0] + inner[:7], Hq=Hq, Hkv=Hkv,
+              hd=hd, d=int(rng.choice([256, 512])), F=int(rng.choice([512, 768])),
+              V=int(rng.choice([300, 997, 2048])), P=int(rng.integers(5, 41)), G=int(rng.integers(10, 25)),
+              seed=700 + i, width=Wd)
+    if rng.random() < 0.25:
+        return kw, None, None
+    return kw, float(rng.choice([0.0, 0.3, 0.5])), float(rng.choice([0.6, 0.85]))
+
+
+@pytest.mark.parametrize("i", range(N_TREE_CASES))
+def test_random_tree_configuration_matches_oracle(i):
+    from tests.test_gpu_tree import run_and_compare
+
+    kw, p1, pW = _draw_tree(i)
+    print("tree case", i, kw, "p1", p1, "pW", pW, flush=True)
+    w = gpu_workload_tiny(**kw)
+    T, W, prompt, uni = _inputs(w)
+    ref, _ = ar_greedy(w, W, prompt, w.G)
+    recs, ologs, o = run_and_compare(w, T, W, prompt, uni, ref, p1, pW)
+    assert len(o.adopted) <= 3, o.adopted
+    assert recs["n_new"].max() >= 2  # the tree widens
