@@ -16,7 +16,8 @@ for DRAM; a 64-byte request counts 2, a 128-byte one 4) with the 32/64/128-byte
 request counts TCC_EA0_RDREQ_{32B,64B,128B}_sum; writes: TCC_EA0_WRREQ_sum and
 TCC_EA0_WRREQ_64B_sum (32- or 64-byte requests) -- checks them on plain
 dispatches of known size (a sum over 1 GiB reads it once, a fill of 1 GiB
-writes it once, a 1 GiB copy does both), and prints, per cycle kernel, the
+writes it once, the runtime's 1 GiB copy and an elementwise one do both), and
+prints, per cycle kernel, the
 counted bytes per dispatch against the algorithmic bytes per dispatch of the
 step's schedule (bench.py --dump-schedule).  The gate/up record (with a hash
 of the kernel sources) feeds bench.py's roofline `traffic`, reported only
@@ -40,6 +41,7 @@ GU_REGEX = r"k_gemv_stage<unsigned short, 2[,>]"
 ENTRY_REGEX = r"k_(tree_)?entry<"  # the first kernel of every cycle (single chain or draft tree)
 COPY_REGEX = r"copy"
 SUM_REGEX = r"reduce_kernel"
+ECOPY_REGEX = r"MulFunctor"  # the elementwise copy x * 1
 FILL_REGEX = r"FillFunctor"
 COPY_BYTES = 1 << 30
 
@@ -207,7 +209,9 @@ def traffic(read_dir: str, write_dir: str, sched_json: str):
     out = {"workload": w.name, "source_hash": kernel_source_hash(), "kernels": []}
     # calibration dispatches (before the cycles): the largest one of each kind
     for key, per, fn, rx in (("copy_read", rd, _read_bytes, COPY_REGEX), ("copy_write", wr, _write_bytes, COPY_REGEX),
-                             ("sum_read", rd, _read_bytes, SUM_REGEX), ("fill_write", wr, _write_bytes, FILL_REGEX)):
+                             ("sum_read", rd, _read_bytes, SUM_REGEX), ("fill_write", wr, _write_bytes, FILL_REGEX),
+                             ("ecopy_read", rd, _read_bytes, ECOPY_REGEX),
+                             ("ecopy_write", wr, _write_bytes, ECOPY_REGEX)):
         cps = [e for e in per.values() if re.search(rx, e["name"])]
         if cps:
             out[key] = max((fn(e) for e in cps), key=lambda v: v[0] if isinstance(v, tuple) else v)
@@ -240,6 +244,10 @@ def traffic_table(rec) -> str:
         lines.append(f"calibration sum over 1 GiB: DRAM reads {sr[0] / COPY_BYTES:.3f}x, all reads "
                      f"{sr[1] / COPY_BYTES:.3f}x; fill of 1 GiB: writes {(fw or 0) / COPY_BYTES:.3f}x of the known bytes"
                      if sr else f"calibration fill of 1 GiB: writes {(fw or 0) / COPY_BYTES:.3f}x of the known bytes")
+    er, ew = rec.get("ecopy_read"), rec.get("ecopy_write")
+    if er:
+        lines.append(f"calibration elementwise copy (1 GiB read + 1 GiB written): DRAM reads {er[0] / COPY_BYTES:.3f}x, "
+                     f"all reads {er[1] / COPY_BYTES:.3f}x, writes {(ew or 0) / COPY_BYTES:.3f}x of the known bytes")
     cr, cw = rec.get("copy_read"), rec.get("copy_write")
     if cr:
         lines.append(f"calibration copy (1 GiB read + 1 GiB written): DRAM reads {cr[0] / COPY_BYTES:.3f}x, "

@@ -100,7 +100,11 @@ def test_traffic_per_kernel_and_copy_check(tmp_path):
     fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>, std::array<char*, 1ul> >(int, at::native::FillFunctor<float>, std::array<char*, 1ul>)"
     rd.insert(0, (0, red, 100, {"TCC_EA0_RDREQ_DRAM_32B_sum": GIB / 32 * 1.01, "TCC_EA0_RDREQ_32B_sum": 0,
                                "TCC_EA0_RDREQ_64B_sum": GIB / 64, "TCC_EA0_RDREQ_128B_sum": 0}))
+    mul = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<float, float, float, at::native::binary_internal::MulFunctor<float> >, std::array<char*, 2ul> >(int, at::native::AUnaryFunctor<float, float, float, at::native::binary_internal::MulFunctor<float> >, std::array<char*, 2ul>)"
+    rd.insert(1, (-1, mul, 100, {"TCC_EA0_RDREQ_DRAM_32B_sum": GIB / 32, "TCC_EA0_RDREQ_32B_sum": 0,
+                               "TCC_EA0_RDREQ_64B_sum": 0, "TCC_EA0_RDREQ_128B_sum": GIB / 128}))
     wr = [(0, fill, 100, {"TCC_EA0_WRREQ_sum": GIB / 64, "TCC_EA0_WRREQ_64B_sum": GIB / 128}),
+          (-1, mul, 100, {"TCC_EA0_WRREQ_sum": GIB / 64, "TCC_EA0_WRREQ_64B_sum": GIB / 64}),
           (1, copy, 100, {"TCC_EA0_WRREQ_sum": GIB / 64, "TCC_EA0_WRREQ_64B_sum": GIB / 64}),
           (4, GU, 7, {"TCC_EA0_WRREQ_sum": 10, "TCC_EA0_WRREQ_64B_sum": 4}),
           (5, GU, 7, {"TCC_EA0_WRREQ_sum": 10, "TCC_EA0_WRREQ_64B_sum": 4})]
@@ -113,7 +117,9 @@ def test_traffic_per_kernel_and_copy_check(tmp_path):
     assert rec["copy_write"] == pytest.approx(GIB)
     assert rec["sum_read"][0] == pytest.approx(1.01 * GIB) and rec["sum_read"][1] == pytest.approx(GIB)
     assert rec["fill_write"] == pytest.approx(GIB * 0.75)  # half the requests 32-byte, half 64-byte
+    assert rec["ecopy_read"][0] == pytest.approx(GIB) and rec["ecopy_write"] == pytest.approx(GIB)
     table = ps.traffic_table(rec)
+    assert "elementwise copy (1 GiB read + 1 GiB written): DRAM reads 1.000x" in table
     assert "sum over 1 GiB: DRAM reads 1.010x" in table and "writes 0.750x" in table
     gu = next(k for k in rec["kernels"] if k["kernel"] == "stage gate/up")
     assert gu["dispatches"] == 2
