@@ -129,12 +129,11 @@ def main():
     torch.cuda.synchronize()
     log(f"weights generated on GPU in {time.time() - t0:.1f}s")
     # dispatches of known HBM traffic that the traffic counters are checked
-    # on: a 1 GiB fill (writes), a sum over it (reads), the runtime's 1 GiB
-    # copy and a plain elementwise 1 GiB copy (x * 1: reads and writes)
+    # on: a 1 GiB fill (writes), a sum over it (reads) and an elementwise
+    # 1 GiB copy (x * 1: reads and writes), issued last before the engine
     calib_src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
     calib_sum = calib_src.sum()
     calib_dst = torch.empty_like(calib_src)
-    calib_dst.copy_(calib_src)
     torch.mul(calib_src, 1.0, out=calib_dst)
     torch.cuda.synchronize()
     assert float(calib_sum) == float(1 << 28)

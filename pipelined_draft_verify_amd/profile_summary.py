@@ -16,8 +16,8 @@ for DRAM; a 64-byte request counts 2, a 128-byte one 4) with the 32/64/128-byte
 request counts TCC_EA0_RDREQ_{32B,64B,128B}_sum; writes: TCC_EA0_WRREQ_sum and
 TCC_EA0_WRREQ_64B_sum (32- or 64-byte requests) -- checks them on plain
 dispatches of known size (a sum over 1 GiB reads it once, a fill of 1 GiB
-writes it once, the runtime's 1 GiB copy and an elementwise one do both), and
-prints, per cycle kernel, the
+writes it once, an elementwise 1 GiB copy does both), and prints, per cycle
+kernel, the
 counted bytes per dispatch against the algorithmic bytes per dispatch of the
 step's schedule (bench.py --dump-schedule).  The gate/up record (with a hash
 of the kernel sources) feeds bench.py's roofline `traffic`, reported only
@@ -39,7 +39,6 @@ ROOT = os.path.dirname(HERE)
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_gate_up_4b_n8.json")
 GU_REGEX = r"k_gemv_stage<unsigned short, 2[,>]"
 ENTRY_REGEX = r"k_(tree_)?entry<"  # the first kernel of every cycle (single chain or draft tree)
-COPY_REGEX = r"copy"
 SUM_REGEX = r"reduce_kernel"
 ECOPY_REGEX = r"MulFunctor"  # the elementwise copy x * 1
 FILL_REGEX = r"FillFunctor"
@@ -133,12 +132,6 @@ def counter_avg(d: str, counter: str, regex: str):
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
-def copy_reading(d: str, counter: str):
-    """Counter value of the 1 GiB calibration copy: by far the largest copy dispatch."""
-    vals = counter_values(d, counter, COPY_REGEX)
-    return max(vals) if vals else None
-
-
 RD_COUNTERS = ("TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
                "TCC_EA0_RDREQ_128B_sum")
 WR_COUNTERS = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")
@@ -207,14 +200,18 @@ def traffic(read_dir: str, write_dir: str, sched_json: str):
     sched = sc["cycles"]
     rd, wr = _per_dispatch(read_dir), _per_dispatch(write_dir)
     out = {"workload": w.name, "source_hash": kernel_source_hash(), "kernels": []}
-    # calibration dispatches (before the cycles): the largest one of each kind
-    for key, per, fn, rx in (("copy_read", rd, _read_bytes, COPY_REGEX), ("copy_write", wr, _write_bytes, COPY_REGEX),
-                             ("sum_read", rd, _read_bytes, SUM_REGEX), ("fill_write", wr, _write_bytes, FILL_REGEX),
+    # calibration dispatches: bench.py issues them after generating the
+    # weights (whose own fills, scalings and copies match the same kernel
+    # names) and before the engine's first kernel -- the last dispatch of each
+    # kind before the first spd:: kernel
+    for key, per, fn, rx in (("sum_read", rd, _read_bytes, SUM_REGEX), ("fill_write", wr, _write_bytes, FILL_REGEX),
                              ("ecopy_read", rd, _read_bytes, ECOPY_REGEX),
                              ("ecopy_write", wr, _write_bytes, ECOPY_REGEX)):
-        cps = [e for e in per.values() if re.search(rx, e["name"])]
+        ids = sorted(per)
+        eng0 = next((i for i in ids if "spd::" in per[i]["name"]), None)
+        cps = [i for i in ids if (eng0 is None or i < eng0) and re.search(rx, per[i]["name"])]
         if cps:
-            out[key] = max((fn(e) for e in cps), key=lambda v: v[0] if isinstance(v, tuple) else v)
+            out[key] = fn(per[cps[-1]])
     ids_r = sorted(rd)
     first = next((i for i in ids_r if re.search(ENTRY_REGEX, rd[i]["name"])), 0)
     for label, rx, which, alg in cycle_kernels(w, sched):
@@ -248,11 +245,6 @@ def traffic_table(rec) -> str:
     if er:
         lines.append(f"calibration elementwise copy (1 GiB read + 1 GiB written): DRAM reads {er[0] / COPY_BYTES:.3f}x, "
                      f"all reads {er[1] / COPY_BYTES:.3f}x, writes {(ew or 0) / COPY_BYTES:.3f}x of the known bytes")
-    cr, cw = rec.get("copy_read"), rec.get("copy_write")
-    if cr:
-        lines.append(f"calibration copy (1 GiB read + 1 GiB written): DRAM reads {cr[0] / COPY_BYTES:.3f}x, "
-                     f"all reads {cr[1] / COPY_BYTES:.3f}x, writes "
-                     f"{(cw or 0) / COPY_BYTES:.3f}x of the known bytes")
     lines.append(f"{'kernel':46s} {'dispatches':>10s} {'algorithmic MB':>15s} {'DRAM read MB':>13s} "
                  f"{'all read MB':>12s} {'write MB':>9s} {'read/alg':>9s}")
     for k in rec["kernels"]:
