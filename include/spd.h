@@ -249,13 +249,20 @@ typedef struct spd_handle spd_t;
 
 /* Bytes of device workspace spd_init needs for `cfg` (KV caches of target
  * and PDM, in-flight slots, anchor store, scratch, logits, rings, control
- * block, cycle-record ring).  Pure host computation.  SPD_EINVAL if the
+ * block, cycle-record ring and, for bf16 models, a copy of the draft module's
+ * layer matrices in matrix-core tile order: Ls * 2 * ((Hq + 2 Hkv) hd d +
+ * Hq hd d + 3 F d) bytes).  Pure host computation.  SPD_EINVAL if the
  * configuration is invalid. */
 SPD_API int spd_workspace_bytes(const spd_config *cfg, size_t *bytes);
 
 /* Validate `cfg`, record the weight pointers, carve `workspace` (device
  * memory of at least spd_workspace_bytes, 256-byte aligned) and build the
- * anchor-pattern and RoPE tables on the device.  stage_stream carries the
+ * anchor-pattern and RoPE tables on the device.  For bf16 models the draft
+ * module's layer matrices (w_qkv, w_o, w_gu, w_down of every pdm layer) are
+ * copied into the workspace in matrix-core tile order: the cycles read that
+ * copy, so later changes to those caller buffers take effect only through a
+ * new spd_init; every other weight is read from the caller's buffers, which
+ * must stay valid until spd_destroy.  stage_stream carries the
  * target stage step and verification; pdm_stream the draft module.  The
  * streams must be distinct and of default priority.  On success *out holds
  * the handle.  Errors: SPD_EINVAL (constraints above, null pointers,
