@@ -3,9 +3,9 @@
 The same workload runs once on an engine whose scratch is carved from its
 workspace (spd_init) and once on an engine whose scratch is the library's
 static device array (spd_init_static_scratch); records, tokens, logits, draft
-logits, anchors and KV caches must be bit-identical.  Two static-scratch
-engines in a row, the second with a smaller input, so that the second starts
-from the first one's leftover scratch contents.
+logits, anchors and KV caches must be bit-identical.  Static-scratch engines
+in a row, the second with a smaller input, so that it starts from the first
+one's leftover scratch contents, and a third with a small draft tree.
 """
 import numpy as np
 import pytest
@@ -17,12 +17,14 @@ from tests.gpu_common import gpu_workload_tiny
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, T, static, uni, ref, p):
+def _run(w, T, static, uni, ref, p, tree=None):
     from pipelined_draft_verify_amd import SPDEngine
 
     eng = SPDEngine(w, T, static_scratch=static)
     eng.set_uniforms(uni)
-    if ref is not None:
+    if ref is not None and tree is not None:
+        eng.set_tree_forced(ref, *tree)
+    elif ref is not None:
         eng.set_forced(ref, p)
     eng.prefill(si.make_prompt(w))
     recs = eng.run(batch=128)
@@ -39,9 +41,9 @@ def _run(w, T, static, uni, ref, p):
     return out
 
 
-def _check(w, T, uni, ref=None, p=None):
-    a = _run(w, T, False, uni, ref, p)
-    b = _run(w, T, True, uni, ref, p)
+def _check(w, T, uni, ref=None, p=None, tree=None):
+    a = _run(w, T, False, uni, ref, p, tree)
+    b = _run(w, T, True, uni, ref, p, tree)
     assert b["ws"] < a["ws"]  # the static engine's workspace holds no scratch
     for k in a:
         if k != "ws":
@@ -70,3 +72,11 @@ def test_static_scratch_matches_spd_init_two_calls():
                            Ls=2, G=24, seed=81)
     T2 = {k: v.to("cuda:0") for k, v in si.make_weights(w2, "cpu").items()}
     _check(w2, T2, si.make_uniforms(w2))
+    # third call: a small bf16 draft tree (its per-leaf scan partials live in the scratch too)
+    w3 = gpu_workload_tiny(dtype="bf16", L=8, n=4, Hq=8, Hkv=2, F=768, V=500, anchors=[0, 2, 4, 8], Ls=2,
+                           width=4, G=24, seed=82)
+    T3c = si.make_weights(w3, "cpu")
+    W3 = si.nest_weights(si.weights_numpy_f32(T3c), w3)
+    ref3, _ = ar_greedy(w3, W3, si.make_prompt(w3), w3.G)
+    T3 = {k: v.to("cuda:0") for k, v in T3c.items()}
+    _check(w3, T3, si.make_uniforms(w3), ref=ref3, tree=(0.3, 0.8))
