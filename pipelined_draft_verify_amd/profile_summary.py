@@ -2,6 +2,7 @@
 
   python -m pipelined_draft_verify_amd.profile_summary stats <kernel_stats.csv> [--cmd "..."]
   python -m pipelined_draft_verify_amd.profile_summary timeline <kernel_trace.csv> --cycles K [--skip S] [--cmd "..."]
+  python -m pipelined_draft_verify_amd.profile_summary gaps <kernel_trace.csv> --cycles K [--skip S] [--cmd "..."]
   python -m pipelined_draft_verify_amd.profile_summary traffic <fetch_dir> <write_dir> --cmd "..."
   python -m pipelined_draft_verify_amd.profile_summary mfma <counter_dir> [--cmd "..."]
 
@@ -9,6 +10,12 @@
 end (a cycle starts at each k_entry or k_tree_entry dispatch), and prints, per stream and per kernel/grid, the launches,
 average duration and time per cycle, plus each stream's busy time and the
 device-idle time (no kernel on any stream).
+
+`gaps` takes the same cycles and prints, per stream, the idle time between
+consecutive kernels of that stream (start of one minus end of the one before),
+summed per transition (kernel -> next kernel): launch gaps inside a graph,
+waits on the other stream, and waits on the host when it enqueues slower
+than the GPU runs.
 
 `traffic` reads two counter-collection runs of one workload step -- reads:
 TCC_EA0_RDREQ_DRAM_32B_sum (32-byte units of L2-to-memory read requests bound
@@ -74,16 +81,20 @@ def stats(path: str, top: int = 16) -> str:
     return "\n".join(out)
 
 
-def timeline(path: str, cycles: int, skip: int = 0, top: int = 30) -> str:
+def _region(path: str, cycles: int, skip: int):
+    """Dispatches of cycles [-(cycles + skip), -skip) of the trace, in start
+    order; host-side copies between steps (rollback) are not part of it."""
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
     ent = [i for i, r in enumerate(rows) if re.search(ENTRY_REGEX, r["Kernel_Name"])]
     if len(ent) < cycles + skip:
         raise ValueError(f"trace has {len(ent)} cycles, fewer than {cycles + skip}")
-    # cycles [-(cycles + skip), -skip) of the trace; host-side copies between
-    # steps (rollback) are not part of the region
     lo = ent[-(cycles + skip)]
     hi = ent[-skip] if skip else len(rows)
-    sel = [r for r in rows[lo:hi] if "copyBuffer" not in r["Kernel_Name"]]
+    return [r for r in rows[lo:hi] if "copyBuffer" not in r["Kernel_Name"]]
+
+
+def timeline(path: str, cycles: int, skip: int = 0, top: int = 30) -> str:
+    sel = _region(path, cycles, skip)
     t0 = int(sel[0]["Start_Timestamp"])
     t1 = max(int(r["End_Timestamp"]) for r in sel)
     span = (t1 - t0) / 1e3
@@ -111,6 +122,28 @@ def timeline(path: str, cycles: int, skip: int = 0, top: int = 30) -> str:
     out.append(f"{'stream':>6s} {'kernel':34s} {'grid (threads x, y, z)':>24s} {'calls':>6s} {'avg us':>8s} {'us/cycle':>9s}")
     for (st, name, gx, gy, gz), (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:top]:
         out.append(f"{st:>6s} {name[:34]:34s} {gx + ',' + gy + ',' + gz:>24s} {n:6d} {t / n:8.2f} {t / cycles:9.2f}")
+    return "\n".join(out)
+
+
+def gaps(path: str, cycles: int, skip: int = 0, top: int = 12) -> str:
+    sel = _region(path, cycles, skip)
+    out = []
+    per_stream = {}
+    for r in sel:
+        per_stream.setdefault(r["Stream_Id"], []).append(r)
+    for st in sorted(per_stream):
+        ks = per_stream[st]
+        agg = {}
+        for a, b in zip(ks, ks[1:]):
+            g = (int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) / 1e3
+            e = agg.setdefault((_short(a["Kernel_Name"]), _short(b["Kernel_Name"])), [0, 0.0])
+            e[0] += 1
+            e[1] += max(g, 0.0)
+        tot = sum(v[1] for v in agg.values())
+        out.append(f"stream {st}: {len(ks)} kernels, idle between them {tot / cycles:.1f} us/cycle")
+        out.append(f"  {'kernel -> next kernel':72s} {'count':>6s} {'mean us':>8s} {'us/cycle':>9s}")
+        for (a, b), (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:top]:
+            out.append(f"  {(a[:34] + ' -> ' + b[:34]):72s} {n:6d} {t / n:8.2f} {t / cycles:9.2f}")
     return "\n".join(out)
 
 
@@ -301,6 +334,11 @@ def main(argv=None):
     t.add_argument("--cycles", type=int, required=True)
     t.add_argument("--skip", type=int, default=0)
     t.add_argument("--cmd", default="")
+    gp = sub.add_parser("gaps")
+    gp.add_argument("csv")
+    gp.add_argument("--cycles", type=int, required=True)
+    gp.add_argument("--skip", type=int, default=0)
+    gp.add_argument("--cmd", default="")
     b = sub.add_parser("traffic")
     b.add_argument("read_dir")
     b.add_argument("write_dir")
@@ -319,6 +357,10 @@ def main(argv=None):
         if args.cmd:
             print(f"command: {args.cmd}")
         print(timeline(args.csv, args.cycles, args.skip))
+    elif args.what == "gaps":
+        if args.cmd:
+            print(f"command: {args.cmd}")
+        print(gaps(args.csv, args.cycles, args.skip))
     elif args.what == "mfma":
         if args.cmd:
             print(f"command: {args.cmd}")

@@ -58,6 +58,25 @@ def test_timeline_needs_enough_cycles(tmp_path):
         ps.timeline(str(p), cycles=2)
 
 
+def test_gaps_per_stream_and_transition(tmp_path):
+    rows = []
+    for c in range(4):
+        rows += _cycle(c * 100_000)
+    rows.append(("__amd_rocclr_copyBuffer", 1, 85_000, 95_000))
+    p = tmp_path / "trace.csv"
+    _write_trace(p, rows)
+    lines = ps.gaps(str(p), cycles=3, skip=1).splitlines()
+    # stream 1: entry -> gate/up 5 us in each of the 3 cycles; gate/up ->
+    # next entry 30 us twice (the last cycle's follower is outside the region)
+    assert lines[0] == "stream 1: 6 kernels, idle between them 25.0 us/cycle"
+    eg = [l for l in lines if "k_entry<bf16> -> k_gemv_stage<bf16, 2" in l]
+    assert len(eg) == 1 and eg[0].split()[-3:] == ["3", "5.00", "5.00"]
+    ge = [l for l in lines if "k_gemv_stage<bf16, 2, false> -> k_entry<bf16>" in l]
+    assert len(ge) == 1 and ge[0].split()[-3:] == ["2", "30.00", "20.00"]
+    # stream 2: one draft kernel per cycle, 40 us apart
+    assert "stream 2: 3 kernels, idle between them 26.7 us/cycle" in lines
+
+
 def _write_counters(d, rows):
     """rows: (dispatch id, kernel, grid, {counter: value})."""
     os.makedirs(d, exist_ok=True)
