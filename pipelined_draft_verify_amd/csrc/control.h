@@ -681,10 +681,17 @@ __global__ __launch_bounds__(kWG) void k_entry(Ctrl* C, const Geo g, int32_t* to
   if (!s_ok) return;
   const int slot = s_pos % g.nslots;
   const WT* e = embed + (size_t)s_tok * g.d;
-  for (int i = threadIdx.x; i < g.d; i += kWG) {
-    const float v = from_store(e[i]);
-    hslots[(size_t)slot * g.d + i] = v;
-    anchors[((size_t)slot * g.m + 0) * g.d + i] = v;
+  for (int i0 = threadIdx.x; i0 < g.d; i0 += kBatch * kWG) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = (i0 + u * kWG < g.d) ? from_store(e[i0 + u * kWG]) : 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kWG;
+      if (i >= g.d) break;
+      hslots[(size_t)slot * g.d + i] = v[u];
+      anchors[((size_t)slot * g.m + 0) * g.d + i] = v[u];
+    }
   }
 }
 

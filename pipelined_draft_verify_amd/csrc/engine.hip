@@ -979,7 +979,7 @@ int pdm_chain(spd_t* h, hipStream_t ps) {
       fa.ring = h->ring;
       fa.ctrl = h->ctrl;
       fa.g = g;
-      hipLaunchKernelGGL(k_tree_finalize, dim3(1), dim3(kWave), 0, ps, fa);
+      hipLaunchKernelGGL(k_tree_finalize, dim3(1), dim3(kWG), 0, ps, fa);
       return hipGetLastError() == hipSuccess ? SPD_OK : SPD_EHIP;
     }
     launch_stage<WT, EPI_ARGMAX>(h, hd, 1, ps, &grid);

@@ -32,9 +32,18 @@ namespace spd {
 // latency instead of L2 latency.  Copied word by word by the workgroup.
 static_assert(sizeof(Tree) % 4 == 0, "the tree block is copied in 4-byte words");
 __device__ __forceinline__ void tree_copy(Tree* dst, const Tree* src) {
+  constexpr int NW = (int)(sizeof(Tree) / 4);
   const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
   uint32_t* d = reinterpret_cast<uint32_t*>(dst);
-  for (int i = threadIdx.x; i < (int)(sizeof(Tree) / 4); i += blockDim.x) d[i] = s[i];
+  const int nt = blockDim.x;
+  for (int i0 = threadIdx.x; i0 < NW; i0 += kBatch * nt) {
+    uint32_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = s[min(i0 + u * nt, NW - 1)];  // unconditional: all in flight
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (i0 + u * nt < NW) d[i0 + u * nt] = v[u];
+  }
 }
 
 template <typename WT>
@@ -257,12 +266,23 @@ __global__ __launch_bounds__(kWG) void k_tree_entry(Ctrl* C, const Geo g, int32_
     spd_cycle_rec* r = ring + C->rec_slot;
     for (int l = threadIdx.x; l < SPD_MAX_LAYERS; l += kWG) r->kv_len[l] = 0;
   }
-  for (int k = 0; k < s_n; ++k) {
-    const WT* e = embed + (size_t)s_tok[k] * g.d;
-    for (int i = threadIdx.x; i < g.d; i += kWG) {
-      const float v = from_store(e[i]);
-      hslots[(size_t)s_slot[k] * g.d + i] = v;
-      anchors[((size_t)s_slot[k] * g.m + 0) * g.d + i] = v;
+  // the new nodes' embeddings (node k = index / d), kBatch loads in flight
+  const int tot = s_n * g.d;
+  for (int j0 = threadIdx.x; j0 < tot; j0 += kBatch * kWG) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int jj = min(j0 + u * kWG, tot - 1);
+      const int k = jj / g.d, i = jj - k * g.d;
+      v[u] = from_store(embed[(size_t)s_tok[k] * g.d + i]);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int jj = j0 + u * kWG;
+      if (jj >= tot) break;
+      const int k = jj / g.d, i = jj - k * g.d;
+      hslots[(size_t)s_slot[k] * g.d + i] = v[u];
+      anchors[((size_t)s_slot[k] * g.m + 0) * g.d + i] = v[u];
     }
   }
 }
@@ -277,12 +297,25 @@ __global__ __launch_bounds__(kWG) void k_tree_lane_copy(const Ctrl* C, const Geo
   const int lo = T->copy_lo, np = T->copy_hi - T->copy_lo + 1;
   if (np <= 0) return;
   const int n = g.Hkv * g.hd * np;
-  for (int idx = threadIdx.x; idx < n; idx += kWG) {
-    const int p = lo + idx % np, rest = idx / np;
-    const int dim = rest % g.hd, kvh = rest / g.hd;
-    const size_t ik = k_index(g, layer, kvh, p, dim), iv = v_index(g, layer, kvh, p, dim);
-    kc[dst + ik] = kc[src + ik];
-    vc[dst + iv] = vc[src + iv];
+  for (int i0 = threadIdx.x; i0 < n; i0 += kBatch * kWG) {
+    size_t ik[kBatch], iv[kBatch];
+    WT kx[kBatch], vx[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int idx = min(i0 + u * kWG, n - 1);
+      const int p = lo + idx % np, rest = idx / np;
+      const int dim = rest % g.hd, kvh = rest / g.hd;
+      ik[u] = k_index(g, layer, kvh, p, dim);
+      iv[u] = v_index(g, layer, kvh, p, dim);
+      kx[u] = kc[src + ik[u]];
+      vx[u] = vc[src + iv[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (i0 + u * kWG >= n) break;
+      kc[dst + ik[u]] = kx[u];
+      vc[dst + iv[u]] = vx[u];
+    }
   }
 }
 
@@ -299,6 +332,36 @@ struct TreeVerifyArgs {
   Ctrl* ctrl;
   Geo g;
 };
+
+// Key/values of position j in KV lane src copied to every other lane, all
+// layers; kBatch elements per thread in flight.
+template <typename KT>
+__device__ __forceinline__ void kv_broadcast(const Geo& g, KT* kc, KT* vc, int src, int j) {
+  const int n = g.L * g.Hkv * g.hd;
+  for (int i0 = threadIdx.x; i0 < n; i0 += kBatch * kCtlThreads) {
+    size_t ik[kBatch], iv[kBatch];
+    KT kx[kBatch], vx[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int idx = min(i0 + u * kCtlThreads, n - 1);
+      const int dim = idx % g.hd, rest = idx / g.hd;
+      const int kvh = rest % g.Hkv, layer = rest / g.Hkv;
+      ik[u] = k_index(g, layer, kvh, j, dim);
+      iv[u] = v_index(g, layer, kvh, j, dim);
+      kx[u] = kc[src * g.lane_kv + ik[u]];
+      vx[u] = vc[src * g.lane_kv + iv[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (i0 + u * kCtlThreads >= n) break;
+      for (int ln = 0; ln < g.W; ++ln) {
+        if (ln == src) continue;
+        kc[ln * g.lane_kv + ik[u]] = kx[u];
+        vc[ln * g.lane_kv + iv[u]] = vx[u];
+      }
+    }
+  }
+}
 
 __global__ __launch_bounds__(kCtlThreads) void k_tree_verify(const TreeVerifyArgs A) {
   __shared__ ArgPair sh_ap[kCtlThreads / kWave];
@@ -332,29 +395,10 @@ __global__ __launch_bounds__(kCtlThreads) void k_tree_verify(const TreeVerifyArg
   const int ex = T->exit_slot;
   const ArgPair best = block_argmax_parts(A.parts, A.nparts, sh_ap);
   // the exiting node's key/values join every lane (its position is verified)
-  {
-    const int src = T->lane[ex];
-    const int n = g.L * g.Hkv * g.hd;
-    for (int idx = threadIdx.x; idx < n; idx += kCtlThreads) {
-      const int dim = idx % g.hd, rest = idx / g.hd;
-      const int kvh = rest % g.Hkv, layer = rest / g.Hkv;
-      const size_t ik = k_index(g, layer, kvh, j, dim), iv = v_index(g, layer, kvh, j, dim);
-      for (int ln = 0; ln < W; ++ln) {
-        if (ln == src) continue;
-        if (A.kv_bytes == 2) {
-          uint16_t* kc = reinterpret_cast<uint16_t*>(A.kc);
-          uint16_t* vc = reinterpret_cast<uint16_t*>(A.vc);
-          kc[ln * g.lane_kv + ik] = kc[src * g.lane_kv + ik];
-          vc[ln * g.lane_kv + iv] = vc[src * g.lane_kv + iv];
-        } else {
-          float* kc = reinterpret_cast<float*>(A.kc);
-          float* vc = reinterpret_cast<float*>(A.vc);
-          kc[ln * g.lane_kv + ik] = kc[src * g.lane_kv + ik];
-          vc[ln * g.lane_kv + iv] = vc[src * g.lane_kv + iv];
-        }
-      }
-    }
-  }
+  if (A.kv_bytes == 2)
+    kv_broadcast(g, reinterpret_cast<uint16_t*>(A.kc), reinterpret_cast<uint16_t*>(A.vc), T->lane[ex], j);
+  else
+    kv_broadcast(g, reinterpret_cast<float*>(A.kc), reinterpret_cast<float*>(A.vc), T->lane[ex], j);
   for (int l = threadIdx.x; l < g.L; l += kCtlThreads) A.kv_len[l] = j + 1;  // committed (and (i) on reject)
   if (threadIdx.x == 0) {
     const int y = valid_token(best.i, g.V, &C->flags);
@@ -434,7 +478,13 @@ struct TreeScanArgs {
 // (every lane returns it).
 __device__ __forceinline__ float parts_max_wave(const ArgPair* p, int n) {
   float m = -INFINITY;
-  for (int k = threadIdx.x & (kWave - 1); k < n; k += kWave) m = fmaxf(m, p[k].v);
+  for (int k0 = threadIdx.x & (kWave - 1); k0 < n; k0 += kBatch * kWave) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = (k0 + u * kWave < n) ? p[k0 + u * kWave].v : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) m = fmaxf(m, v[u]);
+  }
   return wave_max(m);
 }
 
@@ -463,10 +513,17 @@ __global__ __launch_bounds__(kWG) void k_tree_scan(const TreeScanArgs A) {
   }
   double z = 0.0;
   const int base = blockIdx.x * kTreeScanBlk;
+  float xs[kTreeScanIds];
+#pragma unroll
+  for (int e = 0; e < kTreeScanIds; ++e) {
+    const int v = base + e * kWG + threadIdx.x;
+    xs[e] = v < g.V ? l[v] : 0.f;
+  }
+#pragma unroll
   for (int e = 0; e < kTreeScanIds; ++e) {
     const int v = base + e * kWG + threadIdx.x;
     if (v >= g.V) break;
-    const float x = l[v];
+    const float x = xs[e];
     z += exp((double)x - M);
     if (better(x, v, tv[W - 1], ti[W - 1])) {
       int k = W - 1;
@@ -524,7 +581,8 @@ struct TreeFinalizeArgs {
   Geo g;
 };
 
-__global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs A) {
+__global__ __launch_bounds__(kWG) void k_tree_finalize(const TreeFinalizeArgs A) {
+  static_assert(kWG / kWave >= kMaxW, "one wave per leaf");
   Ctrl* C = A.ctrl;
   Tree* TG = tree_of(C);
   const Geo& g = A.g;
@@ -534,22 +592,49 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
   // counts and rank tables meanwhile; nothing read here changes); the
   // candidates are written to the tree block itself
   __shared__ Tree sT;
+  // the forced policy's reference tokens at positions oldest .. t + 1, and the
+  // draft logit of the token at t + 1 under each leaf
+  __shared__ int s_ref[SPD_MAX_STAGES + 2];
+  __shared__ float s_lref[kMaxW];
   tree_copy(&sT, TG);
+  const int t = C->t, oldest = t - C->a + 1;
+  const bool forced = A.policy == SPD_DRAFT_FORCED && t + 1 < A.ref_len;
+  if (forced && (int)threadIdx.x <= t + 1 - oldest) {
+    const int r = A.ref[oldest + threadIdx.x];
+    s_ref[threadIdx.x] = r;
+    if (oldest + (int)threadIdx.x == t + 1) {
+      float lr[kMaxW];
+#pragma unroll
+      for (int m = 0; m < kMaxW; ++m) lr[m] = m < W ? A.logits[(size_t)m * g.V + r] : 0.f;
+#pragma unroll
+      for (int m = 0; m < kMaxW; ++m) s_lref[m] = lr[m];
+    }
+  }
   __syncthreads();
   const Tree* T = &sT;
-  const int t = C->t, oldest = t - C->a + 1, nl = T->nleaves;
-  // per leaf, by the whole wave: the max logit (over the head's per-workgroup
-  // partials), the normaliser (the scan blocks' sums; lane-strided, then a
-  // fixed butterfly) and the best W tokens (each lane's best W of its share of
-  // the blocks' lists, then W rounds of a wave argmax)
-  const int lane = threadIdx.x;
+  const int nl = T->nleaves;
+  // per leaf, by one wave (leaf m on wave m): the max logit (over the head's
+  // per-workgroup partials), the normaliser (the scan blocks' sums;
+  // lane-strided, then a fixed butterfly) and the best W tokens (each lane's
+  // best W of its share of the blocks' lists, then W rounds of a wave argmax)
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   __shared__ double s_lM[kMaxW], s_lZ[kMaxW];
   __shared__ float s_bv[kMaxW][kMaxW];
   __shared__ int s_bi[kMaxW][kMaxW];
-  for (int m = 0; m < nl; ++m) {
+  for (int m = wave; m < nl; m += kWG / kWave) {
     const float mx = parts_max_wave(A.parts + (size_t)m * A.nparts, A.nparts);
     double z = 0.0;
-    for (int b = lane; b < A.nblk; b += kWave) z += A.zpart[(size_t)m * A.nblk + b];
+    for (int b0 = lane; b0 < A.nblk; b0 += kBatch * kWave) {
+      double zb[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int b = b0 + u * kWave;
+        zb[u] = b < A.nblk ? A.zpart[(size_t)m * A.nblk + b] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (b0 + u * kWave < A.nblk) z += zb[u];
+    }
     z = wave_sum_d(z);
     float tv[kMaxW];
     int ti[kMaxW];
@@ -557,17 +642,27 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
       tv[k] = -INFINITY;
       ti[k] = 0x7FFFFFFF;
     }
-    for (int e = lane; e < A.nblk * W; e += kWave) {
-      const ArgPair c = A.tpart[(size_t)m * A.nblk * W + e];
-      if (!better(c.v, c.i, tv[W - 1], ti[W - 1])) continue;
-      int q = W - 1;
-      while (q > 0 && better(c.v, c.i, tv[q - 1], ti[q - 1])) {
-        tv[q] = tv[q - 1];
-        ti[q] = ti[q - 1];
-        --q;
+    const int ne = A.nblk * W;
+    for (int e0 = lane; e0 < ne; e0 += kBatch * kWave) {
+      ArgPair cb[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = e0 + u * kWave;
+        cb[u] = e < ne ? A.tpart[(size_t)m * ne + e] : ArgPair{-INFINITY, 0x7FFFFFFF};
       }
-      tv[q] = c.v;
-      ti[q] = c.i;
+      for (int u = 0; u < kBatch; ++u) {
+        if (e0 + u * kWave >= ne) break;
+        const ArgPair c = cb[u];
+        if (!better(c.v, c.i, tv[W - 1], ti[W - 1])) continue;
+        int q = W - 1;
+        while (q > 0 && better(c.v, c.i, tv[q - 1], ti[q - 1])) {
+          tv[q] = tv[q - 1];
+          ti[q] = ti[q - 1];
+          --q;
+        }
+        tv[q] = c.v;
+        ti[q] = c.i;
+      }
     }
     int head = 0;
     for (int k = 0; k < W; ++k) {
@@ -588,7 +683,7 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
     }
   }
   __syncthreads();
-  if (lane != 0) return;
+  if (threadIdx.x != 0) return;
   // candidates, ranking and the forced policy: one thread
   int cl[kMaxCand], ct[kMaxCand], crank[kMaxCand];
   double cs[kMaxCand], clq[kMaxCand];
@@ -638,7 +733,7 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
   }
   // forced policy (harness device): the pair (forced leaf, ref[q])
   const int q = t + 1;
-  if (A.policy == SPD_DRAFT_FORCED && q < A.ref_len) {
+  if (forced) {
     // the leaf whose path matches the reference for the longest prefix from
     // the oldest position (ties: the lower rank)
     int star = 0, best = -1;
@@ -646,7 +741,7 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
       int match[SPD_MAX_STAGES + 1];
       int x = lslot[m], np = 0;
       for (int p = t; p >= oldest; --p) {
-        match[np++] = T->tok[x] == A.ref[p];
+        match[np++] = T->tok[x] == s_ref[p - oldest];
         if (p > oldest) x = T->parent[x];
       }
       int k = 0;
@@ -656,7 +751,7 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
         star = m;
       }
     }
-    const int R = A.ref[q];
+    const int R = s_ref[q - oldest];
     const float u = A.uni[(size_t)q * SPD_U_COUNT + SPD_U_FORCE];
     const float* ls = A.logits + (size_t)star * g.V;
     int at = -1;
@@ -673,7 +768,7 @@ __global__ __launch_bounds__(kWave) void k_tree_finalize(const TreeFinalizeArgs 
       for (int i = nc; i > ins; --i) {
         cl[i] = cl[i - 1]; ct[i] = ct[i - 1]; crank[i] = crank[i - 1]; cs[i] = cs[i - 1]; clq[i] = clq[i - 1];
       }
-      const double lq = (double)ls[R] - lM[star] - lZ[star];
+      const double lq = (double)s_lref[star] - lM[star] - lZ[star];
       cl[ins] = lslot[star];
       ct[ins] = R;
       crank[ins] = star;
