@@ -10,11 +10,6 @@ namespace spd {
 
 constexpr int kWG = 256;          // threads per workgroup for the streaming kernels
 constexpr int kWave = 64;         // CDNA wavefront
-// Strided loops over global memory in the control kernels issue kBatch loads
-// before the first is used: a loop body with one load and its use waits out
-// one memory round trip per iteration.  Each thread still handles its
-// elements in the same order.
-constexpr int kBatch = 8;
 constexpr int kSplit = 256;       // attention positions per split (one per thread)
 constexpr int kMaxQ = 16;         // query vectors per attention workgroup
 constexpr int kRowsMR = 16;       // activation rows per pass of the row-batched GEMV

@@ -8,6 +8,12 @@ namespace spd {
 
 constexpr int kCtlThreads = 1024;
 
+// Strided loops over global memory in the control kernels issue kBatch loads
+// before the first is used: a loop body with one load and its use waits out
+// one memory round trip per iteration.  Each thread still handles its
+// elements in the same order.
+constexpr int kBatch = 8;
+
 // ---- block-wide helpers for 1024-thread kernels ----------------------------
 __device__ __forceinline__ ArgPair block_argmax_parts(const ArgPair* parts, int nparts, ArgPair* sh) {
   float v = -INFINITY;
