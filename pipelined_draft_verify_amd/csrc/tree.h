@@ -621,6 +621,14 @@ __global__ __launch_bounds__(kWG) void k_tree_finalize(const TreeFinalizeArgs A)
   __shared__ double s_lM[kMaxW], s_lZ[kMaxW];
   __shared__ float s_bv[kMaxW][kMaxW];
   __shared__ int s_bi[kMaxW][kMaxW];
+  // the serial part's working lists, indexed at run time: in LDS rather than
+  // in per-lane scratch memory
+  __shared__ int cl[kMaxCand], ct[kMaxCand], crank[kMaxCand];
+  __shared__ double cs[kMaxCand], clq[kMaxCand];
+  __shared__ double lM[kMaxW], lZ[kMaxW], cum[kMaxW];
+  __shared__ int lslot[kMaxW];
+  __shared__ double lqs[SPD_MAX_STAGES + 1];
+  __shared__ int match[SPD_MAX_STAGES + 1];
   for (int m = wave; m < nl; m += kWG / kWave) {
     const float mx = parts_max_wave(A.parts + (size_t)m * A.nparts, A.nparts);
     double z = 0.0;
@@ -685,18 +693,13 @@ __global__ __launch_bounds__(kWG) void k_tree_finalize(const TreeFinalizeArgs A)
   __syncthreads();
   if (threadIdx.x != 0) return;
   // candidates, ranking and the forced policy: one thread
-  int cl[kMaxCand], ct[kMaxCand], crank[kMaxCand];
-  double cs[kMaxCand], clq[kMaxCand];
-  int nc = 0;
-  double lM[kMaxW], lZ[kMaxW], cum[kMaxW];
-  int lslot[kMaxW], top0 = -1;
+  int nc = 0, top0 = -1;
   for (int m = 0; m < nl; ++m) {
     lM[m] = s_lM[m];
     lZ[m] = s_lZ[m];
     const int sl = T->row_slot[T->nrows - nl + m];
     lslot[m] = sl;
     // cum: log Q over the path above the oldest position, in position order
-    double lqs[SPD_MAX_STAGES + 1];
     int np = 0, x = sl;
     for (int p = t; p > oldest; --p) {
       lqs[np++] = T->logq[x];
@@ -738,7 +741,6 @@ __global__ __launch_bounds__(kWG) void k_tree_finalize(const TreeFinalizeArgs A)
     // the oldest position (ties: the lower rank)
     int star = 0, best = -1;
     for (int m = 0; m < nl; ++m) {
-      int match[SPD_MAX_STAGES + 1];
       int x = lslot[m], np = 0;
       for (int p = t; p >= oldest; --p) {
         match[np++] = T->tok[x] == s_ref[p - oldest];
