@@ -177,3 +177,29 @@ def test_static_scratch_rejects_oversized_configs():
     with pytest.raises(A.SPDError) as e:
         A.spd_init_static_scratch(c)  # ... whose scratch exceeds the static array
     assert e.value.code == A.SPD_ESCRATCH
+
+
+def test_tree_constraints_are_checked():
+    """Draft trees are greedy, pre-step, softmax-attention, uniform-stage
+    configurations of two or more stages whose draft-module rows
+    (2 + (n - 1) W) fit two row tiles; width 0 or 1 is a chain."""
+    w = si.workload("4b_tree4_n8")
+    assert A.spd_workspace_bytes(make_config(w)) > 0
+    for width in (0, 1, 2, 3):
+        assert A.spd_workspace_bytes(make_config(w.replace(width=width))) > 0
+    # n = 16 at width 2 is exactly 32 rows; width 3 is 47
+    assert A.spd_workspace_bytes(make_config(si.workload("4b_n16").replace(width=2))) > 0
+    for kw in [dict(width=-1), dict(width=5),                     # outside 0..SPD_MAX_WIDTH
+               dict(mode="sample", temperature=1.0),              # greedy only
+               dict(schedule="post"),                             # pre-step only
+               dict(n=1),                                         # at least two stages
+               dict(attn_period=4),                               # softmax attention only
+               dict(n=4, split=(5, 9, 9, 9))]:                    # uniform stages only
+        with pytest.raises(A.SPDError) as e:
+            A.spd_workspace_bytes(make_config(w.replace(**kw)))
+        assert e.value.code == A.SPD_EINVAL, kw
+        if "width" not in kw:  # the same setting is a valid chain: the tree rule refused it
+            assert A.spd_workspace_bytes(make_config(w.replace(width=1, **kw))) > 0, kw
+    with pytest.raises(A.SPDError) as e:
+        A.spd_workspace_bytes(make_config(si.workload("4b_n16").replace(width=3)))
+    assert e.value.code == A.SPD_EINVAL
