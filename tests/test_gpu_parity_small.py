@@ -299,3 +299,49 @@ def test_error_paths_from_the_host():
         eng.rollback(w.P, w.V)
     eng.run()
     eng.close()
+
+
+def test_setter_refusals_from_the_host():
+    """The policy, uniform-table and launch-mode calls refuse what their
+    declarations exclude, and a refused call leaves the engine usable."""
+    from pipelined_draft_verify_amd import SPDEngine, SPDError
+    from pipelined_draft_verify_amd import _abi as A
+
+    def einval(fn, *args):
+        with pytest.raises(SPDError) as e:
+            fn(*args)
+        assert e.value.code == A.SPD_EINVAL
+
+    # a chain
+    w = gpu_workload_tiny(seed=61)
+    T, W, prompt, uni = _inputs(w)
+    ref, _ = ar_greedy(w, W, prompt, w.G)
+    eng = SPDEngine(w, {k: v.to("cuda:0") for k, v in T.items()})
+    einval(eng.set_forced, ref, 0.8)                 # forced drafts need the uniform table
+    einval(eng.set_uniforms, uni[: w.max_ctx - 1])   # fewer positions than the context holds
+    eng.set_uniforms(uni)
+    einval(eng.set_forced, ref, 1.5)                 # acceptance outside [0, 1]
+    einval(eng.set_tree_forced, ref, 0.3, 0.8)       # the tree policy on a chain
+    einval(A.spd_set_launch_mode, eng.h, 4)          # not eager or graph
+    einval(eng.prefill, list(prompt[:-1]) + [w.V])   # a prompt token outside the vocabulary
+    eng.set_forced(ref, 0.8)
+    first = eng.prefill(prompt)
+    eng.run()
+    toks = eng.tokens(w.P, w.G)
+    eng.close()
+    assert [first] + toks[1:] == ref[w.P:] == toks
+
+    # a draft tree
+    w = gpu_workload_tiny(L=4, n=2, width=2, seed=62)
+    T, W, prompt, uni = _inputs(w)
+    ref, _ = ar_greedy(w, W, prompt, w.G)
+    eng = SPDEngine(w, {k: v.to("cuda:0") for k, v in T.items()})
+    eng.set_uniforms(uni)
+    einval(eng.set_forced, ref, 0.8)                 # a tree takes the tree policy
+    einval(eng.set_tree_forced, ref, 0.9, 0.5)       # p_first above p_tree
+    eng.set_tree_forced(ref, 0.3, 0.8)
+    first = eng.prefill(prompt)
+    eng.run()
+    toks = eng.tokens(w.P, w.G)
+    eng.close()
+    assert [first] + toks[1:] == ref[w.P:] == toks
